@@ -1,0 +1,271 @@
+"""Benchmark: fused graph attention forward+backward on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME]
+
+A step is one forward and one backward pass of the whole fused layer over the
+workload's graph, inputs already resident in device memory. The default
+workload is the Graph Transformer on a Chung-Lu power-law graph
+(N = 200,000, exponent 2.1, mean in-degree 15, in-degree cap 20,000, plus
+self-loops; H = 4, D = 128; bf16 inputs, fp32 accumulation).
+
+Prints one JSON line. ``value`` is E*H / step time in GEdge.head/s (E counts
+self-loops). ``roofline`` is for the kernel with the largest share of the step:
+algorithmic bytes per launch (the per-edge and per-node traffic model of that
+kernel) over its mean launch time, timed with HIP events recorded by the
+library on the launch stream during the timed steps. ``cpu_baseline`` times
+the fp64 CPU oracle on a bounded sample of the same workload (rows 0..r-1 of
+the CSR, the rest emptied) on this host's cores.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+DEFAULT_WORKLOAD = "gt_powerlaw200k_h4d128_bf16"
+KERNEL_SOURCES = ["sparse_graph_attention_csr_amd/csrc/device.hpp",
+                  "sparse_graph_attention_csr_amd/csrc/gather.hpp",
+                  "sparse_graph_attention_csr_amd/csrc/launch_gt.hip",
+                  "sparse_graph_attention_csr_amd/csrc/launch_gat.hip"]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def algorithmic_bytes(kernel: str, n: int, e: int, H: int, D: int, b: int) -> int | None:
+    """Bytes a kernel must move: neighbour-row gathers per edge plus the
+    per-node reads and writes of its own rows (R = H*D*b bytes per node row)."""
+    R = H * D * b
+    model = {
+        # K_j, V_j and colidx per edge; Q_i read, out_i and lse_i written per node
+        "gt_fwd_rows": (2 * R + 4, 2 * R + 4 * H + 8),
+        # K_j, V_j, colidx per edge; Q_i, dO_i, O_i, lse_i read, dQ_i and (lse, Delta) written
+        "gt_bwd_rows": (2 * R + 4, 4 * R + 12 * H + 8),
+        # Q_i, dO_i, (lse_i, Delta_i), rowidx per edge; K_j, V_j read, dK_j, dV_j written
+        "gt_bwd_cols": (2 * R + 8 * H + 4, 4 * R + 8),
+        # Xt_j and colidx per edge; Xs_i read, out_i, lse_i written
+        "gat_fwd_rows": (R + 4, 2 * R + 4 * H + 8),
+        # Xt_j, colidx per edge; Xs_i, dO_i, O_i, lse_i read, dXs_i, (lse, Delta) written
+        "gat_bwd_rows": (R + 4, 4 * R + 12 * H + 8),
+        # Xs_i, dO_i, (lse_i, Delta_i), rowidx per edge; Xt_j read, dXt_j written
+        "gat_bwd_cols": (2 * R + 8 * H + 4, 2 * R + 8),
+    }.get(kernel)
+    if model is None:
+        return None
+    per_edge, per_node = model
+    return per_edge * e + per_node * n
+
+
+def read_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the kernel sources as they are now."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_counters.md")
+    if not os.path.exists(path):
+        return None
+    txt = open(path).read()
+    m = re.search(r"kernel_source_hash:\s*(\w+)", txt)
+    t = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", txt)
+    if not m or not t or m.group(1) != kernel_source_hash():
+        return None
+    return float(t.group(1))
+
+
+def cpu_baseline(w, seconds: float):
+    """The oracle on rows 0..r-1 of the workload (other rows emptied), sized to
+    about `seconds` of host time; returns a dict for the JSON line."""
+    import numpy as np
+
+    import oracle
+    spec = w["spec"]
+    rp, ci = w["rowptr"], w["colidx"]
+
+    def run(r):
+        sub = rp.copy()
+        sub[r + 1:] = rp[r]
+        e = int(sub[-1])
+        t0 = time.perf_counter()
+        if spec.op == "gt":
+            oracle.gt_fwd(sub, ci[:e], w["q"], w["k"], w["v"], rows=np.arange(r))
+            if spec.passes == "fwd+bwd":
+                oracle.gt_bwd(sub, ci[:e], w["q"], w["k"], w["v"], w["dout"],
+                              dst_rows=np.arange(r), src_rows=np.unique(ci[:e]))
+        else:
+            oracle.gat_fwd(sub, ci[:e], w["xs"], w["xt"], w["a"], 0.2, rows=np.arange(r))
+            if spec.passes == "fwd+bwd":
+                oracle.gat_bwd(sub, ci[:e], w["xs"], w["xt"], w["a"], w["dout"], 0.2,
+                               dst_rows=np.arange(r), src_rows=np.unique(ci[:e]))
+        return e, time.perf_counter() - t0
+
+    n = rp.size - 1
+    r = min(n, 2000)
+    e, t = run(r)
+    while t < seconds / 8 and r < n:        # grow the probe until it is long enough to scale
+        r = min(n, r * 4)
+        e, t = run(r)
+    if r < n and t < seconds / 2:
+        target = e * seconds / max(t, 1e-9)
+        r = int(min(n, np.searchsorted(rp, target)))
+        e, t = run(r)
+    rate = e * spec.heads / t / 1e9
+    return {"value": rate, "unit": "GEdge*head/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": f"destination rows 0..{r - 1} of {n} ({e} of {int(rp[-1])} edges), "
+                      f"{spec.passes}, fp64, {t:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--chunk", type=int, default=0)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from sparse_graph_attention_csr_amd import binding as B
+    from sparse_graph_attention_csr_amd import inputs as I
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    spec = I.WORKLOADS[args.workload]
+    w = I.make_workload(args.workload)
+    rp, ci = w["rowptr"], w["colidx"]
+    n, e = rp.size - 1, int(rp[-1])
+    H, D = spec.heads, spec.dim
+    dt = B.BF16 if spec.dtype == I.BF16 else B.F32
+    nbytes = 2 if dt == B.BF16 else 4
+
+    t0 = time.perf_counter()
+    g = B.DeviceGraph(rp, ci, device=dev, chunk=args.chunk)
+    torch.cuda.synchronize()
+    plan_ms = (time.perf_counter() - t0) * 1e3
+
+    def todev(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(a).to(dev)
+
+    lse = torch.empty(n, H, dtype=torch.float32, device=dev)
+    if spec.op == "gt":
+        Q, K, V = todev(w["q"]), todev(w["k"]), todev(w["v"])
+        out = torch.empty_like(Q)
+        wsf = g.workspace(B.OP_GT_FWD, H, D, dt)
+        bwd = spec.passes == "fwd+bwd"
+        if bwd:
+            dO = todev(w["dout"])
+            dQ, dK, dV = (torch.empty_like(Q) for _ in range(3))
+            wsb = g.workspace(B.OP_GT_BWD, H, D, dt)
+
+        def step():
+            B.gt_fwd(g.plan, g.rowptr, g.colidx, Q, K, V, out, lse, wsf)
+            if bwd:
+                B.gt_bwd(g.plan, g.rowptr, g.colidx, Q, K, V, out, lse, dO, dQ, dK, dV, wsb)
+    else:
+        Xs, Xt = todev(w["xs"]), todev(w["xt"])
+        A = torch.from_numpy(w["a"]).to(dev)
+        out = torch.empty_like(Xs)
+        wsf = g.workspace(B.OP_GAT_FWD, H, D, dt)
+        bwd = spec.passes == "fwd+bwd"
+        if bwd:
+            dO = todev(w["dout"])
+            dXs, dXt = torch.empty_like(Xs), torch.empty_like(Xs)
+            dA = torch.empty(H, D, dtype=torch.float32, device=dev)
+            wsb = g.workspace(B.OP_GAT_BWD, H, D, dt)
+
+        def step():
+            B.gat_fwd(g.plan, g.rowptr, g.colidx, Xs, Xt, A, 0.2, out, lse, wsf)
+            if bwd:
+                B.gat_bwd(g.plan, g.rowptr, g.colidx, Xs, Xt, A, 0.2, out, lse, dO, dXs, dXt,
+                          dA, wsb)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    B.trace_clear()
+    B.trace_enable(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    B.trace_enable(False)
+    recs = B.trace_read()
+    B.trace_clear()
+
+    ms_per_step = elapsed * 1e3 / args.steps
+    value = e * H / (ms_per_step / 1e3) / 1e9
+
+    per = {}
+    for name, ms in recs:
+        d = per.setdefault(name, [0.0, 0])
+        d[0] += ms
+        d[1] += 1
+    kernels = {}
+    for name, (tot, cnt) in per.items():
+        avg = tot / cnt
+        ab = algorithmic_bytes(name, n, e, H, D, nbytes)
+        kernels[name] = {"ms": round(avg, 4), "launches_per_step": cnt / args.steps,
+                         "share": round(tot / max(sum(v[0] for v in per.values()), 1e-12), 4)}
+        if ab is not None:
+            kernels[name]["algorithmic_bytes"] = ab
+            kernels[name]["achieved_gbs"] = round(ab / (avg * 1e-3) / 1e9, 1)
+    dom = max((k for k in kernels if "algorithmic_bytes" in kernels[k]),
+              key=lambda k: kernels[k]["ms"] * kernels[k]["launches_per_step"])
+    dk = kernels[dom]
+    achieved = dk["achieved_gbs"]
+    traffic = read_traffic(dom, args.workload)
+    roofline = {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                "algorithmic_bytes": dk["algorithmic_bytes"]}
+
+    line = {
+        "metric": "fused graph-attn fwd+bwd GEdge*head/s; achieved HBM GB/s vs MI355X peak",
+        "value": round(value, 4),
+        "unit": "GEdge*head/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if dt == B.BF16 else "f32",
+        "data": "synthetic (seeded generator, seed 0)",
+        "config": {"workload": args.workload, "graph": spec.graph, "nodes": n, "edges": e,
+                   "heads": H, "head_dim": D, "passes": spec.passes,
+                   "chunk": g.plan.stats()["chunk"]},
+        "roofline": roofline,
+        "kernels": kernels,
+        "plan_ms": round(plan_ms, 1),
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,314 @@
+// C ABI of the fused graph-attention library: argument checks, workspace
+// layout, plan upload, kernel-timing trace, dispatch to the launchers.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "launch.hpp"
+#include "plan.hpp"
+
+namespace sgat {
+
+Decomp decompose(int dt, int D, int H)
+{
+    Decomp d{};
+    d.vec = dt == SGAT_F32 ? 4 : 8;
+    d.sph = D / d.vec;
+    const int hg_max = 64 / d.sph;
+    const int want = std::min(H, hg_max);
+    int hg = 1;
+    while (hg < want) hg <<= 1;
+    d.hg = hg;
+    d.epw = 64 / (hg * d.sph);
+    d.n_hg = (H + hg - 1) / hg;
+    return d;
+}
+
+int64_t wave_grid(int64_t units)
+{
+    const int64_t blocks = (units + kWavesPerBlock - 1) / kWavesPerBlock;
+    return (blocks + kGridQuantum - 1) / kGridQuantum * kGridQuantum;
+}
+
+// ---------------------------------------------------------------------------
+// trace
+// ---------------------------------------------------------------------------
+
+namespace {
+struct TraceRec {
+    std::string name;
+    hipEvent_t start = nullptr, stop = nullptr;
+};
+bool g_trace = false;
+std::vector<TraceRec> g_recs;
+size_t g_used = 0;
+}  // namespace
+
+int launch(const char* name, const void* fn, dim3 grid, dim3 block, void* arg, hipStream_t s)
+{
+    void* args[] = {arg};
+    TraceRec* rec = nullptr;
+    if (g_trace) {
+        if (g_used == g_recs.size()) {
+            TraceRec r;
+            if (hipEventCreate(&r.start) != hipSuccess || hipEventCreate(&r.stop) != hipSuccess)
+                return SGAT_HIP_ERROR;
+            g_recs.push_back(r);
+        }
+        rec = &g_recs[g_used++];
+        rec->name = name;
+        if (hipEventRecord(rec->start, s) != hipSuccess) return SGAT_HIP_ERROR;
+    }
+    hipError_t e = hipLaunchKernel(fn, grid, block, args, 0, s);
+    if (e != hipSuccess) return SGAT_HIP_ERROR;
+    if (rec && hipEventRecord(rec->stop, s) != hipSuccess) return SGAT_HIP_ERROR;
+    return SGAT_OK;
+}
+
+// ---------------------------------------------------------------------------
+// argument checks and workspace layout
+// ---------------------------------------------------------------------------
+
+namespace {
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int check_common(const sgat_plan* plan, int64_t n, int64_t nnz, const int64_t* rowptr,
+                 const int32_t* colidx, int H, int D, int dt)
+{
+    if (!plan) return SGAT_INVALID_ARGUMENT;
+    if (H < 1 || H > 16 || (D != 32 && D != 64 && D != 128)) return SGAT_INVALID_ARGUMENT;
+    if (dt != SGAT_F32 && dt != SGAT_BF16) return SGAT_INVALID_ARGUMENT;
+    if (n != plan->p.n || nnz != plan->p.nnz) return SGAT_PLAN_MISMATCH;
+    if (!plan->p.uploaded) return SGAT_NOT_UPLOADED;
+    if (!rowptr || (nnz > 0 && !colidx)) return SGAT_INVALID_ARGUMENT;
+    return SGAT_OK;
+}
+
+int check_tensor(const void* p, int64_t n)
+{
+    if (n == 0) return SGAT_OK;
+    if (!p || !aligned(p, 16)) return SGAT_INVALID_ARGUMENT;
+    return SGAT_OK;
+}
+
+struct Layout {
+    size_t off[6] = {};
+    size_t total = 0;
+};
+
+// Regions, each 256-byte aligned, in this order.
+Layout ws_layout(const Plan& p, int op, int H, int D)
+{
+    const size_t HD = static_cast<size_t>(H) * D;
+    size_t sz[6] = {};
+    switch (op) {
+    case SGAT_OP_GT_FWD:
+    case SGAT_OP_GAT_FWD:
+        sz[0] = static_cast<size_t>(p.row_slots) * HD * 4;          // part_acc
+        sz[1] = static_cast<size_t>(p.row_slots) * H * 8;           // part_ml
+        break;
+    case SGAT_OP_GT_BWD:
+        sz[0] = static_cast<size_t>(p.n) * H * 8;                   // stats
+        sz[1] = static_cast<size_t>(p.row_slots) * HD * 4;          // dQ partials
+        sz[2] = static_cast<size_t>(p.col_slots) * HD * 4;          // dK partials
+        sz[3] = static_cast<size_t>(p.col_slots) * HD * 4;          // dV partials
+        break;
+    case SGAT_OP_GAT_BWD:
+        sz[0] = static_cast<size_t>(p.n) * H * 8;                   // stats
+        sz[1] = static_cast<size_t>(p.row_slots) * HD * 4;          // dXs partials
+        sz[2] = static_cast<size_t>(p.col_slots) * HD * 4;          // dXt partials
+        sz[4] = static_cast<size_t>(gat_bwd_row_blocks(p)) * HD * 4; // da partials
+        break;
+    default:
+        break;
+    }
+    Layout L;
+    size_t off = 0;
+    for (int r = 0; r < 6; ++r) {
+        L.off[r] = off;
+        off = align_up(off + sz[r]);
+    }
+    L.total = off;
+    return L;
+}
+
+template <class T>
+T* at(void* ws, size_t off) { return reinterpret_cast<T*>(static_cast<char*>(ws) + off); }
+
+int check_ws(const Plan& p, int op, int H, int D, const void* ws, size_t ws_bytes, Layout& L)
+{
+    L = ws_layout(p, op, H, D);
+    if (ws_bytes < L.total) return SGAT_WORKSPACE_TOO_SMALL;
+    if (L.total > 0 && (!ws || !aligned(ws, 256))) return SGAT_INVALID_ARGUMENT;
+    return SGAT_OK;
+}
+
+}  // namespace
+}  // namespace sgat
+
+using namespace sgat;
+
+extern "C" {
+
+const char* sgat_status_string(int st)
+{
+    switch (st) {
+    case SGAT_OK: return "ok";
+    case SGAT_INVALID_ARGUMENT: return "invalid argument";
+    case SGAT_INVALID_CSR: return "invalid CSR";
+    case SGAT_WORKSPACE_TOO_SMALL: return "workspace or buffer too small";
+    case SGAT_PLAN_MISMATCH: return "n or nnz differs from the plan";
+    case SGAT_HIP_ERROR: return "HIP error";
+    case SGAT_NOT_UPLOADED: return "plan not uploaded";
+    case SGAT_OUT_OF_HOST_MEMORY: return "out of host memory";
+    case SGAT_UNSUPPORTED: return "unsupported for this plan";
+    default: return "unknown status";
+    }
+}
+
+int sgat_plan_upload(sgat_plan* plan, void* dev_buf, size_t bytes, void* stream)
+{
+    if (!plan || !dev_buf) return SGAT_INVALID_ARGUMENT;
+    Plan& p = plan->p;
+    if (bytes < p.device_bytes) return SGAT_WORKSPACE_TOO_SMALL;
+    if (!aligned(dev_buf, kAlign)) return SGAT_INVALID_ARGUMENT;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    for (int a = 0; a < SGAT_ARR_COUNT; ++a) {
+        if (p.bytes[a] == 0) continue;
+        // pageable source: the copy has read it by the time the call returns
+        if (hipMemcpyAsync(static_cast<char*>(dev_buf) + p.offset[a], p.host_array(a), p.bytes[a],
+                           hipMemcpyHostToDevice, s) != hipSuccess)
+            return SGAT_HIP_ERROR;
+    }
+    p.dev = static_cast<const unsigned char*>(dev_buf);
+    p.uploaded = true;
+    return SGAT_OK;
+}
+
+int sgat_workspace_bytes(const sgat_plan* plan, int op, int H, int D, int dtype, size_t* bytes)
+{
+    if (!plan || !bytes) return SGAT_INVALID_ARGUMENT;
+    if (op < SGAT_OP_GT_FWD || op > SGAT_OP_GAT_BWD) return SGAT_INVALID_ARGUMENT;
+    if (H < 1 || H > 16 || (D != 32 && D != 64 && D != 128)) return SGAT_INVALID_ARGUMENT;
+    if (dtype != SGAT_F32 && dtype != SGAT_BF16) return SGAT_INVALID_ARGUMENT;
+    *bytes = ws_layout(plan->p, op, H, D).total;
+    return SGAT_OK;
+}
+
+int gt_fwd(const sgat_plan* plan, int64_t n, int64_t nnz, const int64_t* rowptr,
+           const int32_t* colidx, int H, int D, int dtype, const void* Q, const void* K,
+           const void* V, void* out, float* lse, void* ws, size_t ws_bytes, int use_tiles,
+           void* stream)
+{
+    int rc = check_common(plan, n, nnz, rowptr, colidx, H, D, dtype);
+    if (rc) return rc;
+    for (const void* t : {Q, K, V, static_cast<const void*>(out)})
+        if ((rc = check_tensor(t, n))) return rc;
+    if (n > 0 && (!lse || !aligned(lse, 4))) return SGAT_INVALID_ARGUMENT;
+    if (use_tiles != 0) return use_tiles == 1 ? SGAT_UNSUPPORTED : SGAT_INVALID_ARGUMENT;
+    Layout L;
+    if ((rc = check_ws(plan->p, SGAT_OP_GT_FWD, H, D, ws, ws_bytes, L))) return rc;
+    if (n == 0) return SGAT_OK;
+    FwdWs w{at<float>(ws, L.off[0]), at<float>(ws, L.off[1])};
+    return launch_gt_fwd(plan->p, H, D, dtype, colidx, Q, K, V, out, lse, w,
+                         static_cast<hipStream_t>(stream));
+}
+
+int gt_bwd(const sgat_plan* plan, int64_t n, int64_t nnz, const int64_t* rowptr,
+           const int32_t* colidx, int H, int D, int dtype, const void* Q, const void* K,
+           const void* V, const void* out, const float* lse, const void* dout, void* dQ, void* dK,
+           void* dV, void* ws, size_t ws_bytes, int use_tiles, void* stream)
+{
+    int rc = check_common(plan, n, nnz, rowptr, colidx, H, D, dtype);
+    if (rc) return rc;
+    for (const void* t : {Q, K, V, out, dout, static_cast<const void*>(dQ),
+                          static_cast<const void*>(dK), static_cast<const void*>(dV)})
+        if ((rc = check_tensor(t, n))) return rc;
+    if (n > 0 && (!lse || !aligned(lse, 4))) return SGAT_INVALID_ARGUMENT;
+    if (use_tiles != 0) return use_tiles == 1 ? SGAT_UNSUPPORTED : SGAT_INVALID_ARGUMENT;
+    Layout L;
+    if ((rc = check_ws(plan->p, SGAT_OP_GT_BWD, H, D, ws, ws_bytes, L))) return rc;
+    if (n == 0) return SGAT_OK;
+    BwdWs w{at<void>(ws, L.off[0]), at<float>(ws, L.off[1]), at<float>(ws, L.off[2]),
+            at<float>(ws, L.off[3]), nullptr};
+    return launch_gt_bwd(plan->p, H, D, dtype, colidx, Q, K, V, out, lse, dout, dQ, dK, dV, w,
+                         static_cast<hipStream_t>(stream));
+}
+
+int gat_fwd(const sgat_plan* plan, int64_t n, int64_t nnz, const int64_t* rowptr,
+            const int32_t* colidx, int H, int D, int dtype, const void* x_dst, const void* x_nbr,
+            const float* a, float negative_slope, void* out, float* lse, void* ws,
+            size_t ws_bytes, void* stream)
+{
+    int rc = check_common(plan, n, nnz, rowptr, colidx, H, D, dtype);
+    if (rc) return rc;
+    for (const void* t : {x_dst, x_nbr, static_cast<const void*>(out)})
+        if ((rc = check_tensor(t, n))) return rc;
+    if (n > 0 && (!lse || !aligned(lse, 4) || !a || !aligned(a, 16))) return SGAT_INVALID_ARGUMENT;
+    if (!(negative_slope == negative_slope)) return SGAT_INVALID_ARGUMENT;   // NaN
+    Layout L;
+    if ((rc = check_ws(plan->p, SGAT_OP_GAT_FWD, H, D, ws, ws_bytes, L))) return rc;
+    if (n == 0) return SGAT_OK;
+    FwdWs w{at<float>(ws, L.off[0]), at<float>(ws, L.off[1])};
+    return launch_gat_fwd(plan->p, H, D, dtype, colidx, x_dst, x_nbr, a, negative_slope, out,
+                          lse, w, static_cast<hipStream_t>(stream));
+}
+
+int gat_bwd(const sgat_plan* plan, int64_t n, int64_t nnz, const int64_t* rowptr,
+            const int32_t* colidx, int H, int D, int dtype, const void* x_dst, const void* x_nbr,
+            const float* a, float negative_slope, const void* out, const float* lse,
+            const void* dout, void* dx_dst, void* dx_nbr, float* da, void* ws, size_t ws_bytes,
+            void* stream)
+{
+    int rc = check_common(plan, n, nnz, rowptr, colidx, H, D, dtype);
+    if (rc) return rc;
+    for (const void* t : {x_dst, x_nbr, out, dout, static_cast<const void*>(dx_dst),
+                          static_cast<const void*>(dx_nbr)})
+        if ((rc = check_tensor(t, n))) return rc;
+    if (!da || !aligned(da, 4)) return SGAT_INVALID_ARGUMENT;
+    if (n > 0 && (!lse || !aligned(lse, 4) || !a || !aligned(a, 16))) return SGAT_INVALID_ARGUMENT;
+    if (!(negative_slope == negative_slope)) return SGAT_INVALID_ARGUMENT;
+    Layout L;
+    if ((rc = check_ws(plan->p, SGAT_OP_GAT_BWD, H, D, ws, ws_bytes, L))) return rc;
+    if (n == 0) return launch_da_zero(da, H * D, static_cast<hipStream_t>(stream));
+    BwdWs w{at<void>(ws, L.off[0]), at<float>(ws, L.off[1]), at<float>(ws, L.off[2]), nullptr,
+            at<float>(ws, L.off[4])};
+    return launch_gat_bwd(plan->p, H, D, dtype, colidx, x_dst, x_nbr, a, negative_slope, out, lse,
+                          dout, dx_dst, dx_nbr, da, w, static_cast<hipStream_t>(stream));
+}
+
+int sgat_trace_enable(int on)
+{
+    g_trace = on != 0;
+    return SGAT_OK;
+}
+
+int sgat_trace_clear(void)
+{
+    g_used = 0;
+    return SGAT_OK;
+}
+
+int sgat_trace_count(void) { return static_cast<int>(g_used); }
+
+int sgat_trace_get(int index, char* name, size_t name_len, float* ms)
+{
+    if (index < 0 || static_cast<size_t>(index) >= g_used) return SGAT_INVALID_ARGUMENT;
+    const TraceRec& r = g_recs[static_cast<size_t>(index)];
+    if (name && name_len > 0) {
+        std::strncpy(name, r.name.c_str(), name_len - 1);
+        name[name_len - 1] = '\0';
+    }
+    if (ms) {
+        float t = 0.f;
+        if (hipEventElapsedTime(&t, r.start, r.stop) != hipSuccess) return SGAT_HIP_ERROR;
+        *ms = t;
+    }
+    return SGAT_OK;
+}
+
+}  // extern "C"

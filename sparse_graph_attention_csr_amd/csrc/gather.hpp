@@ -1,0 +1,698 @@
+// Gather-path kernels: one wavefront per work item (a whole row, or one chunk
+// of a split row), neighbour rows gathered straight from HBM in 16-byte lane
+// fragments, scores and weights kept in registers.
+//
+// The fused forward computes, per destination i and head h, the scores of its
+// in-edges, an online softmax and the weighted sum of neighbour rows in one
+// pass, so no edge-level value reaches device memory (Yandex Research blog "On
+// efficient scaling of GNNs via IO-aware layer implementations", paragraph on
+// attention-based architectures). Scores are kept in base 2: s2 = s * log2(e).
+//
+// The backward recomputes alpha_ij = exp(s_ij - lse_i) from the forward's
+// per-(node, head) log-sum-exp (same paragraph: recomputation from compact
+// statistics). The CSR pass produces dQ (or dXs and da) and the statistic
+// Delta_i = dout_i . out_i; the transposed-CSR pass produces dK, dV (or dXt)
+// by gathering over each source's out-edges, so no atomics are needed.
+#pragma once
+
+#include "device.hpp"
+
+namespace sgat {
+
+constexpr float kNegInf = -__builtin_huge_valf();
+
+struct RowStat { float lse2; float delta; };   // lse * log2(e), Delta
+
+// ---------------------------------------------------------------------------
+// forward: online softmax over one row (or chunk)
+// ---------------------------------------------------------------------------
+
+// Online-softmax state of one lane: running max m (base 2), sum l and the
+// weighted accumulator of this lane's VEC channels.
+template <int VEC>
+struct Online {
+    float m = kNegInf, l = 0.f;
+    float acc[VEC] = {};
+};
+
+// Merge the states of the EPW edge groups of a wave (log-sum-exp merge).
+template <int VEC, int LPE>
+__device__ __forceinline__ void merge_groups(Online<VEC>& s)
+{
+#pragma unroll
+    for (int off = LPE; off < kWave; off <<= 1) {
+        const float m2 = __shfl_xor(s.m, off);
+        const float l2 = __shfl_xor(s.l, off);
+        const float mn = fmaxf(s.m, m2);
+        const float c1 = s.m == kNegInf ? 0.f : fast_exp2(s.m - mn);
+        const float c2 = m2 == kNegInf ? 0.f : fast_exp2(m2 - mn);
+        s.l = s.l * c1 + l2 * c2;
+#pragma unroll
+        for (int k = 0; k < VEC; ++k) s.acc[k] = s.acc[k] * c1 + __shfl_xor(s.acc[k], off) * c2;
+        s.m = mn;
+    }
+}
+
+template <int VEC, int LPE>
+__device__ __forceinline__ void sum_groups(float (&x)[VEC])
+{
+#pragma unroll
+    for (int off = LPE; off < kWave; off <<= 1)
+#pragma unroll
+        for (int k = 0; k < VEC; ++k) x[k] += __shfl_xor(x[k], off);
+}
+
+// Write a finished row (slot < 0) or a chunk's partial state (slot >= 0).
+template <int DT, int VEC>
+__device__ __forceinline__ void fwd_store(const Online<VEC>& s, const sgat_work_item& it,
+                                          int64_t HD, int H, int head, int col, bool leader,
+                                          void* out, float* lse, float* part_acc, float* part_ml)
+{
+    if (it.slot < 0) {
+        const float inv = s.l > 0.f ? 1.f / s.l : 0.f;
+        float o[VEC];
+#pragma unroll
+        for (int k = 0; k < VEC; ++k) o[k] = s.acc[k] * inv;
+        stg<DT>(out, static_cast<int64_t>(it.row) * HD + col, o);
+        if (leader)
+            lse[static_cast<int64_t>(it.row) * H + head] =
+                s.l > 0.f ? (s.m + __log2f(s.l)) * kLn2 : kNegInf;
+    } else {
+        st_f32<VEC>(part_acc + static_cast<int64_t>(it.slot) * HD + col, s.acc);
+        if (leader) {
+            float2* ml = reinterpret_cast<float2*>(part_ml) + static_cast<int64_t>(it.slot) * H + head;
+            *ml = make_float2(s.m, s.l);
+        }
+    }
+}
+
+struct GtFwdArgs {
+    const sgat_work_item* items;
+    int64_t n_units;
+    int n_hg, H;
+    const int32_t* colidx;
+    const void *Q, *K, *V;
+    void* out;
+    float* lse;
+    float *part_acc, *part_ml;
+    float scale2;   // log2(e) / sqrt(D)
+};
+
+template <int DT, int D, int EPW, int U>
+__global__ __launch_bounds__(kBlock) void gt_fwd_rows(GtFwdArgs a)
+{
+    using G = Geo<DT, D, EPW>;
+    constexpr int VEC = G::VEC;
+    const int64_t unit = logical_block() * kWavesPerBlock + wave_id();
+    if (unit >= a.n_units) return;
+    const int64_t ii = unit / a.n_hg;
+    const int hg = static_cast<int>(unit - ii * a.n_hg);
+    const sgat_work_item it = a.items[ii];
+    const G g(hg, a.H);
+    const int64_t HD = static_cast<int64_t>(a.H) * D;
+
+    Frag q = frag_zero();
+    if (g.hvalid) q = ldg<DT>(a.Q, static_cast<int64_t>(it.row) * HD + g.col);
+    Online<VEC> st;
+    const int32_t* ci = a.colidx + it.begin;
+    for (int base = 0; base < it.len; base += kWave) {
+        const int nb = min(kWave, it.len - base);
+        const int cj = g.lane < nb ? ci[base + g.lane] : 0;
+        for (int t = 0; t < nb; t += EPW * U) {
+            Frag kf[U], vf[U];
+            bool ok[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int e = t + u * EPW + g.sub;
+                ok[u] = e < nb;
+                const int64_t j = bcast<EPW>(cj, e);
+                kf[u] = frag_zero();
+                vf[u] = frag_zero();
+                if (ok[u] && g.hvalid) {
+                    kf[u] = ldg<DT>(a.K, j * HD + g.col);
+                    vf[u] = ldg<DT>(a.V, j * HD + g.col);
+                }
+            }
+            float s[U];
+            float mb = kNegInf;
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const float hs = head_sum<G::SPH>(dot<DT>(q, kf[u])) * a.scale2;
+                s[u] = ok[u] ? hs : kNegInf;
+                mb = fmaxf(mb, s[u]);
+            }
+            const float mn = fmaxf(st.m, mb);
+            const float corr = mn == kNegInf ? 1.f : fast_exp2(st.m - mn);
+            st.l *= corr;
+#pragma unroll
+            for (int k = 0; k < VEC; ++k) st.acc[k] *= corr;
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const float p = ok[u] ? fast_exp2(s[u] - mn) : 0.f;
+                st.l += p;
+                float v[VEC];
+                to_f32<DT>(vf[u], v);
+#pragma unroll
+                for (int k = 0; k < VEC; ++k) st.acc[k] = fmaf(p, v[k], st.acc[k]);
+            }
+            st.m = mn;
+        }
+    }
+    if constexpr (EPW > 1) merge_groups<VEC, G::LPE>(st);
+    if (g.sub == 0 && g.hvalid)
+        fwd_store<DT, VEC>(st, it, HD, a.H, g.head, g.col, g.leader, a.out, a.lse, a.part_acc,
+                           a.part_ml);
+}
+
+struct GatFwdArgs {
+    const sgat_work_item* items;
+    int64_t n_units;
+    int n_hg, H;
+    const int32_t* colidx;
+    const void *Xs, *Xt;
+    const float* att;
+    float slope;
+    void* out;
+    float* lse;
+    float *part_acc, *part_ml;
+};
+
+template <int DT, int D, int EPW, int U>
+__global__ __launch_bounds__(kBlock) void gat_fwd_rows(GatFwdArgs a)
+{
+    using G = Geo<DT, D, EPW>;
+    constexpr int VEC = G::VEC;
+    const int64_t unit = logical_block() * kWavesPerBlock + wave_id();
+    if (unit >= a.n_units) return;
+    const int64_t ii = unit / a.n_hg;
+    const int hg = static_cast<int>(unit - ii * a.n_hg);
+    const sgat_work_item it = a.items[ii];
+    const G g(hg, a.H);
+    const int64_t HD = static_cast<int64_t>(a.H) * D;
+
+    float xs[VEC] = {}, at[VEC] = {};
+    if (g.hvalid) {
+        to_f32<DT>(ldg<DT>(a.Xs, static_cast<int64_t>(it.row) * HD + g.col), xs);
+        ld_f32<VEC>(a.att + g.col, at);
+#pragma unroll
+        for (int k = 0; k < VEC; ++k) at[k] *= kLog2e;
+    }
+    Online<VEC> st;
+    const int32_t* ci = a.colidx + it.begin;
+    for (int base = 0; base < it.len; base += kWave) {
+        const int nb = min(kWave, it.len - base);
+        const int cj = g.lane < nb ? ci[base + g.lane] : 0;
+        for (int t = 0; t < nb; t += EPW * U) {
+            Frag xf[U];
+            bool ok[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int e = t + u * EPW + g.sub;
+                ok[u] = e < nb;
+                const int64_t j = bcast<EPW>(cj, e);
+                xf[u] = frag_zero();
+                if (ok[u] && g.hvalid) xf[u] = ldg<DT>(a.Xt, j * HD + g.col);
+            }
+            float s[U];
+            float mb = kNegInf;
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                float x[VEC];
+                to_f32<DT>(xf[u], x);
+                float part = 0.f;
+#pragma unroll
+                for (int k = 0; k < VEC; ++k) {
+                    const float z = xs[k] + x[k];
+                    part = fmaf(at[k], z > 0.f ? z : a.slope * z, part);
+                }
+                const float hs = head_sum<G::SPH>(part);
+                s[u] = ok[u] ? hs : kNegInf;
+                mb = fmaxf(mb, s[u]);
+            }
+            const float mn = fmaxf(st.m, mb);
+            const float corr = mn == kNegInf ? 1.f : fast_exp2(st.m - mn);
+            st.l *= corr;
+#pragma unroll
+            for (int k = 0; k < VEC; ++k) st.acc[k] *= corr;
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const float p = ok[u] ? fast_exp2(s[u] - mn) : 0.f;
+                st.l += p;
+                float x[VEC];
+                to_f32<DT>(xf[u], x);
+#pragma unroll
+                for (int k = 0; k < VEC; ++k) st.acc[k] = fmaf(p, x[k], st.acc[k]);
+            }
+            st.m = mn;
+        }
+    }
+    if constexpr (EPW > 1) merge_groups<VEC, G::LPE>(st);
+    if (g.sub == 0 && g.hvalid)
+        fwd_store<DT, VEC>(st, it, HD, a.H, g.head, g.col, g.leader, a.out, a.lse, a.part_acc,
+                           a.part_ml);
+}
+
+// Log-sum-exp merge of the chunks of split rows, chunk order fixed.
+struct LseMergeArgs {
+    const sgat_split* splits;
+    int H, D;
+    const float *part_acc, *part_ml;
+    void* out;
+    float* lse;
+};
+
+template <int DT>
+__global__ __launch_bounds__(kBlock) void lse_merge(LseMergeArgs a)
+{
+    const sgat_split sp = a.splits[blockIdx.x];
+    const int HD = a.H * a.D;
+    const float2* ml = reinterpret_cast<const float2*>(a.part_ml);
+    for (int e = threadIdx.x; e < HD; e += blockDim.x) {
+        const int h = e / a.D;
+        float M = kNegInf;
+        for (int k = 0; k < sp.nslots; ++k)
+            M = fmaxf(M, ml[static_cast<int64_t>(sp.first_slot + k) * a.H + h].x);
+        float L = 0.f, A = 0.f;
+        if (M != kNegInf) {
+            for (int k = 0; k < sp.nslots; ++k) {
+                const int64_t s = sp.first_slot + k;
+                const float2 v = ml[s * a.H + h];
+                const float c = v.x == kNegInf ? 0.f : fast_exp2(v.x - M);
+                L = fmaf(v.y, c, L);
+                A = fmaf(a.part_acc[s * HD + e], c, A);
+            }
+        }
+        const float o = L > 0.f ? A / L : 0.f;
+        const int64_t oi = static_cast<int64_t>(sp.row) * HD + e;
+        if constexpr (DT == SGAT_F32) static_cast<float*>(a.out)[oi] = o;
+        else static_cast<__bf16*>(a.out)[oi] = static_cast<__bf16>(o);
+        if (e % a.D == 0)
+            a.lse[static_cast<int64_t>(sp.row) * a.H + h] = L > 0.f ? (M + __log2f(L)) * kLn2 : kNegInf;
+    }
+}
+
+// Fixed-order sum of the partial gradients of split rows (or sources).
+struct SumMergeArgs {
+    const sgat_split* splits;
+    int HD;
+    const float* part;
+    float scale;
+    void* out;
+};
+
+template <int DT>
+__global__ __launch_bounds__(kBlock) void sum_merge(SumMergeArgs a)
+{
+    const sgat_split sp = a.splits[blockIdx.x];
+    for (int e = threadIdx.x; e < a.HD; e += blockDim.x) {
+        float s = 0.f;
+        for (int k = 0; k < sp.nslots; ++k)
+            s += a.part[static_cast<int64_t>(sp.first_slot + k) * a.HD + e];
+        s *= a.scale;
+        const int64_t oi = static_cast<int64_t>(sp.row) * a.HD + e;
+        if constexpr (DT == SGAT_F32) static_cast<float*>(a.out)[oi] = s;
+        else static_cast<__bf16*>(a.out)[oi] = static_cast<__bf16>(s);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// backward, CSR pass
+// ---------------------------------------------------------------------------
+
+template <int DT, int VEC>
+__device__ __forceinline__ void grad_store(const float (&x)[VEC], float scale,
+                                           const sgat_work_item& it, int64_t HD, int col,
+                                           void* out, float* part)
+{
+    if (it.slot < 0) {
+        float o[VEC];
+#pragma unroll
+        for (int k = 0; k < VEC; ++k) o[k] = x[k] * scale;
+        stg<DT>(out, static_cast<int64_t>(it.row) * HD + col, o);
+    } else {
+        st_f32<VEC>(part + static_cast<int64_t>(it.slot) * HD + col, x);
+    }
+}
+
+struct GtBwdRowArgs {
+    const sgat_work_item* items;
+    int64_t n_units;
+    int n_hg, H;
+    const int32_t* colidx;
+    const void *Q, *K, *V, *O, *dO;
+    const float* lse;
+    RowStat* stats;
+    void* dQ;
+    float* part;
+    float scale2;   // log2(e) / sqrt(D)
+    float oscale;   // 1 / sqrt(D)
+};
+
+template <int DT, int D, int EPW, int U>
+__global__ __launch_bounds__(kBlock) void gt_bwd_rows(GtBwdRowArgs a)
+{
+    using G = Geo<DT, D, EPW>;
+    constexpr int VEC = G::VEC;
+    const int64_t unit = logical_block() * kWavesPerBlock + wave_id();
+    if (unit >= a.n_units) return;
+    const int64_t ii = unit / a.n_hg;
+    const int hg = static_cast<int>(unit - ii * a.n_hg);
+    const sgat_work_item it = a.items[ii];
+    const G g(hg, a.H);
+    const int64_t HD = static_cast<int64_t>(a.H) * D;
+    const int64_t ro = static_cast<int64_t>(it.row) * HD + g.col;
+
+    Frag q = frag_zero(), dof = frag_zero(), of = frag_zero();
+    float lse2 = 0.f;
+    if (g.hvalid) {
+        q = ldg<DT>(a.Q, ro);
+        dof = ldg<DT>(a.dO, ro);
+        of = ldg<DT>(a.O, ro);
+        lse2 = a.lse[static_cast<int64_t>(it.row) * a.H + g.head] * kLog2e;
+    }
+    const float delta = head_sum<G::SPH>(dot<DT>(dof, of));
+    if ((it.flags & 1) && g.sub == 0 && g.hvalid && g.leader)
+        a.stats[static_cast<int64_t>(it.row) * a.H + g.head] = RowStat{lse2, delta};
+
+    float dq[VEC] = {};
+    const int32_t* ci = a.colidx + it.begin;
+    for (int base = 0; base < it.len; base += kWave) {
+        const int nb = min(kWave, it.len - base);
+        const int cj = g.lane < nb ? ci[base + g.lane] : 0;
+        for (int t = 0; t < nb; t += EPW * U) {
+            Frag kf[U], vf[U];
+            bool ok[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int e = t + u * EPW + g.sub;
+                ok[u] = e < nb;
+                const int64_t j = bcast<EPW>(cj, e);
+                kf[u] = frag_zero();
+                vf[u] = frag_zero();
+                if (ok[u] && g.hvalid) {
+                    kf[u] = ldg<DT>(a.K, j * HD + g.col);
+                    vf[u] = ldg<DT>(a.V, j * HD + g.col);
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const float s2 = head_sum<G::SPH>(dot<DT>(q, kf[u])) * a.scale2;
+                const float dp = head_sum<G::SPH>(dot<DT>(dof, vf[u]));
+                const float p = ok[u] ? fast_exp2(s2 - lse2) : 0.f;
+                const float ds = p * (dp - delta);
+                float kx[VEC];
+                to_f32<DT>(kf[u], kx);
+#pragma unroll
+                for (int k = 0; k < VEC; ++k) dq[k] = fmaf(ds, kx[k], dq[k]);
+            }
+        }
+    }
+    if constexpr (EPW > 1) sum_groups<VEC, G::LPE>(dq);
+    if (g.sub == 0 && g.hvalid) grad_store<DT, VEC>(dq, a.oscale, it, HD, g.col, a.dQ, a.part);
+}
+
+// GATv2 CSR pass: dXs and the da partials. Grid-stride over items with a
+// fixed grid so the da partials are one per workgroup; blockIdx.y = head group.
+struct GatBwdRowArgs {
+    const sgat_work_item* items;
+    int64_t n_items;
+    int H;
+    const int32_t* colidx;
+    const void *Xs, *Xt, *O, *dO;
+    const float* att;
+    float slope;
+    const float* lse;
+    RowStat* stats;
+    void* dXs;
+    float* part;
+    float* da_part;   // [gridDim.x][H*D]
+};
+
+template <int DT, int D, int EPW, int U>
+__global__ __launch_bounds__(kBlock) void gat_bwd_rows(GatBwdRowArgs a)
+{
+    using G = Geo<DT, D, EPW>;
+    constexpr int VEC = G::VEC;
+    __shared__ float red[kWavesPerBlock][G::LPE * VEC];
+    const int hg = blockIdx.y;
+    const G g(hg, a.H);
+    const int64_t HD = static_cast<int64_t>(a.H) * D;
+    const int wid = wave_id();
+
+    float at[VEC] = {};
+    if (g.hvalid) ld_f32<VEC>(a.att + g.col, at);
+    float da[VEC] = {};
+
+    const int64_t stride = static_cast<int64_t>(gridDim.x) * kWavesPerBlock;
+    for (int64_t ii = static_cast<int64_t>(blockIdx.x) * kWavesPerBlock + wid; ii < a.n_items;
+         ii += stride) {
+        const sgat_work_item it = a.items[ii];
+        const int64_t ro = static_cast<int64_t>(it.row) * HD + g.col;
+        float xs[VEC] = {};
+        Frag dof = frag_zero(), of = frag_zero();
+        float lse2 = 0.f;
+        if (g.hvalid) {
+            to_f32<DT>(ldg<DT>(a.Xs, ro), xs);
+            dof = ldg<DT>(a.dO, ro);
+            of = ldg<DT>(a.O, ro);
+            lse2 = a.lse[static_cast<int64_t>(it.row) * a.H + g.head] * kLog2e;
+        }
+        const float delta = head_sum<G::SPH>(dot<DT>(dof, of));
+        if ((it.flags & 1) && g.sub == 0 && g.hvalid && g.leader)
+            a.stats[static_cast<int64_t>(it.row) * a.H + g.head] = RowStat{lse2, delta};
+
+        float dxs[VEC] = {};
+        const int32_t* ci = a.colidx + it.begin;
+        for (int base = 0; base < it.len; base += kWave) {
+            const int nb = min(kWave, it.len - base);
+            const int cj = g.lane < nb ? ci[base + g.lane] : 0;
+            for (int t = 0; t < nb; t += EPW * U) {
+                Frag xf[U];
+                bool ok[U];
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    const int e = t + u * EPW + g.sub;
+                    ok[u] = e < nb;
+                    const int64_t j = bcast<EPW>(cj, e);
+                    xf[u] = frag_zero();
+                    if (ok[u] && g.hvalid) xf[u] = ldg<DT>(a.Xt, j * HD + g.col);
+                }
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    float x[VEC], z[VEC];
+                    to_f32<DT>(xf[u], x);
+                    float part = 0.f;
+#pragma unroll
+                    for (int k = 0; k < VEC; ++k) {
+                        z[k] = xs[k] + x[k];
+                        part = fmaf(at[k], z[k] > 0.f ? z[k] : a.slope * z[k], part);
+                    }
+                    const float e2 = head_sum<G::SPH>(part) * kLog2e;
+                    const float dp = head_sum<G::SPH>(dot<DT>(dof, xf[u]));
+                    const float p = ok[u] ? fast_exp2(e2 - lse2) : 0.f;
+                    const float dE = p * (dp - delta);
+#pragma unroll
+                    for (int k = 0; k < VEC; ++k) {
+                        const bool pos = z[k] > 0.f;
+                        dxs[k] = fmaf(dE * at[k], pos ? 1.f : a.slope, dxs[k]);
+                        da[k] = fmaf(dE, pos ? z[k] : a.slope * z[k], da[k]);
+                    }
+                }
+            }
+        }
+        if constexpr (EPW > 1) sum_groups<VEC, G::LPE>(dxs);
+        if (g.sub == 0 && g.hvalid) grad_store<DT, VEC>(dxs, 1.f, it, HD, g.col, a.dXs, a.part);
+    }
+    // da: edge groups, then the waves of the block, in fixed order
+    if constexpr (EPW > 1) sum_groups<VEC, G::LPE>(da);
+    if (g.sub == 0) {
+#pragma unroll
+        for (int k = 0; k < VEC; ++k) red[wid][g.pos * VEC + k] = da[k];
+    }
+    __syncthreads();
+    constexpr int W = G::LPE * VEC;   // HG heads * D channels
+    for (int t = threadIdx.x; t < W; t += kBlock) {
+        const int head = hg * G::HG + t / D;
+        if (head >= a.H) continue;
+        float s = 0.f;
+#pragma unroll
+        for (int w = 0; w < kWavesPerBlock; ++w) s += red[w][t];
+        a.da_part[static_cast<int64_t>(blockIdx.x) * HD + head * D + (t % D)] = s;
+    }
+}
+
+struct DaReduceArgs {
+    const float* da_part;
+    int G, HD;
+    float* da;
+};
+
+// ---------------------------------------------------------------------------
+// backward, transposed-CSR pass (one wave per source or source chunk)
+// ---------------------------------------------------------------------------
+
+struct GtBwdColArgs {
+    const sgat_work_item* items;
+    int64_t n_units;
+    int n_hg, H;
+    const int32_t* rowidx;
+    const void *Q, *K, *V, *dO;
+    const RowStat* stats;
+    void *dK, *dV;
+    float *part_k, *part_v;
+    float scale2, oscale;
+};
+
+template <int DT, int D, int EPW, int U>
+__global__ __launch_bounds__(kBlock) void gt_bwd_cols(GtBwdColArgs a)
+{
+    using G = Geo<DT, D, EPW>;
+    constexpr int VEC = G::VEC;
+    const int64_t unit = logical_block() * kWavesPerBlock + wave_id();
+    if (unit >= a.n_units) return;
+    const int64_t ii = unit / a.n_hg;
+    const int hg = static_cast<int>(unit - ii * a.n_hg);
+    const sgat_work_item it = a.items[ii];
+    const G g(hg, a.H);
+    const int64_t HD = static_cast<int64_t>(a.H) * D;
+
+    Frag kj = frag_zero(), vj = frag_zero();
+    if (g.hvalid) {
+        kj = ldg<DT>(a.K, static_cast<int64_t>(it.row) * HD + g.col);
+        vj = ldg<DT>(a.V, static_cast<int64_t>(it.row) * HD + g.col);
+    }
+    float dk[VEC] = {}, dv[VEC] = {};
+    const int32_t* ri = a.rowidx + it.begin;
+    for (int base = 0; base < it.len; base += kWave) {
+        const int nb = min(kWave, it.len - base);
+        const int ci = g.lane < nb ? ri[base + g.lane] : 0;
+        for (int t = 0; t < nb; t += EPW * U) {
+            Frag qf[U], df[U];
+            RowStat rs[U];
+            bool ok[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int e = t + u * EPW + g.sub;
+                ok[u] = e < nb;
+                const int64_t i = bcast<EPW>(ci, e);
+                qf[u] = frag_zero();
+                df[u] = frag_zero();
+                rs[u] = RowStat{0.f, 0.f};
+                if (ok[u] && g.hvalid) {
+                    qf[u] = ldg<DT>(a.Q, i * HD + g.col);
+                    df[u] = ldg<DT>(a.dO, i * HD + g.col);
+                    rs[u] = a.stats[i * a.H + g.head];
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const float s2 = head_sum<G::SPH>(dot<DT>(kj, qf[u])) * a.scale2;
+                const float dp = head_sum<G::SPH>(dot<DT>(df[u], vj));
+                const float p = ok[u] ? fast_exp2(s2 - rs[u].lse2) : 0.f;
+                const float ds = p * (dp - rs[u].delta);
+                float qx[VEC], dx[VEC];
+                to_f32<DT>(qf[u], qx);
+                to_f32<DT>(df[u], dx);
+#pragma unroll
+                for (int k = 0; k < VEC; ++k) {
+                    dv[k] = fmaf(p, dx[k], dv[k]);
+                    dk[k] = fmaf(ds, qx[k], dk[k]);
+                }
+            }
+        }
+    }
+    if constexpr (EPW > 1) {
+        sum_groups<VEC, G::LPE>(dk);
+        sum_groups<VEC, G::LPE>(dv);
+    }
+    if (g.sub == 0 && g.hvalid) {
+        grad_store<DT, VEC>(dk, a.oscale, it, HD, g.col, a.dK, a.part_k);
+        grad_store<DT, VEC>(dv, 1.f, it, HD, g.col, a.dV, a.part_v);
+    }
+}
+
+struct GatBwdColArgs {
+    const sgat_work_item* items;
+    int64_t n_units;
+    int n_hg, H;
+    const int32_t* rowidx;
+    const void *Xs, *Xt, *dO;
+    const float* att;
+    float slope;
+    const RowStat* stats;
+    void* dXt;
+    float* part;
+};
+
+template <int DT, int D, int EPW, int U>
+__global__ __launch_bounds__(kBlock) void gat_bwd_cols(GatBwdColArgs a)
+{
+    using G = Geo<DT, D, EPW>;
+    constexpr int VEC = G::VEC;
+    const int64_t unit = logical_block() * kWavesPerBlock + wave_id();
+    if (unit >= a.n_units) return;
+    const int64_t ii = unit / a.n_hg;
+    const int hg = static_cast<int>(unit - ii * a.n_hg);
+    const sgat_work_item it = a.items[ii];
+    const G g(hg, a.H);
+    const int64_t HD = static_cast<int64_t>(a.H) * D;
+
+    Frag xtf = frag_zero();
+    float xt[VEC] = {}, at[VEC] = {};
+    if (g.hvalid) {
+        xtf = ldg<DT>(a.Xt, static_cast<int64_t>(it.row) * HD + g.col);
+        ld_f32<VEC>(a.att + g.col, at);
+    }
+    to_f32<DT>(xtf, xt);
+    float dxt[VEC] = {};
+    const int32_t* ri = a.rowidx + it.begin;
+    for (int base = 0; base < it.len; base += kWave) {
+        const int nb = min(kWave, it.len - base);
+        const int ci = g.lane < nb ? ri[base + g.lane] : 0;
+        for (int t = 0; t < nb; t += EPW * U) {
+            Frag sf[U], df[U];
+            RowStat rs[U];
+            bool ok[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int e = t + u * EPW + g.sub;
+                ok[u] = e < nb;
+                const int64_t i = bcast<EPW>(ci, e);
+                sf[u] = frag_zero();
+                df[u] = frag_zero();
+                rs[u] = RowStat{0.f, 0.f};
+                if (ok[u] && g.hvalid) {
+                    sf[u] = ldg<DT>(a.Xs, i * HD + g.col);
+                    df[u] = ldg<DT>(a.dO, i * HD + g.col);
+                    rs[u] = a.stats[i * a.H + g.head];
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                float xs[VEC], z[VEC];
+                to_f32<DT>(sf[u], xs);
+                float part = 0.f;
+#pragma unroll
+                for (int k = 0; k < VEC; ++k) {
+                    z[k] = xs[k] + xt[k];
+                    part = fmaf(at[k], z[k] > 0.f ? z[k] : a.slope * z[k], part);
+                }
+                const float e2 = head_sum<G::SPH>(part) * kLog2e;
+                const float dp = head_sum<G::SPH>(dot<DT>(df[u], xtf));
+                const float p = ok[u] ? fast_exp2(e2 - rs[u].lse2) : 0.f;
+                const float dE = p * (dp - rs[u].delta);
+                float dx[VEC];
+                to_f32<DT>(df[u], dx);
+#pragma unroll
+                for (int k = 0; k < VEC; ++k) {
+                    const float gz = z[k] > 0.f ? 1.f : a.slope;
+                    dxt[k] = fmaf(p, dx[k], fmaf(dE * at[k], gz, dxt[k]));
+                }
+            }
+        }
+    }
+    if constexpr (EPW > 1) sum_groups<VEC, G::LPE>(dxt);
+    if (g.sub == 0 && g.hvalid) grad_store<DT, VEC>(dxt, 1.f, it, HD, g.col, a.dXt, a.part);
+}
+
+}  // namespace sgat

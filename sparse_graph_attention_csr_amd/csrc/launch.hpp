@@ -1,0 +1,69 @@
+// Internal host interface between the C ABI and the kernel launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <cstdint>
+
+#include "device.hpp"
+#include "plan.hpp"
+
+namespace sgat {
+
+// Work decomposition for element type dt, head dim D and H heads: lanes per
+// head SPH = D / VEC; a head group is the largest power of two of heads (at
+// most H rounded up) whose 16-byte fragments fit 64 lanes; EPW = edges a wave
+// processes side by side; n_hg = head groups per row.
+struct Decomp {
+    int vec, sph, hg, epw, n_hg;
+};
+Decomp decompose(int dt, int D, int H);
+
+// Grid of the GATv2 CSR backward pass (its da partials are one per workgroup).
+int gat_bwd_row_blocks(const Plan& p);
+
+struct FwdWs {
+    float* part_acc;   // [row_slots][H*D]
+    float* part_ml;    // [row_slots][H][2]
+};
+struct BwdWs {
+    void* stats;       // [n][H] (lse * log2 e, Delta)
+    float* part_row;   // [row_slots][H*D]
+    float* part_col0;  // [col_slots][H*D]
+    float* part_col1;  // [col_slots][H*D] (GT only)
+    float* da_part;    // [gat_bwd_row_blocks][H*D] (GATv2 only)
+};
+
+int launch_gt_fwd(const Plan& p, int H, int D, int dt, const int32_t* colidx, const void* Q,
+                  const void* K, const void* V, void* out, float* lse, const FwdWs& ws,
+                  hipStream_t s);
+int launch_gt_bwd(const Plan& p, int H, int D, int dt, const int32_t* colidx, const void* Q,
+                  const void* K, const void* V, const void* O, const float* lse, const void* dO,
+                  void* dQ, void* dK, void* dV, const BwdWs& ws, hipStream_t s);
+int launch_gat_fwd(const Plan& p, int H, int D, int dt, const int32_t* colidx, const void* Xs,
+                   const void* Xt, const float* att, float slope, void* out, float* lse,
+                   const FwdWs& ws, hipStream_t s);
+int launch_gat_bwd(const Plan& p, int H, int D, int dt, const int32_t* colidx, const void* Xs,
+                   const void* Xt, const float* att, float slope, const void* O, const float* lse,
+                   const void* dO, void* dXs, void* dXt, float* da, const BwdWs& ws,
+                   hipStream_t s);
+
+// da = 0 (the empty sum, for a graph without nodes), by a kernel.
+int launch_da_zero(float* da, int HD, hipStream_t s);
+
+// Launch one kernel through hipLaunchKernel, bracketed by trace events when
+// tracing is on. Returns SGAT_OK or SGAT_HIP_ERROR.
+int launch(const char* name, const void* fn, dim3 grid, dim3 block, void* arg, hipStream_t s);
+
+// Blocks for `units` one-wave units, rounded up to the XCD remap quantum.
+int64_t wave_grid(int64_t units);
+
+}  // namespace sgat
+
+// Every (dtype, D, EPW) the gather kernels are compiled for.
+#define SGAT_GATHER_CONFIGS(X)                                                        \
+    X(SGAT_BF16, 32, 1) X(SGAT_BF16, 32, 2) X(SGAT_BF16, 32, 4) X(SGAT_BF16, 32, 8)   \
+    X(SGAT_BF16, 32, 16) X(SGAT_BF16, 64, 1) X(SGAT_BF16, 64, 2) X(SGAT_BF16, 64, 4)  \
+    X(SGAT_BF16, 64, 8) X(SGAT_BF16, 128, 1) X(SGAT_BF16, 128, 2) X(SGAT_BF16, 128, 4) \
+    X(SGAT_F32, 32, 1) X(SGAT_F32, 32, 2) X(SGAT_F32, 32, 4) X(SGAT_F32, 32, 8)       \
+    X(SGAT_F32, 64, 1) X(SGAT_F32, 64, 2) X(SGAT_F32, 64, 4) X(SGAT_F32, 128, 1)      \
+    X(SGAT_F32, 128, 2)

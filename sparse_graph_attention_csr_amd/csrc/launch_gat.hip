@@ -1,0 +1,156 @@
+// GATv2 launchers: forward rows (+ log-sum-exp merge), backward CSR pass with
+// da partials (+ merge, + fixed-order da reduction), transposed-CSR pass (+ merge).
+#include <algorithm>
+
+#include "gather.hpp"
+#include "launch.hpp"
+
+namespace sgat {
+
+namespace {
+constexpr int kUnrollFwd = 8;
+constexpr int kUnrollBwd = 4;
+constexpr int kGatBwdMaxBlocks = 2048;
+}
+
+// Fixed-order sum of the per-workgroup da partials.
+__global__ __launch_bounds__(kBlock) void da_reduce(DaReduceArgs a)
+{
+    for (int e = blockIdx.x * blockDim.x + threadIdx.x; e < a.HD; e += gridDim.x * blockDim.x) {
+        float s = 0.f;
+        for (int b = 0; b < a.G; ++b) s += a.da_part[static_cast<int64_t>(b) * a.HD + e];
+        a.da[e] = s;
+    }
+}
+
+
+int gat_bwd_row_blocks(const Plan& p)
+{
+    const int64_t need = (static_cast<int64_t>(p.row_items.size()) + kWavesPerBlock - 1) / kWavesPerBlock;
+    return static_cast<int>(std::max<int64_t>(1, std::min<int64_t>(need, kGatBwdMaxBlocks)));
+}
+
+int launch_da_zero(float* da, int HD, hipStream_t s)
+{
+    DaReduceArgs d{nullptr, 0, HD, da};
+    return launch("gat_bwd_da_reduce", reinterpret_cast<const void*>(&da_reduce),
+                  dim3(static_cast<unsigned>((HD + kBlock - 1) / kBlock)), dim3(kBlock), &d, s);
+}
+
+int launch_gat_fwd(const Plan& p, int H, int D, int dt, const int32_t* colidx, const void* Xs,
+                   const void* Xt, const float* att, float slope, void* out, float* lse,
+                   const FwdWs& ws, hipStream_t s)
+{
+    const Decomp dc = decompose(dt, D, H);
+    GatFwdArgs a;
+    a.items = p.dptr<sgat_work_item>(SGAT_ARR_ROW_ITEMS);
+    a.n_units = static_cast<int64_t>(p.row_items.size()) * dc.n_hg;
+    a.n_hg = dc.n_hg;
+    a.H = H;
+    a.colidx = colidx;
+    a.Xs = Xs; a.Xt = Xt;
+    a.att = att;
+    a.slope = slope;
+    a.out = out;
+    a.lse = lse;
+    a.part_acc = ws.part_acc;
+    a.part_ml = ws.part_ml;
+    const void* fn = nullptr;
+#define X(DT_, D_, E_) \
+    if (dt == DT_ && D == D_ && dc.epw == E_) fn = reinterpret_cast<const void*>(&gat_fwd_rows<DT_, D_, E_, kUnrollFwd>);
+    SGAT_GATHER_CONFIGS(X)
+#undef X
+    if (!fn) return SGAT_INVALID_ARGUMENT;
+    if (a.n_units > 0) {
+        int rc = launch("gat_fwd_rows", fn, dim3(static_cast<unsigned>(wave_grid(a.n_units))),
+                        dim3(kBlock), &a, s);
+        if (rc) return rc;
+    }
+    if (!p.row_splits.empty()) {
+        LseMergeArgs m{p.dptr<sgat_split>(SGAT_ARR_ROW_SPLITS), H, D, ws.part_acc, ws.part_ml,
+                       out, lse};
+        const void* mf = dt == SGAT_F32 ? reinterpret_cast<const void*>(&lse_merge<SGAT_F32>)
+                                        : reinterpret_cast<const void*>(&lse_merge<SGAT_BF16>);
+        int rc = launch("gat_fwd_merge", mf, dim3(static_cast<unsigned>(p.row_splits.size())),
+                        dim3(kBlock), &m, s);
+        if (rc) return rc;
+    }
+    return SGAT_OK;
+}
+
+int launch_gat_bwd(const Plan& p, int H, int D, int dt, const int32_t* colidx, const void* Xs,
+                   const void* Xt, const float* att, float slope, const void* O, const float* lse,
+                   const void* dO, void* dXs, void* dXt, float* da, const BwdWs& ws,
+                   hipStream_t s)
+{
+    const Decomp dc = decompose(dt, D, H);
+    const int HD = H * D;
+    const int gx = gat_bwd_row_blocks(p);
+
+    GatBwdRowArgs r;
+    r.items = p.dptr<sgat_work_item>(SGAT_ARR_ROW_ITEMS);
+    r.n_items = static_cast<int64_t>(p.row_items.size());
+    r.H = H;
+    r.colidx = colidx;
+    r.Xs = Xs; r.Xt = Xt; r.O = O; r.dO = dO;
+    r.att = att;
+    r.slope = slope;
+    r.lse = lse;
+    r.stats = static_cast<RowStat*>(ws.stats);
+    r.dXs = dXs;
+    r.part = ws.part_row;
+    r.da_part = ws.da_part;
+
+    GatBwdColArgs c;
+    c.items = p.dptr<sgat_work_item>(SGAT_ARR_COL_ITEMS);
+    c.n_units = static_cast<int64_t>(p.col_items.size()) * dc.n_hg;
+    c.n_hg = dc.n_hg;
+    c.H = H;
+    c.rowidx = p.dptr<int32_t>(SGAT_ARR_ROWIDX);
+    c.Xs = Xs; c.Xt = Xt; c.dO = dO;
+    c.att = att;
+    c.slope = slope;
+    c.stats = static_cast<const RowStat*>(ws.stats);
+    c.dXt = dXt;
+    c.part = ws.part_col0;
+
+    const void *fr = nullptr, *fc = nullptr;
+#define X(DT_, D_, E_)                                                                 \
+    if (dt == DT_ && D == D_ && dc.epw == E_) {                                        \
+        fr = reinterpret_cast<const void*>(&gat_bwd_rows<DT_, D_, E_, kUnrollBwd>);    \
+        fc = reinterpret_cast<const void*>(&gat_bwd_cols<DT_, D_, E_, kUnrollBwd>);    \
+    }
+    SGAT_GATHER_CONFIGS(X)
+#undef X
+    if (!fr || !fc) return SGAT_INVALID_ARGUMENT;
+    const void* msum = dt == SGAT_F32 ? reinterpret_cast<const void*>(&sum_merge<SGAT_F32>)
+                                      : reinterpret_cast<const void*>(&sum_merge<SGAT_BF16>);
+    int rc;
+    // the row pass always runs: it writes the da partials of every workgroup
+    if ((rc = launch("gat_bwd_rows", fr, dim3(static_cast<unsigned>(gx), static_cast<unsigned>(dc.n_hg)),
+                     dim3(kBlock), &r, s)))
+        return rc;
+    if (!p.row_splits.empty()) {
+        SumMergeArgs m{p.dptr<sgat_split>(SGAT_ARR_ROW_SPLITS), HD, ws.part_row, 1.f, dXs};
+        if ((rc = launch("gat_bwd_rows_merge", msum, dim3(static_cast<unsigned>(p.row_splits.size())),
+                         dim3(kBlock), &m, s)))
+            return rc;
+    }
+    DaReduceArgs d{ws.da_part, gx, HD, da};
+    if ((rc = launch("gat_bwd_da_reduce", reinterpret_cast<const void*>(&da_reduce),
+                     dim3(static_cast<unsigned>((HD + kBlock - 1) / kBlock)), dim3(kBlock), &d, s)))
+        return rc;
+    if (c.n_units > 0 &&
+        (rc = launch("gat_bwd_cols", fc, dim3(static_cast<unsigned>(wave_grid(c.n_units))),
+                     dim3(kBlock), &c, s)))
+        return rc;
+    if (!p.col_splits.empty()) {
+        SumMergeArgs m{p.dptr<sgat_split>(SGAT_ARR_COL_SPLITS), HD, ws.part_col0, 1.f, dXt};
+        if ((rc = launch("gat_bwd_cols_merge", msum, dim3(static_cast<unsigned>(p.col_splits.size())),
+                         dim3(kBlock), &m, s)))
+            return rc;
+    }
+    return SGAT_OK;
+}
+
+}  // namespace sgat

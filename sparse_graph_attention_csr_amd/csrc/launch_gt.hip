@@ -1,0 +1,129 @@
+// Graph Transformer launchers: forward rows (+ log-sum-exp merge of split
+// rows), backward CSR pass (+ merge), backward transposed-CSR pass (+ merge).
+#include "gather.hpp"
+#include "launch.hpp"
+
+namespace sgat {
+
+namespace {
+constexpr int kUnrollFwd = 8;
+constexpr int kUnrollBwd = 4;
+}
+
+int launch_gt_fwd(const Plan& p, int H, int D, int dt, const int32_t* colidx, const void* Q,
+                  const void* K, const void* V, void* out, float* lse, const FwdWs& ws,
+                  hipStream_t s)
+{
+    const Decomp dc = decompose(dt, D, H);
+    GtFwdArgs a;
+    a.items = p.dptr<sgat_work_item>(SGAT_ARR_ROW_ITEMS);
+    a.n_units = static_cast<int64_t>(p.row_items.size()) * dc.n_hg;
+    a.n_hg = dc.n_hg;
+    a.H = H;
+    a.colidx = colidx;
+    a.Q = Q; a.K = K; a.V = V;
+    a.out = out;
+    a.lse = lse;
+    a.part_acc = ws.part_acc;
+    a.part_ml = ws.part_ml;
+    a.scale2 = kLog2e / sqrtf(static_cast<float>(D));
+    const void* fn = nullptr;
+#define X(DT_, D_, E_) \
+    if (dt == DT_ && D == D_ && dc.epw == E_) fn = reinterpret_cast<const void*>(&gt_fwd_rows<DT_, D_, E_, kUnrollFwd>);
+    SGAT_GATHER_CONFIGS(X)
+#undef X
+    if (!fn) return SGAT_INVALID_ARGUMENT;
+    if (a.n_units > 0) {
+        int rc = launch("gt_fwd_rows", fn, dim3(static_cast<unsigned>(wave_grid(a.n_units))),
+                        dim3(kBlock), &a, s);
+        if (rc) return rc;
+    }
+    if (!p.row_splits.empty()) {
+        LseMergeArgs m{p.dptr<sgat_split>(SGAT_ARR_ROW_SPLITS), H, D, ws.part_acc, ws.part_ml,
+                       out, lse};
+        const void* mf = dt == SGAT_F32 ? reinterpret_cast<const void*>(&lse_merge<SGAT_F32>)
+                                        : reinterpret_cast<const void*>(&lse_merge<SGAT_BF16>);
+        int rc = launch("gt_fwd_merge", mf, dim3(static_cast<unsigned>(p.row_splits.size())),
+                        dim3(kBlock), &m, s);
+        if (rc) return rc;
+    }
+    return SGAT_OK;
+}
+
+static int merge_sum(const char* name, const std::vector<sgat_split>& sp, const sgat_split* dsp,
+                     int HD, const float* part, float scale, void* out, int dt, hipStream_t s)
+{
+    if (sp.empty()) return SGAT_OK;
+    SumMergeArgs m{dsp, HD, part, scale, out};
+    const void* mf = dt == SGAT_F32 ? reinterpret_cast<const void*>(&sum_merge<SGAT_F32>)
+                                    : reinterpret_cast<const void*>(&sum_merge<SGAT_BF16>);
+    return launch(name, mf, dim3(static_cast<unsigned>(sp.size())), dim3(kBlock), &m, s);
+}
+
+int launch_gt_bwd(const Plan& p, int H, int D, int dt, const int32_t* colidx, const void* Q,
+                  const void* K, const void* V, const void* O, const float* lse, const void* dO,
+                  void* dQ, void* dK, void* dV, const BwdWs& ws, hipStream_t s)
+{
+    const Decomp dc = decompose(dt, D, H);
+    const float scale2 = kLog2e / sqrtf(static_cast<float>(D));
+    const float oscale = 1.f / sqrtf(static_cast<float>(D));
+    const int HD = H * D;
+
+    GtBwdRowArgs r;
+    r.items = p.dptr<sgat_work_item>(SGAT_ARR_ROW_ITEMS);
+    r.n_units = static_cast<int64_t>(p.row_items.size()) * dc.n_hg;
+    r.n_hg = dc.n_hg;
+    r.H = H;
+    r.colidx = colidx;
+    r.Q = Q; r.K = K; r.V = V; r.O = O; r.dO = dO;
+    r.lse = lse;
+    r.stats = static_cast<RowStat*>(ws.stats);
+    r.dQ = dQ;
+    r.part = ws.part_row;
+    r.scale2 = scale2;
+    r.oscale = oscale;
+
+    GtBwdColArgs c;
+    c.items = p.dptr<sgat_work_item>(SGAT_ARR_COL_ITEMS);
+    c.n_units = static_cast<int64_t>(p.col_items.size()) * dc.n_hg;
+    c.n_hg = dc.n_hg;
+    c.H = H;
+    c.rowidx = p.dptr<int32_t>(SGAT_ARR_ROWIDX);
+    c.Q = Q; c.K = K; c.V = V; c.dO = dO;
+    c.stats = static_cast<const RowStat*>(ws.stats);
+    c.dK = dK; c.dV = dV;
+    c.part_k = ws.part_col0;
+    c.part_v = ws.part_col1;
+    c.scale2 = scale2;
+    c.oscale = oscale;
+
+    const void *fr = nullptr, *fc = nullptr;
+#define X(DT_, D_, E_)                                                                 \
+    if (dt == DT_ && D == D_ && dc.epw == E_) {                                        \
+        fr = reinterpret_cast<const void*>(&gt_bwd_rows<DT_, D_, E_, kUnrollBwd>);     \
+        fc = reinterpret_cast<const void*>(&gt_bwd_cols<DT_, D_, E_, kUnrollBwd>);     \
+    }
+    SGAT_GATHER_CONFIGS(X)
+#undef X
+    if (!fr || !fc) return SGAT_INVALID_ARGUMENT;
+    int rc;
+    if (r.n_units > 0 &&
+        (rc = launch("gt_bwd_rows", fr, dim3(static_cast<unsigned>(wave_grid(r.n_units))),
+                     dim3(kBlock), &r, s)))
+        return rc;
+    if ((rc = merge_sum("gt_bwd_rows_merge", p.row_splits,
+                        p.dptr<sgat_split>(SGAT_ARR_ROW_SPLITS), HD, ws.part_row, oscale, dQ, dt,
+                        s)))
+        return rc;
+    if (c.n_units > 0 &&
+        (rc = launch("gt_bwd_cols", fc, dim3(static_cast<unsigned>(wave_grid(c.n_units))),
+                     dim3(kBlock), &c, s)))
+        return rc;
+    const sgat_split* csp = p.dptr<sgat_split>(SGAT_ARR_COL_SPLITS);
+    if ((rc = merge_sum("gt_bwd_cols_merge", p.col_splits, csp, HD, ws.part_col0, oscale, dK, dt,
+                        s)))
+        return rc;
+    return merge_sum("gt_bwd_cols_merge", p.col_splits, csp, HD, ws.part_col1, 1.f, dV, dt, s);
+}
+
+}  // namespace sgat

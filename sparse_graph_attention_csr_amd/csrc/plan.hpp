@@ -1,0 +1,78 @@
+// Host-side plan: the integer preprocessing of one CSR graph.
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+#include <vector>
+
+#include "sgattn.h"
+
+namespace sgat {
+
+constexpr int64_t kDefaultChunk = 512;
+constexpr int32_t kDefaultTileMinNnz = 32;
+constexpr int kTile = 16;
+constexpr size_t kAlign = 256;
+
+inline size_t align_up(size_t x, size_t a = kAlign) { return (x + a - 1) / a * a; }
+
+struct Plan {
+    int64_t n = 0, nnz = 0;
+    int64_t chunk = kDefaultChunk;
+    int32_t tile_min_nnz = kDefaultTileMinNnz;
+    bool block_sparse = false;
+    int64_t max_in_degree = 0, max_out_degree = 0;
+
+    std::vector<sgat_work_item> row_items;
+    std::vector<sgat_split> row_splits;
+    int64_t row_slots = 0;
+
+    std::vector<int64_t> colptr;
+    std::vector<int32_t> rowidx;
+    std::vector<sgat_work_item> col_items;
+    std::vector<sgat_split> col_splits;
+    int64_t col_slots = 0;
+
+    std::vector<int64_t> tile_rowptr;
+    std::vector<int32_t> tile_col;
+    std::vector<uint16_t> tile_mask;   // [tiles][16]
+    std::vector<int64_t> res_rowptr;
+    std::vector<int32_t> res_colidx;
+    int64_t tile_edges = 0;
+
+    // device image: every array at a 256-byte aligned offset of one buffer
+    size_t offset[SGAT_ARR_COUNT] = {};
+    size_t bytes[SGAT_ARR_COUNT] = {};
+    size_t device_bytes = 0;
+    const unsigned char* dev = nullptr;
+    bool uploaded = false;
+
+    const void* host_array(int id) const;
+    void layout();
+    template <class T>
+    const T* dptr(int id) const { return reinterpret_cast<const T*>(dev + offset[id]); }
+};
+
+// A1: returns SGAT_OK or SGAT_INVALID_CSR / SGAT_INVALID_ARGUMENT.
+int validate_csr(int64_t n, int64_t nnz, const int64_t* rowptr, const int32_t* colidx);
+
+// A2: degree-binned work list over any CSR-like pointer array.
+void build_work_list(int64_t n, const int64_t* ptr, int64_t chunk,
+                     std::vector<sgat_work_item>& items, std::vector<sgat_split>& splits,
+                     int64_t& nslots);
+
+// A3: transposed CSR by stable counting sort of edges by source.
+void build_transpose(int64_t n, const int64_t* rowptr, const int32_t* colidx,
+                     std::vector<int64_t>& colptr, std::vector<int32_t>& rowidx);
+
+// A4: 16x16 dense tiles with at least `min_nnz` distinct edges, plus residual CSR.
+void build_tiles(int64_t n, const int64_t* rowptr, const int32_t* colidx, int32_t min_nnz,
+                 std::vector<int64_t>& tile_rowptr, std::vector<int32_t>& tile_col,
+                 std::vector<uint16_t>& tile_mask, std::vector<int64_t>& res_rowptr,
+                 std::vector<int32_t>& res_colidx, int64_t& tile_edges);
+
+}  // namespace sgat
+
+struct sgat_plan {
+    sgat::Plan p;
+};

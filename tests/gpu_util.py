@@ -1,0 +1,105 @@
+"""Helpers for the GPU tests: move seeded host arrays to the device, run the
+library's entry points through the binding, bring results back as fp64."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+
+TOL = {"f32": 1e-4, "bf16": 2e-2}   # max abs error relative to the output's max abs value
+
+
+def note(msg: str):
+    print(f"[gpu] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def dev(arr: np.ndarray, device="cuda"):
+    import torch
+    if arr.dtype == np.uint16:
+        return torch.from_numpy(np.ascontiguousarray(arr).view(np.int16)).to(device).view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(arr, dtype=np.float32)).to(device)
+
+
+def host(t) -> np.ndarray:
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def widen(arr: np.ndarray) -> np.ndarray:
+    """Exact fp64 values of fp32 arrays or bf16 bit patterns."""
+    if arr.dtype == np.uint16:
+        return (arr.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    return arr.astype(np.float64)
+
+
+def rel_err(gpu, ref) -> float:
+    gpu = np.asarray(gpu, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    fin = np.isfinite(ref)
+    if not np.array_equal(np.isfinite(gpu), fin):
+        return float("inf")
+    if not np.array_equal(gpu[~fin], ref[~fin]):
+        return float("inf")
+    if not fin.any():
+        return 0.0
+    scale = np.abs(ref[fin]).max()
+    if scale == 0:
+        return float(np.abs(gpu[fin]).max())
+    return float(np.abs(gpu[fin] - ref[fin]).max() / scale)
+
+
+def row_rel_err(gpu, ref) -> float:
+    """Worst per-(row, head) relative error (rows x heads x channels)."""
+    worst = 0.0
+    for r in range(ref.shape[0]):
+        for h in range(ref.shape[1]):
+            worst = max(worst, rel_err(gpu[r, h], ref[r, h]))
+    return worst
+
+
+class Runner:
+    """Runs the four entry points on one DeviceGraph."""
+
+    def __init__(self, rowptr, colidx, **plan_kw):
+        from sparse_graph_attention_csr_amd import binding as B
+        self.B = B
+        self.g = B.DeviceGraph(rowptr, colidx, **plan_kw)
+
+    def gt_fwd(self, q, k, v):
+        import torch
+        B, g = self.B, self.g
+        n, H, D = q.shape
+        out = torch.empty_like(q)
+        lse = torch.empty((n, H), dtype=torch.float32, device=q.device)
+        ws = g.workspace(B.OP_GT_FWD, H, D, B._dtype_code(q))
+        B.gt_fwd(g.plan, g.rowptr, g.colidx, q, k, v, out, lse, ws)
+        return out, lse
+
+    def gt_bwd(self, q, k, v, out, lse, dout):
+        import torch
+        B, g = self.B, self.g
+        n, H, D = q.shape
+        dq, dk, dv = (torch.empty_like(q) for _ in range(3))
+        ws = g.workspace(B.OP_GT_BWD, H, D, B._dtype_code(q))
+        B.gt_bwd(g.plan, g.rowptr, g.colidx, q, k, v, out, lse, dout, dq, dk, dv, ws)
+        return dq, dk, dv
+
+    def gat_fwd(self, xs, xt, a, slope=0.2):
+        import torch
+        B, g = self.B, self.g
+        n, H, D = xs.shape
+        out = torch.empty_like(xs)
+        lse = torch.empty((n, H), dtype=torch.float32, device=xs.device)
+        ws = g.workspace(B.OP_GAT_FWD, H, D, B._dtype_code(xs))
+        B.gat_fwd(g.plan, g.rowptr, g.colidx, xs, xt, a, slope, out, lse, ws)
+        return out, lse
+
+    def gat_bwd(self, xs, xt, a, out, lse, dout, slope=0.2):
+        import torch
+        B, g = self.B, self.g
+        n, H, D = xs.shape
+        dxs, dxt = torch.empty_like(xs), torch.empty_like(xs)
+        da = torch.empty((H, D), dtype=torch.float32, device=xs.device)
+        ws = g.workspace(B.OP_GAT_BWD, H, D, B._dtype_code(xs))
+        B.gat_bwd(g.plan, g.rowptr, g.colidx, xs, xt, a, slope, out, lse, dout, dxs, dxt, da, ws)
+        return dxs, dxt, da

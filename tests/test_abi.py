@@ -1,0 +1,131 @@
+"""The C ABI without a GPU: the library loads, exports every function the
+header declares, and rejects invalid arguments with the documented status
+before any HIP call (fake non-null device pointers are never dereferenced)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from sparse_graph_attention_csr_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def header_functions():
+    src = open(os.path.join(ROOT, "include", "sgattn.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(\w+)\s*\(", src, flags=re.M)
+    return sorted(set(names))
+
+
+def test_library_exports_every_declared_function():
+    names = header_functions()
+    assert len(names) >= 17
+    L = B.lib()
+    missing = [n for n in names if not hasattr(L, n)]
+    assert not missing, missing
+    assert set(names) == set(B._SIGS), "binding signatures out of sync with the header"
+
+
+def test_status_strings():
+    for st in range(9):
+        assert B.status_string(st) != "unknown status"
+    assert B.status_string(99) == "unknown status"
+
+
+FAKE = 1 << 20   # aligned, non-null, never dereferenced
+
+
+@pytest.fixture()
+def plan():
+    rp = np.array([0, 2, 3, 3, 5], dtype=np.int64)
+    ci = np.array([0, 1, 2, 1, 3], dtype=np.int32)
+    return B.Plan(rp, ci, chunk=1)
+
+
+def call_gt_fwd(plan, n=None, nnz=None, H=2, D=32, dt=0, q=FAKE, lse=FAKE, ws=FAKE, wsb=1 << 30,
+                tiles=0):
+    return B.lib().gt_fwd(plan.handle if plan is not None else None,
+                          plan.n if n is None else n, plan.nnz if nnz is None else nnz,
+                          FAKE, FAKE, H, D, dt, q, FAKE, FAKE, FAKE, lse, ws, wsb, tiles, None)
+
+
+def test_gt_fwd_argument_checks(plan):
+    L = B.lib()
+    assert L.gt_fwd(None, 4, 5, FAKE, FAKE, 2, 32, 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, 0,
+                    None) == 1
+    assert call_gt_fwd(plan, H=0) == 1
+    assert call_gt_fwd(plan, H=17) == 1
+    assert call_gt_fwd(plan, D=48) == 1
+    assert call_gt_fwd(plan, dt=2) == 1
+    assert call_gt_fwd(plan, n=5) == 4
+    assert call_gt_fwd(plan, nnz=4) == 4
+    assert call_gt_fwd(plan) == 6            # not uploaded
+
+
+def test_workspace_bytes(plan):
+    s = plan.stats()
+    assert s["row_splits"] == 2 and s["row_slots"] == 4
+    for op in range(4):
+        for dt in (0, 1):
+            nb = plan.workspace_bytes(op, 2, 32, dt)
+            assert nb % 256 == 0
+    # forward: partial accumulators and (max, sum) per slot, each region 256-aligned
+    HD = 2 * 32
+    fwd = plan.workspace_bytes(B.OP_GT_FWD, 2, 32, 1)
+    assert fwd == (-(-4 * HD * 4 // 256) * 256) + (-(-4 * 2 * 8 // 256) * 256)
+    with pytest.raises(B.SgatError):
+        plan.workspace_bytes(7, 2, 32, 0)
+    with pytest.raises(B.SgatError):
+        plan.workspace_bytes(0, 2, 40, 0)
+
+
+def test_upload_checks(plan):
+    L = B.lib()
+    nb = plan.device_bytes()
+    assert nb > 0 and nb % 256 == 0
+    assert L.sgat_plan_upload(plan.handle, None, nb, None) == 1
+    assert L.sgat_plan_upload(plan.handle, FAKE, nb - 1, None) == 3
+    assert L.sgat_plan_upload(plan.handle, FAKE + 8, nb, None) == 1
+
+
+def test_export_checks(plan):
+    L = B.lib()
+    b = ctypes.c_size_t()
+    assert L.sgat_plan_array_bytes(plan.handle, 11, ctypes.byref(b)) == 1
+    assert L.sgat_plan_array_bytes(plan.handle, B.ARR_ROW_ITEMS, ctypes.byref(b)) == 0
+    assert b.value == plan.stats()["row_items"] * 24
+    buf = ctypes.create_string_buffer(b.value)
+    assert L.sgat_plan_export(plan.handle, B.ARR_ROW_ITEMS, buf, b.value - 1) == 3
+
+
+def test_other_entry_points_check_arguments(plan):
+    L = B.lib()
+    n, nnz = plan.n, plan.nnz
+    args_bwd = [FAKE] * 9
+    assert L.gt_bwd(plan.handle, n, nnz, FAKE, FAKE, 2, 64, 1, *args_bwd, FAKE, 1 << 30, 0,
+                    None) == 6
+    assert L.gt_bwd(plan.handle, n + 1, nnz, FAKE, FAKE, 2, 64, 1, *args_bwd, FAKE, 1 << 30, 0,
+                    None) == 4
+    assert L.gat_fwd(plan.handle, n, nnz, FAKE, FAKE, 2, 64, 1, FAKE, FAKE, FAKE, 0.2, FAKE, FAKE,
+                     FAKE, 1 << 30, None) == 6
+    assert L.gat_fwd(plan.handle, n, nnz, FAKE, FAKE, 2, 64, 3, FAKE, FAKE, FAKE, 0.2, FAKE, FAKE,
+                     FAKE, 1 << 30, None) == 1
+    assert L.gat_bwd(plan.handle, n, nnz, FAKE, FAKE, 2, 64, 1, FAKE, FAKE, FAKE, 0.2, FAKE, FAKE,
+                     FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30, None) == 6
+    assert L.gat_bwd(None, n, nnz, FAKE, FAKE, 2, 64, 1, FAKE, FAKE, FAKE, 0.2, FAKE, FAKE,
+                     FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30, None) == 1
+
+
+def test_plan_create_null_out():
+    rp = np.array([0, 0], dtype=np.int64)
+    assert B.lib().sgat_plan_create(1, 0, rp.ctypes.data, None, None, None) == 1
+
+
+def test_trace_api_without_launches():
+    B.trace_enable(True)
+    B.trace_clear()
+    assert B.trace_read() == []
+    B.trace_enable(False)

@@ -1,0 +1,175 @@
+"""GPU parity against the fp64 oracle, element by element, on small seeded
+graphs that span several work items, split rows (chunks merged by
+log-sum-exp), split sources, empty rows, repeated edges and every lane layout
+(edges per wave, head groups, padded heads) the kernels are compiled for.
+
+Bar: max |gpu - oracle| / max |oracle| per output tensor <= 1e-4 for fp32
+inputs and <= 2e-2 for bf16 inputs (fp32 accumulation)."""
+import numpy as np
+import pytest
+
+import oracle
+from sparse_graph_attention_csr_amd import inputs as I
+from tests.gpu_util import TOL, Runner, dev, host, note, rel_err, widen
+
+pytestmark = pytest.mark.gpu
+
+# (dtype, H, D): covers EPW = 1, 2, 4, 16, several head groups, padded heads
+LAYOUTS = [
+    ("f32", 4, 32), ("f32", 1, 64), ("f32", 3, 128), ("f32", 16, 32),
+    ("bf16", 4, 128), ("bf16", 8, 64), ("bf16", 2, 64), ("bf16", 1, 32),
+    ("bf16", 5, 32), ("bf16", 16, 128), ("bf16", 3, 64),
+]
+
+
+def graph(seed, n=300):
+    rng = np.random.default_rng(seed)
+    return I.random_csr(n, 20, rng, empty_frac=0.05, dup_frac=0.1, heavy_rows=3, heavy_deg=700)
+
+
+def tensors(seed, n, H, D, dt, names):
+    rng = np.random.default_rng(seed)
+    return {nm: I.normal_tensor(rng, (n, H, D), dt) for nm in names}
+
+
+@pytest.mark.parametrize("chunk", [0, 5])
+@pytest.mark.parametrize("dt,H,D", LAYOUTS)
+def test_gt_parity(dt, H, D, chunk):
+    note(f"gt parity dt={dt} H={H} D={D} chunk={chunk}")
+    rp, ci = graph(100 + H + D)
+    n = rp.size - 1
+    t = tensors(7, n, H, D, dt, ["q", "k", "v", "dout"])
+    r = Runner(rp, ci, chunk=chunk)
+    q, k, v, do = (dev(t[x]) for x in ("q", "k", "v", "dout"))
+    out, lse = r.gt_fwd(q, k, v)
+    ro, rl = oracle.gt_fwd(rp, ci, t["q"], t["k"], t["v"])
+    assert rel_err(host(out), ro) <= TOL[dt]
+    assert rel_err(host(lse), rl) <= TOL[dt]
+    dq, dk, dv = r.gt_bwd(q, k, v, out, lse, do)
+    # the backward consumes the GPU's stored output, as a caller's would
+    rq, rk, rv = oracle.gt_bwd(rp, ci, t["q"], t["k"], t["v"], t["dout"])
+    assert rel_err(host(dq), rq) <= TOL[dt]
+    assert rel_err(host(dk), rk) <= TOL[dt]
+    assert rel_err(host(dv), rv) <= TOL[dt]
+
+
+@pytest.mark.parametrize("chunk", [0, 5])
+@pytest.mark.parametrize("dt,H,D", [("f32", 2, 64), ("f32", 4, 32), ("bf16", 2, 64),
+                                    ("bf16", 4, 128), ("bf16", 8, 64), ("bf16", 3, 32)])
+def test_gat_parity(dt, H, D, chunk):
+    note(f"gat parity dt={dt} H={H} D={D} chunk={chunk}")
+    rp, ci = graph(200 + H + D)
+    n = rp.size - 1
+    t = tensors(8, n, H, D, dt, ["xs", "xt", "dout"])
+    a = np.random.default_rng(9).standard_normal((H, D)).astype(np.float32) / np.sqrt(D)
+    r = Runner(rp, ci, chunk=chunk)
+    xs, xt, do = (dev(t[x]) for x in ("xs", "xt", "dout"))
+    ad = dev(a)
+    out, lse = r.gat_fwd(xs, xt, ad)
+    ro, rl = oracle.gat_fwd(rp, ci, t["xs"], t["xt"], a)
+    assert rel_err(host(out), ro) <= TOL[dt]
+    assert rel_err(host(lse), rl) <= TOL[dt]
+    dxs, dxt, da = r.gat_bwd(xs, xt, ad, out, lse, do)
+    rs, rt, ra = oracle.gat_bwd(rp, ci, t["xs"], t["xt"], a, t["dout"])
+    assert rel_err(host(dxs), rs) <= TOL[dt]
+    assert rel_err(host(dxt), rt) <= TOL[dt]
+    assert rel_err(host(da), ra) <= TOL[dt]
+
+
+def test_er_workload_forward_full():
+    """The fp32 Erdos-Renyi workload (N=1000, H=4, D=32), every output element."""
+    note("gt_er1k_h4d32_f32 forward")
+    w = I.make_workload("gt_er1k_h4d32_f32")
+    r = Runner(w["rowptr"], w["colidx"])
+    out, lse = r.gt_fwd(dev(w["q"]), dev(w["k"]), dev(w["v"]))
+    ro, rl = oracle.gt_fwd(w["rowptr"], w["colidx"], w["q"], w["k"], w["v"])
+    assert rel_err(host(out), ro) <= 1e-4
+    assert rel_err(host(lse), rl) <= 1e-4
+
+
+def test_single_neighbour_rows_exact():
+    """A row with one in-edge returns that neighbour's V (weight exactly 1)."""
+    note("single neighbour rows")
+    n, H, D = 500, 4, 128
+    rng = np.random.default_rng(11)
+    rp = np.arange(n + 1, dtype=np.int64)
+    ci = rng.integers(0, n, size=n).astype(np.int32)
+    t = tensors(12, n, H, D, "bf16", ["q", "k", "v"])
+    r = Runner(rp, ci)
+    out, lse = r.gt_fwd(dev(t["q"]), dev(t["k"]), dev(t["v"]))
+    assert np.array_equal(host(out), widen(t["v"])[ci])
+    xs = dev(t["q"])
+    a = dev(rng.standard_normal((H, D)).astype(np.float32))
+    out, _ = r.gat_fwd(xs, dev(t["k"]), a)
+    assert np.array_equal(host(out), widen(t["k"])[ci])
+
+
+def test_weights_sum_to_one():
+    note("V = 1 gives out = 1")
+    rp, ci = graph(13)
+    n = rp.size - 1
+    for dt, H, D in (("f32", 4, 32), ("bf16", 4, 128), ("bf16", 2, 64)):
+        t = tensors(14, n, H, D, dt, ["q", "k"])
+        ones = np.ones((n, H, D), dtype=np.float32)
+        if dt == "bf16":
+            ones = I.f32_to_bf16_bits(ones)
+        r = Runner(rp, ci, chunk=7)
+        out, _ = r.gt_fwd(dev(t["q"]), dev(t["k"]), dev(ones))
+        o = host(out)
+        deg = np.diff(rp)
+        assert np.abs(o[deg > 0] - 1).max() <= (1e-6 if dt == "f32" else 8e-3)
+        assert np.all(o[deg == 0] == 0)
+
+
+def test_neighbour_order_and_chunk_invariance():
+    note("permutation / chunk invariance")
+    rp, ci = graph(15)
+    n, H, D = rp.size - 1, 4, 128
+    t = tensors(16, n, H, D, "bf16", ["q", "k", "v"])
+    rng = np.random.default_rng(17)
+    ci2 = ci.copy()
+    for i in range(n):
+        rng.shuffle(ci2[rp[i]:rp[i + 1]])
+    q, k, v = (dev(t[x]) for x in ("q", "k", "v"))
+    base = host(Runner(rp, ci, chunk=0).gt_fwd(q, k, v)[0])
+    for rr, cc, ch in ((rp, ci2, 0), (rp, ci, 1), (rp, ci, 64), (rp, ci, 10 ** 6)):
+        o = host(Runner(rr, cc, chunk=ch).gt_fwd(q, k, v)[0])
+        assert rel_err(o, base) <= 1e-2
+
+
+def test_bitwise_determinism():
+    note("run-to-run determinism")
+    rp, ci = graph(18)
+    n, H, D = rp.size - 1, 2, 64
+    t = tensors(19, n, H, D, "bf16", ["xs", "xt", "dout"])
+    a = dev(np.random.default_rng(20).standard_normal((H, D)).astype(np.float32))
+    r = Runner(rp, ci, chunk=9)
+    xs, xt, do = (dev(t[x]) for x in ("xs", "xt", "dout"))
+    res = []
+    for _ in range(2):
+        out, lse = r.gat_fwd(xs, xt, a)
+        g = r.gat_bwd(xs, xt, a, out, lse, do)
+        res.append([host(x) for x in (out, lse, *g)])
+    for x, y in zip(*res):
+        assert np.array_equal(x, y)
+
+
+def test_empty_graph_and_no_edges():
+    note("empty graph / no edges")
+    import torch
+    for n in (0, 10):
+        rp = np.zeros(n + 1, dtype=np.int64)
+        ci = np.zeros(0, dtype=np.int32)
+        r = Runner(rp, ci)
+        q = torch.randn(n, 2, 64, device="cuda").to(torch.bfloat16)
+        out, lse = r.gt_fwd(q, q, q)
+        if n:
+            assert torch.all(out == 0) and torch.all(torch.isneginf(lse))
+        dq, dk, dv = r.gt_bwd(q, q, q, out, lse, q)
+        if n:
+            assert torch.all(dq == 0) and torch.all(dk == 0) and torch.all(dv == 0)
+        a = torch.randn(2, 64, device="cuda")
+        out, lse = r.gat_fwd(q, q, a)
+        dxs, dxt, da = r.gat_bwd(q, q, a, out, lse, q)
+        torch.cuda.synchronize()
+        assert torch.all(da == 0)

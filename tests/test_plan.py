@@ -1,0 +1,147 @@
+"""Host preprocessing (CSR validation, work lists, transposed CSR, 16x16 tiles):
+the library's arrays must equal an independent numpy statement of the same
+specification byte for byte, and satisfy the structural invariants."""
+import numpy as np
+import pytest
+from hypothesis import given, settings, strategies as st
+
+from oracle import plan_spec as S
+from sparse_graph_attention_csr_amd import binding as B
+from sparse_graph_attention_csr_amd import inputs as I
+
+
+def check_plan(rowptr, colidx, chunk, tmin=0, bs=False):
+    p = B.Plan(rowptr, colidx, chunk=chunk, tile_min_nnz=tmin, block_sparse=bs)
+    C = p.stats()["chunk"]
+    items, splits, nslots = S.work_list(rowptr, C)
+    assert p.export(B.ARR_ROW_ITEMS).tobytes() == items.tobytes()
+    assert p.export(B.ARR_ROW_SPLITS).tobytes() == splits.tobytes()
+    colptr, rowidx = S.transpose(rowptr, colidx)
+    assert np.array_equal(p.export(B.ARR_COLPTR), colptr)
+    assert np.array_equal(p.export(B.ARR_ROWIDX), rowidx)
+    citems, csplits, cslots = S.work_list(colptr, C)
+    assert p.export(B.ARR_COL_ITEMS).tobytes() == citems.tobytes()
+    assert p.export(B.ARR_COL_SPLITS).tobytes() == csplits.tobytes()
+    st_ = p.stats()
+    assert st_["row_slots"] == nslots and st_["col_slots"] == cslots
+    if bs:
+        tr, tc, tm, rr, rc, te = S.tiles(rowptr, colidx, tmin or 32)
+        assert np.array_equal(p.export(B.ARR_TILE_ROWPTR), tr)
+        assert np.array_equal(p.export(B.ARR_TILE_COL), tc)
+        assert np.array_equal(p.export(B.ARR_TILE_MASK), tm)
+        assert np.array_equal(p.export(B.ARR_RES_ROWPTR), rr)
+        assert np.array_equal(p.export(B.ARR_RES_COLIDX), rc)
+        assert st_["tile_edges"] == te
+    return p
+
+
+def invariants(p, rowptr, colidx):
+    n = rowptr.size - 1
+    E = colidx.size
+    deg = np.diff(rowptr)
+    for arr, ptr in ((B.ARR_ROW_ITEMS, rowptr), (B.ARR_COL_ITEMS, p.export(B.ARR_COLPTR))):
+        items = p.export(arr)
+        # every edge covered exactly once, every row present
+        cover = np.zeros(E, dtype=np.int64)
+        for it in items:
+            cover[it["begin"]:it["begin"] + it["len"]] += 1
+        assert np.all(cover == 1)
+        assert set(items["row"].tolist()) == set(range(n))
+        lens = np.bincount(items["row"], weights=items["len"], minlength=n)
+        assert np.array_equal(lens.astype(np.int64), np.diff(ptr))
+    # the transposed CSR is a permutation of the edge multiset
+    colptr = p.export(B.ARR_COLPTR)
+    rowidx = p.export(B.ARR_ROWIDX)
+    dst = np.repeat(np.arange(n), deg)
+    a = np.sort(dst.astype(np.int64) * n + colidx)
+    b = np.sort(rowidx.astype(np.int64) * n + np.repeat(np.arange(n), np.diff(colptr)))
+    assert np.array_equal(a, b)
+
+
+GRAPHS = {
+    "random": dict(n=60, max_deg=12),
+    "empty_rows_dups": dict(n=70, max_deg=9, empty_frac=0.3, dup_frac=0.3),
+    "heavy": dict(n=50, max_deg=5, heavy_rows=3, heavy_deg=140),
+    "ragged_n": dict(n=37, max_deg=30, heavy_rows=2, heavy_deg=37),
+}
+
+
+@pytest.mark.parametrize("name", list(GRAPHS))
+@pytest.mark.parametrize("chunk", [1, 7, 16, 0])
+def test_plan_matches_spec(name, chunk):
+    rp, ci = I.random_csr(rng=np.random.default_rng(hash(name) % 1000), **GRAPHS[name])
+    p = check_plan(rp, ci, chunk, tmin=3, bs=True)
+    invariants(p, rp, ci)
+
+
+def test_plan_on_workload_graph():
+    rp, ci, _ = I.make_graph("gt_er1k_h4d32_f32")
+    for chunk in (4, 8, 0):
+        for tmin in (1, 2, 32):
+            check_plan(rp, ci, chunk, tmin=tmin, bs=True)
+
+
+def test_dense_community_tiles():
+    # four fully connected 16-node blocks plus a few cross edges: every block a tile
+    n = 64
+    dst, src = [], []
+    for c in range(4):
+        for i in range(16):
+            for j in range(16):
+                dst.append(16 * c + i)
+                src.append(16 * c + j)
+    dst += [0, 1, 63]
+    src += [40, 50, 2]
+    rp, ci = I.csr_from_edges(n, np.array(dst), np.array(src), self_loops=False)
+    p = check_plan(rp, ci, 0, tmin=16, bs=True)
+    s = p.stats()
+    assert s["tiles"] == 4 and s["tile_edges"] == 4 * 256 and s["residual_edges"] == 3
+    assert np.all(p.export(B.ARR_TILE_MASK) == 0xFFFF)
+
+
+@settings(max_examples=60, deadline=None)
+@given(n=st.integers(1, 40), max_deg=st.integers(1, 25), chunk=st.integers(1, 20),
+       tmin=st.integers(1, 40), empty=st.floats(0, 0.5), dup=st.floats(0, 0.5),
+       seed=st.integers(0, 2**31 - 1))
+def test_plan_property(n, max_deg, chunk, tmin, empty, dup, seed):
+    rp, ci = I.random_csr(n, max_deg, np.random.default_rng(seed), empty_frac=empty, dup_frac=dup)
+    p = check_plan(rp, ci, chunk, tmin=tmin, bs=True)
+    invariants(p, rp, ci)
+    s = p.stats()
+    assert s["tile_edges"] + s["residual_edges"] == ci.size
+
+
+def test_empty_graphs():
+    for n in (0, 5):
+        rp = np.zeros(n + 1, dtype=np.int64)
+        ci = np.zeros(0, dtype=np.int32)
+        p = check_plan(rp, ci, 0, tmin=1, bs=True)
+        assert p.stats()["row_items"] == n
+
+
+@pytest.mark.parametrize("case", ["first", "monotone", "last", "col_hi", "col_neg"])
+def test_invalid_csr_rejected(case):
+    rp = np.array([0, 2, 3, 5], dtype=np.int64)
+    ci = np.array([0, 1, 2, 1, 0], dtype=np.int32)
+    if case == "first":
+        rp = rp + 1
+    elif case == "monotone":
+        rp = np.array([0, 3, 2, 5])
+    elif case == "last":
+        ci = ci[:4]
+    elif case == "col_hi":
+        ci = ci.copy(); ci[2] = 3
+    else:
+        ci = ci.copy(); ci[0] = -1
+    with pytest.raises(B.SgatError) as e:
+        B.Plan(rp, ci)
+    assert e.value.status == 2
+
+
+def test_invalid_options_rejected():
+    rp = np.array([0, 1], dtype=np.int64)
+    ci = np.array([0], dtype=np.int32)
+    for kw in (dict(chunk=-1), dict(tile_min_nnz=-2), dict(tile_min_nnz=257)):
+        with pytest.raises(B.SgatError) as e:
+            B.Plan(rp, ci, **kw)
+        assert e.value.status == 1
