@@ -30,6 +30,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK = 2.5e15   # dense bf16 matrix-core flop/s
 DEFAULT_WORKLOAD = "gt_powerlaw200k_h4d128_bf16"
 KERNEL_SOURCES = ["sparse_graph_attention_csr_amd/csrc/device.hpp",
                   "sparse_graph_attention_csr_amd/csrc/gather.hpp",
@@ -45,10 +46,36 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def algorithmic_bytes(kernel: str, n: int, e: int, H: int, D: int, b: int) -> int | None:
+def tile_work(plan) -> dict:
+    """Tile and pseudo-tile counts of a block-sparse plan (pseudo-tiles pack 16
+    residual edges of one 16-row block each)."""
+    import numpy as np
+    from sparse_graph_attention_csr_amd import binding as B
+    rr = plan.export(B.ARR_RES_ROWPTR)
+    n = rr.size - 1
+    res_blocks = np.diff(rr[np.minimum(np.arange(0, ((n + 15) // 16) * 16 + 1, 16), n)])
+    pseudo = int(((res_blocks + 15) // 16).sum())
+    s = plan.stats()
+    return {"tiles": s["tiles"], "pseudo_tiles": pseudo, "residual_edges": s["residual_edges"]}
+
+
+def mfma_flops(kernel: str, H: int, D: int, tw: dict) -> float | None:
+    """Issued MFMA flops: per tile (dense or pseudo) and head, S (16x16xD) and
+    the weighted sum (16xDx16), 2 flops per multiply-add each."""
+    if kernel != "gt_bs_fwd" or not tw:
+        return None
+    return float((tw["tiles"] + tw["pseudo_tiles"]) * H * 2 * (2 * 16 * 16 * D))
+
+
+def algorithmic_bytes(kernel: str, n: int, e: int, H: int, D: int, b: int,
+                      tw: dict | None = None) -> int | None:
     """Bytes a kernel must move: neighbour-row gathers per edge plus the
     per-node reads and writes of its own rows (R = H*D*b bytes per node row)."""
     R = H * D * b
+    if kernel == "gt_bs_fwd" and tw:
+        # dense tiles read each node's Q, K, V row once and write out and lse;
+        # residual edges gather K_j and V_j; each tile reads its column and mask
+        return (4 * R + 4 * H + 16) * n + (2 * R + 4) * tw["residual_edges"] + 36 * tw["tiles"]
     model = {
         # K_j, V_j and colidx per edge; Q_i read, out_i and lse_i written per node
         "gt_fwd_rows": (2 * R + 4, 2 * R + 4 * H + 8),
@@ -135,6 +162,8 @@ def main():
     ap.add_argument("--chunk", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--tiles", action="store_true",
+                    help="Graph Transformer forward on the 16x16 tile (MFMA) path")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB three times "
                          "(calibrates the HBM byte counters) and exit")
@@ -171,7 +200,8 @@ def main():
     nbytes = 2 if dt == B.BF16 else 4
 
     t0 = time.perf_counter()
-    g = B.DeviceGraph(rp, ci, device=dev, chunk=args.chunk)
+    g = B.DeviceGraph(rp, ci, device=dev, chunk=args.chunk, block_sparse=args.tiles)
+    tw = tile_work(g.plan) if args.tiles else None
     torch.cuda.synchronize()
     plan_ms = (time.perf_counter() - t0) * 1e3
 
@@ -192,7 +222,7 @@ def main():
             wsb = g.workspace(B.OP_GT_BWD, H, D, dt)
 
         def step():
-            B.gt_fwd(g.plan, g.rowptr, g.colidx, Q, K, V, out, lse, wsf)
+            B.gt_fwd(g.plan, g.rowptr, g.colidx, Q, K, V, out, lse, wsf, use_tiles=args.tiles)
             if bwd:
                 B.gt_bwd(g.plan, g.rowptr, g.colidx, Q, K, V, out, lse, dO, dQ, dK, dV, wsb)
     else:
@@ -240,12 +270,16 @@ def main():
     kernels = {}
     for name, (tot, cnt) in per.items():
         avg = tot / cnt
-        ab = algorithmic_bytes(name, n, e, H, D, nbytes)
+        ab = algorithmic_bytes(name, n, e, H, D, nbytes, tw)
         kernels[name] = {"ms": round(avg, 4), "launches_per_step": cnt / args.steps,
                          "share": round(tot / max(sum(v[0] for v in per.values()), 1e-12), 4)}
         if ab is not None:
             kernels[name]["algorithmic_bytes"] = ab
             kernels[name]["achieved_gbs"] = round(ab / (avg * 1e-3) / 1e9, 1)
+        fl = mfma_flops(name, H, D, tw)
+        if fl is not None:
+            kernels[name]["mfma_tflops"] = round(fl / (avg * 1e-3) / 1e12, 2)
+            kernels[name]["mfma_utilisation"] = round(fl / (avg * 1e-3) / MFMA_BF16_PEAK, 5)
     dom = max((k for k in kernels if "algorithmic_bytes" in kernels[k]),
               key=lambda k: kernels[k]["ms"] * kernels[k]["launches_per_step"])
     dk = kernels[dom]
@@ -270,7 +304,7 @@ def main():
         "data": "synthetic (seeded generator, seed 0)",
         "config": {"workload": args.workload, "graph": spec.graph, "nodes": n, "edges": e,
                    "heads": H, "head_dim": D, "passes": spec.passes,
-                   "chunk": g.plan.stats()["chunk"]},
+                   "chunk": g.plan.stats()["chunk"], "tiles": bool(args.tiles)},
         "roofline": roofline,
         "kernels": kernels,
         "plan_ms": round(plan_ms, 1),

@@ -113,7 +113,12 @@ typedef enum sgat_array {
                                  (16*col+c) -> (16*row+r)                               */
     SGAT_ARR_RES_ROWPTR = 9,  /* int64 [n+1]: edges not covered by a dense tile         */
     SGAT_ARR_RES_COLIDX = 10, /* int32 [residual_edges]                                 */
-    SGAT_ARR_COUNT = 11
+    SGAT_ARR_TILE_ROW = 11,   /* int32 [tiles]: 16-row block index of each tile         */
+    SGAT_ARR_TILE_COLPTR = 12,/* int64 [ceil(n/16)+1]: tiles grouped by block column    */
+    SGAT_ARR_TILE_BYCOL = 13, /* int32 [tiles]: tile ids by block column, then row      */
+    SGAT_ARR_RES_COLPTR = 14, /* int64 [n+1]: residual edges grouped by source          */
+    SGAT_ARR_RES_ROWIDX = 15, /* int32 [residual_edges]: their destinations             */
+    SGAT_ARR_COUNT = 16
 } sgat_array;
 
 /* One unit of work of the gather kernels: `len` consecutive edges starting at

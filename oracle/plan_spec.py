@@ -25,6 +25,10 @@ with at least ``min_nnz`` distinct pairs is dense; dense tiles are listed by
 block row, then block column. Bit c of mask word r marks edge
 (16 bc + c) -> (16 br + r). Every edge not marked in a dense tile (including
 repeats) goes to the residual CSR, in its original order.
+
+Column side of the tiles: the block row of every tile, and the tile ids grouped
+by block column with block rows ascending inside a column; the residual CSR
+transposed like the main one.
 """
 from __future__ import annotations
 
@@ -127,3 +131,12 @@ def tiles(rowptr: np.ndarray, colidx: np.ndarray, min_nnz: int):
     np.cumsum(np.bincount(dst[res], minlength=n), out=res_rowptr[1:])
     res_colidx = src[res].astype(np.int32)
     return tile_rowptr, tile_col, mask.reshape(-1), res_rowptr, res_colidx, int(in_tile.sum())
+
+
+def tile_columns(n: int, tile_rowptr: np.ndarray, tile_col: np.ndarray):
+    nb = (n + 15) // 16
+    tile_row = np.repeat(np.arange(nb, dtype=np.int64), np.diff(tile_rowptr)).astype(np.int32)
+    order = np.lexsort((tile_row, tile_col))      # column, then row
+    tile_colptr = np.zeros(nb + 1, dtype=np.int64)
+    np.cumsum(np.bincount(tile_col, minlength=nb), out=tile_colptr[1:])
+    return tile_row, tile_colptr, order.astype(np.int32)

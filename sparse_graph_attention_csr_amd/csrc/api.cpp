@@ -209,10 +209,13 @@ int gt_fwd(const sgat_plan* plan, int64_t n, int64_t nnz, const int64_t* rowptr,
     for (const void* t : {Q, K, V, static_cast<const void*>(out)})
         if ((rc = check_tensor(t, n))) return rc;
     if (n > 0 && (!lse || !aligned(lse, 4))) return SGAT_INVALID_ARGUMENT;
-    if (use_tiles != 0) return use_tiles == 1 ? SGAT_UNSUPPORTED : SGAT_INVALID_ARGUMENT;
+    if (use_tiles != 0 && use_tiles != 1) return SGAT_INVALID_ARGUMENT;
+    if (use_tiles && (!plan->p.block_sparse || dtype != SGAT_BF16)) return SGAT_UNSUPPORTED;
     Layout L;
     if ((rc = check_ws(plan->p, SGAT_OP_GT_FWD, H, D, ws, ws_bytes, L))) return rc;
     if (n == 0) return SGAT_OK;
+    if (use_tiles)
+        return launch_gt_bs_fwd(plan->p, H, D, Q, K, V, out, lse, static_cast<hipStream_t>(stream));
     FwdWs w{at<float>(ws, L.off[0]), at<float>(ws, L.off[1])};
     return launch_gt_fwd(plan->p, H, D, dtype, colidx, Q, K, V, out, lse, w,
                          static_cast<hipStream_t>(stream));

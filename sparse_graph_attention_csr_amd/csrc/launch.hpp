@@ -47,6 +47,10 @@ int launch_gat_bwd(const Plan& p, int H, int D, int dt, const int32_t* colidx, c
                    const void* dO, void* dXs, void* dXt, float* da, const BwdWs& ws,
                    hipStream_t s);
 
+// Block-sparse forward (bf16 only): dense tiles and residual pseudo-tiles.
+int launch_gt_bs_fwd(const Plan& p, int H, int D, const void* Q, const void* K, const void* V,
+                     void* out, float* lse, hipStream_t s);
+
 // da = 0 (the empty sum, for a graph without nodes), by a kernel.
 int launch_da_zero(float* da, int HD, hipStream_t s);
 

@@ -1,0 +1,31 @@
+// Launchers of the block-sparse (16x16 tile, bf16 MFMA) Graph Transformer path.
+#include "blocksparse.hpp"
+#include "launch.hpp"
+
+namespace sgat {
+
+int launch_gt_bs_fwd(const Plan& p, int H, int D, const void* Q, const void* K, const void* V,
+                     void* out, float* lse, hipStream_t s)
+{
+    BsFwdArgs a;
+    a.n = p.n;
+    a.n_tile_rows = (p.n + kTileDim - 1) / kTileDim;
+    a.H = H;
+    a.tile_rowptr = p.dptr<int64_t>(SGAT_ARR_TILE_ROWPTR);
+    a.tile_col = p.dptr<int32_t>(SGAT_ARR_TILE_COL);
+    a.tile_mask = p.dptr<uint16_t>(SGAT_ARR_TILE_MASK);
+    a.res_rowptr = p.dptr<int64_t>(SGAT_ARR_RES_ROWPTR);
+    a.res_colidx = p.dptr<int32_t>(SGAT_ARR_RES_COLIDX);
+    a.Q = Q; a.K = K; a.V = V;
+    a.out = out;
+    a.lse = lse;
+    a.scale2 = kLog2e / sqrtf(static_cast<float>(D));
+    const void* fn = D == 32 ? reinterpret_cast<const void*>(&gt_bs_fwd<32>)
+                   : D == 64 ? reinterpret_cast<const void*>(&gt_bs_fwd<64>)
+                             : reinterpret_cast<const void*>(&gt_bs_fwd<128>);
+    // one workgroup per tile row, counted as four one-wave units for the grid
+    return launch("gt_bs_fwd", fn, dim3(static_cast<unsigned>(wave_grid(a.n_tile_rows * kWavesPerBlock))),
+                  dim3(kBlock), &a, s);
+}
+
+}  // namespace sgat

@@ -160,6 +160,25 @@ void build_tiles(int64_t n, const int64_t* rowptr, const int32_t* colidx, int32_
     }
 }
 
+void build_tile_columns(int64_t n, const std::vector<int64_t>& tile_rowptr,
+                        const std::vector<int32_t>& tile_col, std::vector<int32_t>& tile_row,
+                        std::vector<int64_t>& tile_colptr, std::vector<int32_t>& tile_bycol)
+{
+    const int64_t nb = (n + kTile - 1) / kTile;
+    const size_t T = tile_col.size();
+    tile_row.assign(T, 0);
+    for (int64_t br = 0; br < nb; ++br)
+        for (int64_t t = tile_rowptr[br]; t < tile_rowptr[br + 1]; ++t)
+            tile_row[static_cast<size_t>(t)] = static_cast<int32_t>(br);
+    tile_colptr.assign(static_cast<size_t>(nb) + 1, 0);
+    for (size_t t = 0; t < T; ++t) tile_colptr[static_cast<size_t>(tile_col[t]) + 1]++;
+    for (int64_t b = 0; b < nb; ++b) tile_colptr[b + 1] += tile_colptr[b];
+    std::vector<int64_t> fill(tile_colptr.begin(), tile_colptr.end() - 1);
+    tile_bycol.assign(T, 0);
+    for (size_t t = 0; t < T; ++t)
+        tile_bycol[static_cast<size_t>(fill[tile_col[t]]++)] = static_cast<int32_t>(t);
+}
+
 const void* Plan::host_array(int id) const
 {
     switch (id) {
@@ -174,6 +193,11 @@ const void* Plan::host_array(int id) const
     case SGAT_ARR_TILE_MASK: return tile_mask.data();
     case SGAT_ARR_RES_ROWPTR: return res_rowptr.data();
     case SGAT_ARR_RES_COLIDX: return res_colidx.data();
+    case SGAT_ARR_TILE_ROW: return tile_row.data();
+    case SGAT_ARR_TILE_COLPTR: return tile_colptr.data();
+    case SGAT_ARR_TILE_BYCOL: return tile_bycol.data();
+    case SGAT_ARR_RES_COLPTR: return res_colptr.data();
+    case SGAT_ARR_RES_ROWIDX: return res_rowidx.data();
     default: return nullptr;
     }
 }
@@ -191,6 +215,11 @@ void Plan::layout()
     bytes[SGAT_ARR_TILE_MASK] = tile_mask.size() * sizeof(uint16_t);
     bytes[SGAT_ARR_RES_ROWPTR] = res_rowptr.size() * sizeof(int64_t);
     bytes[SGAT_ARR_RES_COLIDX] = res_colidx.size() * sizeof(int32_t);
+    bytes[SGAT_ARR_TILE_ROW] = tile_row.size() * sizeof(int32_t);
+    bytes[SGAT_ARR_TILE_COLPTR] = tile_colptr.size() * sizeof(int64_t);
+    bytes[SGAT_ARR_TILE_BYCOL] = tile_bycol.size() * sizeof(int32_t);
+    bytes[SGAT_ARR_RES_COLPTR] = res_colptr.size() * sizeof(int64_t);
+    bytes[SGAT_ARR_RES_ROWIDX] = res_rowidx.size() * sizeof(int32_t);
     size_t off = 0;
     for (int a = 0; a < SGAT_ARR_COUNT; ++a) {
         offset[a] = off;
@@ -239,9 +268,14 @@ int sgat_plan_create(int64_t n, int64_t nnz, const int64_t* rowptr, const int32_
         for (int64_t j = 0; j < n; ++j)
             p.max_out_degree = std::max(p.max_out_degree, p.colptr[j + 1] - p.colptr[j]);
         sgat::build_work_list(n, p.colptr.data(), chunk, p.col_items, p.col_splits, p.col_slots);
-        if (bs)
+        if (bs) {
             sgat::build_tiles(n, rowptr, colidx, tmin, p.tile_rowptr, p.tile_col, p.tile_mask,
                               p.res_rowptr, p.res_colidx, p.tile_edges);
+            sgat::build_tile_columns(n, p.tile_rowptr, p.tile_col, p.tile_row, p.tile_colptr,
+                                     p.tile_bycol);
+            sgat::build_transpose(n, p.res_rowptr.data(), p.res_colidx.data(), p.res_colptr,
+                                  p.res_rowidx);
+        }
         p.layout();
     } catch (const std::bad_alloc&) {
         delete h;

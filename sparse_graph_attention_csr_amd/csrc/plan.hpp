@@ -38,6 +38,11 @@ struct Plan {
     std::vector<uint16_t> tile_mask;   // [tiles][16]
     std::vector<int64_t> res_rowptr;
     std::vector<int32_t> res_colidx;
+    std::vector<int32_t> tile_row;      // block row of each tile
+    std::vector<int64_t> tile_colptr;   // tiles grouped by block column
+    std::vector<int32_t> tile_bycol;
+    std::vector<int64_t> res_colptr;    // transposed residual CSR
+    std::vector<int32_t> res_rowidx;
     int64_t tile_edges = 0;
 
     // device image: every array at a 256-byte aligned offset of one buffer
@@ -70,6 +75,12 @@ void build_tiles(int64_t n, const int64_t* rowptr, const int32_t* colidx, int32_
                  std::vector<int64_t>& tile_rowptr, std::vector<int32_t>& tile_col,
                  std::vector<uint16_t>& tile_mask, std::vector<int64_t>& res_rowptr,
                  std::vector<int32_t>& res_colidx, int64_t& tile_edges);
+
+// A4 (column side): tiles grouped by block column (stable in block row) and
+// the block row of each tile.
+void build_tile_columns(int64_t n, const std::vector<int64_t>& tile_rowptr,
+                        const std::vector<int32_t>& tile_col, std::vector<int32_t>& tile_row,
+                        std::vector<int64_t>& tile_colptr, std::vector<int32_t>& tile_bycol);
 
 }  // namespace sgat
 

@@ -32,6 +32,14 @@ def check_plan(rowptr, colidx, chunk, tmin=0, bs=False):
         assert np.array_equal(p.export(B.ARR_RES_ROWPTR), rr)
         assert np.array_equal(p.export(B.ARR_RES_COLIDX), rc)
         assert st_["tile_edges"] == te
+        n = rowptr.size - 1
+        trow, tcp, tbc = S.tile_columns(n, tr, tc)
+        assert np.array_equal(p.export(B.ARR_TILE_ROW), trow)
+        assert np.array_equal(p.export(B.ARR_TILE_COLPTR), tcp)
+        assert np.array_equal(p.export(B.ARR_TILE_BYCOL), tbc)
+        rcp, rri = S.transpose(rr, rc)
+        assert np.array_equal(p.export(B.ARR_RES_COLPTR), rcp)
+        assert np.array_equal(p.export(B.ARR_RES_ROWIDX), rri)
     return p
 
 
