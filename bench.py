@@ -62,9 +62,13 @@ def tile_work(plan) -> dict:
 def mfma_flops(kernel: str, H: int, D: int, tw: dict) -> float | None:
     """Issued MFMA flops: per tile (dense or pseudo) and head, S (16x16xD) and
     the weighted sum (16xDx16), 2 flops per multiply-add each."""
-    if kernel != "gt_bs_fwd" or not tw:
+    if not tw:
         return None
-    return float((tw["tiles"] + tw["pseudo_tiles"]) * H * 2 * (2 * 16 * 16 * D))
+    per = {"gt_bs_fwd": 2, "gt_bs_bwd_rows": 3, "gt_bs_bwd_cols": 4}.get(kernel)
+    if per is None:
+        return None
+    # forward: S, PV; rows: S, dP, dS K; cols: S, dP, dS^T Q, P^T dO
+    return float((tw["tiles"] + tw["pseudo_tiles"]) * H * per * (2 * 16 * 16 * D))
 
 
 def algorithmic_bytes(kernel: str, n: int, e: int, H: int, D: int, b: int,
@@ -76,6 +80,15 @@ def algorithmic_bytes(kernel: str, n: int, e: int, H: int, D: int, b: int,
         # dense tiles read each node's Q, K, V row once and write out and lse;
         # residual edges gather K_j and V_j; each tile reads its column and mask
         return (4 * R + 4 * H + 16) * n + (2 * R + 4) * tw["residual_edges"] + 36 * tw["tiles"]
+    if kernel == "gt_bs_bwd_rows" and tw:
+        # Q, dO, O, lse read and dQ, (lse, Delta) written per node; K, V once per
+        # node through the tiles; residual edges gather K_j, V_j
+        return (6 * R + 12 * H + 16) * n + (2 * R + 4) * tw["residual_edges"] + 36 * tw["tiles"]
+    if kernel == "gt_bs_bwd_cols" and tw:
+        # K, V read and dK, dV written per node; Q, dO and (lse, Delta) once per
+        # node through the tiles; residual edges gather Q_i, dO_i, (lse_i, Delta_i)
+        return ((6 * R + 8 * H + 16) * n + (2 * R + 8 * H + 4) * tw["residual_edges"]
+                + 40 * tw["tiles"])
     model = {
         # K_j, V_j and colidx per edge; Q_i read, out_i and lse_i written per node
         "gt_fwd_rows": (2 * R + 4, 2 * R + 4 * H + 8),
@@ -224,7 +237,8 @@ def main():
         def step():
             B.gt_fwd(g.plan, g.rowptr, g.colidx, Q, K, V, out, lse, wsf, use_tiles=args.tiles)
             if bwd:
-                B.gt_bwd(g.plan, g.rowptr, g.colidx, Q, K, V, out, lse, dO, dQ, dK, dV, wsb)
+                B.gt_bwd(g.plan, g.rowptr, g.colidx, Q, K, V, out, lse, dO, dQ, dK, dV, wsb,
+                         use_tiles=args.tiles)
     else:
         Xs, Xt = todev(w["xs"]), todev(w["xt"])
         A = torch.from_numpy(w["a"]).to(dev)

@@ -232,10 +232,14 @@ int gt_bwd(const sgat_plan* plan, int64_t n, int64_t nnz, const int64_t* rowptr,
                           static_cast<const void*>(dK), static_cast<const void*>(dV)})
         if ((rc = check_tensor(t, n))) return rc;
     if (n > 0 && (!lse || !aligned(lse, 4))) return SGAT_INVALID_ARGUMENT;
-    if (use_tiles != 0) return use_tiles == 1 ? SGAT_UNSUPPORTED : SGAT_INVALID_ARGUMENT;
+    if (use_tiles != 0 && use_tiles != 1) return SGAT_INVALID_ARGUMENT;
+    if (use_tiles && (!plan->p.block_sparse || dtype != SGAT_BF16)) return SGAT_UNSUPPORTED;
     Layout L;
     if ((rc = check_ws(plan->p, SGAT_OP_GT_BWD, H, D, ws, ws_bytes, L))) return rc;
     if (n == 0) return SGAT_OK;
+    if (use_tiles)
+        return launch_gt_bs_bwd(plan->p, H, D, Q, K, V, out, lse, dout, dQ, dK, dV,
+                                at<void>(ws, L.off[0]), static_cast<hipStream_t>(stream));
     BwdWs w{at<void>(ws, L.off[0]), at<float>(ws, L.off[1]), at<float>(ws, L.off[2]),
             at<float>(ws, L.off[3]), nullptr};
     return launch_gt_bwd(plan->p, H, D, dtype, colidx, Q, K, V, out, lse, dout, dQ, dK, dV, w,

@@ -192,4 +192,306 @@ __global__ __launch_bounds__(kBlock) void gt_bs_fwd(BsFwdArgs a)
     }
 }
 
+// ---------------------------------------------------------------------------
+// backward: recompute S and dP per tile from the forward's lse, no stored
+// edge values; dQ per tile row, dK and dV per tile column, no atomics
+// ---------------------------------------------------------------------------
+
+struct BsBwdArgs {
+    int64_t n, n_blocks;   // 16-node blocks (tile rows or tile columns)
+    int H;
+    const int64_t* tile_rowptr;
+    const int32_t* tile_col;
+    const uint16_t* tile_mask;
+    const int32_t* tile_row;
+    const int64_t* tile_colptr;
+    const int32_t* tile_bycol;
+    const int64_t* res_rowptr;
+    const int32_t* res_colidx;
+    const int64_t* res_colptr;
+    const int32_t* res_rowidx;
+    const void *Q, *K, *V, *O, *dO;
+    const float* lse;
+    RowStat* stats;
+    void *dQ, *dK, *dV;
+    float scale2, oscale;
+};
+
+template <int D>
+struct TileBwd {
+    static constexpr int KS = D / 32;
+    static constexpr int NB = D / 16;
+    static constexpr int LDW = D + 16;
+
+    // Tile-row step: rows i = l%16 of the block, columns c = 4g..4g+3 in this
+    // lane. `base` = element offset of (source of column l%16, head).
+    static __device__ __forceinline__ void row_step(int64_t base, uint32_t valid,
+                                                    const bf16x8_t (&qf)[KS],
+                                                    const bf16x8_t (&df)[KS], float lse2,
+                                                    float delta, f32x4_t (&acc)[NB],
+                                                    const void* K, const void* V, uint16_t* ks,
+                                                    float scale2, int i, int g)
+    {
+        Frag kf[KS], vf[KS];
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+            kf[s] = ldg<SGAT_BF16>(K, base + 32 * s + 8 * g);
+            vf[s] = ldg<SGAT_BF16>(V, base + 32 * s + 8 * g);
+        }
+        f32x4_t st = {0.f, 0.f, 0.f, 0.f}, dp = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+            st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kf[s]), qf[s],
+                                                         st, 0, 0, 0);
+            dp = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, vf[s]), df[s],
+                                                         dp, 0, 0, 0);
+        }
+#pragma unroll
+        for (int s = 0; s < KS; ++s)
+            *reinterpret_cast<Frag*>(ks + i * LDW + 32 * s + 8 * g) = kf[s];
+        short dsb[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const float p = ((valid >> k) & 1u) ? fast_exp2(st[k] * scale2 - lse2) : 0.f;
+            dsb[k] = bf16_bits(p * (dp[k] - delta));
+        }
+        const s16x4_t b = {dsb[0], dsb[1], dsb[2], dsb[3]};
+        __builtin_amdgcn_wave_barrier();
+#pragma unroll
+        for (int s = 0; s < NB; ++s) {
+            s16x4_t ka;
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk)
+                ka[kk] = static_cast<short>(ks[(4 * g + kk) * LDW + 16 * s + i]);
+            acc[s] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ka, b, acc[s], 0, 0, 0);
+        }
+        __builtin_amdgcn_wave_barrier();
+    }
+
+    // Tile-column step: columns c = l%16 (sources of the block), rows
+    // 4g..4g+3 of the tile in this lane. `qbase` = element offset of (the
+    // destination of tile row l%16, head); st[k] = statistics of row 4g+k.
+    static __device__ __forceinline__ void col_step(int64_t qbase, const RowStat (&st)[4],
+                                                    uint32_t valid, const bf16x8_t (&kf)[KS],
+                                                    const bf16x8_t (&vf)[KS], f32x4_t (&dk)[NB],
+                                                    f32x4_t (&dv)[NB], const void* Q,
+                                                    const void* dO, uint16_t* qs, uint16_t* os,
+                                                    float scale2, int c, int g)
+    {
+        Frag qa[KS], oa[KS];
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+            qa[s] = ldg<SGAT_BF16>(Q, qbase + 32 * s + 8 * g);
+            oa[s] = ldg<SGAT_BF16>(dO, qbase + 32 * s + 8 * g);
+        }
+        f32x4_t sc = {0.f, 0.f, 0.f, 0.f}, dp = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+            sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, qa[s]), kf[s],
+                                                         sc, 0, 0, 0);
+            dp = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, oa[s]), vf[s],
+                                                         dp, 0, 0, 0);
+        }
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+            *reinterpret_cast<Frag*>(qs + c * LDW + 32 * s + 8 * g) = qa[s];
+            *reinterpret_cast<Frag*>(os + c * LDW + 32 * s + 8 * g) = oa[s];
+        }
+        short pb[4], db[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const float p = ((valid >> k) & 1u) ? fast_exp2(sc[k] * scale2 - st[k].lse2) : 0.f;
+            pb[k] = bf16_bits(p);
+            db[k] = bf16_bits(p * (dp[k] - st[k].delta));
+        }
+        const s16x4_t P = {pb[0], pb[1], pb[2], pb[3]};
+        const s16x4_t S = {db[0], db[1], db[2], db[3]};
+        __builtin_amdgcn_wave_barrier();
+#pragma unroll
+        for (int s = 0; s < NB; ++s) {
+            s16x4_t qt, ot;
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) {
+                qt[kk] = static_cast<short>(qs[(4 * g + kk) * LDW + 16 * s + c]);
+                ot[kk] = static_cast<short>(os[(4 * g + kk) * LDW + 16 * s + c]);
+            }
+            dk[s] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(qt, S, dk[s], 0, 0, 0);
+            dv[s] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ot, P, dv[s], 0, 0, 0);
+        }
+        __builtin_amdgcn_wave_barrier();
+    }
+};
+
+__device__ __forceinline__ void store_tile_rows(void* dst, int64_t off, const f32x4_t& v, float sc)
+{
+    uint2 w;
+    w.x = pack_bf16x2(v[0] * sc, v[1] * sc);
+    w.y = pack_bf16x2(v[2] * sc, v[3] * sc);
+    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(dst) + off) = w;
+}
+
+// Position of edge e among the 16 rows of a block, from the block's pointers.
+__device__ __forceinline__ int row_in_block(const int64_t* ptr, int64_t lo, int64_t hi, int64_t e)
+{
+    int r = 0;
+    for (int q = 1; q < kTileDim; ++q) {
+        const int64_t x = lo + q < hi ? lo + q : hi;
+        r += ptr[x] <= e ? 1 : 0;
+    }
+    return r;
+}
+
+template <int D>
+__global__ __launch_bounds__(kBlock) void gt_bs_bwd_rows(BsBwdArgs a)
+{
+    using T = TileBwd<D>;
+    __shared__ __attribute__((aligned(16))) uint16_t ks_all[kWavesPerBlock][16 * T::LDW];
+    const int64_t br = logical_block();
+    if (br >= a.n_blocks) return;
+    const int w = wave_id();
+    const int l = threadIdx.x & 63, i = l & 15, g = l >> 4;
+    const int64_t HD = static_cast<int64_t>(a.H) * D;
+    const int64_t r_lo = br * kTileDim;
+    const int64_t r_hi = r_lo + kTileDim < a.n ? r_lo + kTileDim : a.n;
+    const int64_t row = r_lo + i;
+    const bool row_ok = row < a.n;
+    const int64_t tb = a.tile_rowptr[br], te = a.tile_rowptr[br + 1];
+    const int64_t rb = a.res_rowptr[r_lo], re = a.res_rowptr[r_hi];
+    uint16_t* ks = ks_all[w];
+
+    for (int h = w; h < a.H; h += kWavesPerBlock) {
+        const int64_t hoff = static_cast<int64_t>(h) * D;
+        bf16x8_t qf[T::KS], df[T::KS];
+        float dsum = 0.f, lse2 = 0.f;
+#pragma unroll
+        for (int s = 0; s < T::KS; ++s) {
+            qf[s] = bf16x8_t{};
+            df[s] = bf16x8_t{};
+            if (row_ok) {
+                const int64_t o = row * HD + hoff + 32 * s + 8 * g;
+                qf[s] = ld_bf16x8(a.Q, o);
+                const Frag d = ldg<SGAT_BF16>(a.dO, o);
+                df[s] = __builtin_bit_cast(bf16x8_t, d);
+                dsum += dot<SGAT_BF16>(d, ldg<SGAT_BF16>(a.O, o));
+            }
+        }
+        dsum += __shfl_xor(dsum, 16);
+        dsum += __shfl_xor(dsum, 32);
+        if (row_ok) lse2 = a.lse[row * a.H + h] * kLog2e;
+        if (row_ok && g == 0) a.stats[row * a.H + h] = RowStat{lse2, dsum};
+        f32x4_t acc[T::NB];
+#pragma unroll
+        for (int s = 0; s < T::NB; ++s) acc[s] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+        for (int64_t t = tb; t < te; ++t) {
+            const int64_t src = min(static_cast<int64_t>(a.tile_col[t]) * kTileDim + i, a.n - 1);
+            const uint32_t valid = (static_cast<uint32_t>(a.tile_mask[t * kTileDim + i]) >> (4 * g)) & 0xFu;
+            T::row_step(src * HD + hoff, valid, qf, df, lse2, dsum, acc, a.K, a.V, ks, a.scale2, i, g);
+        }
+        for (int64_t e0 = rb; e0 < re; e0 += 16) {
+            const int64_t e = e0 + i;
+            int rr = -1;
+            int64_t src = 0;
+            if (e < re) {
+                src = a.res_colidx[e];
+                rr = row_in_block(a.res_rowptr, r_lo, r_hi, e);
+            }
+            uint32_t valid = 0;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) valid |= (__shfl(rr, 4 * g + k) == i ? 1u : 0u) << k;
+            T::row_step(src * HD + hoff, valid, qf, df, lse2, dsum, acc, a.K, a.V, ks, a.scale2, i, g);
+        }
+        if (row_ok) {
+#pragma unroll
+            for (int s = 0; s < T::NB; ++s)
+                store_tile_rows(a.dQ, row * HD + hoff + 16 * s + 4 * g, acc[s], a.oscale);
+        }
+    }
+}
+
+template <int D>
+__global__ __launch_bounds__(kBlock) void gt_bs_bwd_cols(BsBwdArgs a)
+{
+    using T = TileBwd<D>;
+    __shared__ __attribute__((aligned(16))) uint16_t qs_all[kWavesPerBlock][16 * T::LDW];
+    __shared__ __attribute__((aligned(16))) uint16_t os_all[kWavesPerBlock][16 * T::LDW];
+    const int64_t bc = logical_block();
+    if (bc >= a.n_blocks) return;
+    const int w = wave_id();
+    const int l = threadIdx.x & 63, c = l & 15, g = l >> 4;
+    const int64_t HD = static_cast<int64_t>(a.H) * D;
+    const int64_t c_lo = bc * kTileDim;
+    const int64_t c_hi = c_lo + kTileDim < a.n ? c_lo + kTileDim : a.n;
+    const int64_t j = c_lo + c;
+    const bool j_ok = j < a.n;
+    const int64_t tcb = a.tile_colptr[bc], tce = a.tile_colptr[bc + 1];
+    const int64_t rcb = a.res_colptr[c_lo], rce = a.res_colptr[c_hi];
+    uint16_t* qs = qs_all[w];
+    uint16_t* os = os_all[w];
+
+    for (int h = w; h < a.H; h += kWavesPerBlock) {
+        const int64_t hoff = static_cast<int64_t>(h) * D;
+        bf16x8_t kf[T::KS], vf[T::KS];
+#pragma unroll
+        for (int s = 0; s < T::KS; ++s) {
+            kf[s] = bf16x8_t{};
+            vf[s] = bf16x8_t{};
+            if (j_ok) {
+                kf[s] = ld_bf16x8(a.K, j * HD + hoff + 32 * s + 8 * g);
+                vf[s] = ld_bf16x8(a.V, j * HD + hoff + 32 * s + 8 * g);
+            }
+        }
+        f32x4_t dk[T::NB], dv[T::NB];
+#pragma unroll
+        for (int s = 0; s < T::NB; ++s) {
+            dk[s] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            dv[s] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        }
+        for (int64_t q = tcb; q < tce; ++q) {
+            const int64_t t = a.tile_bycol[q];
+            const int64_t r0 = static_cast<int64_t>(a.tile_row[t]) * kTileDim;
+            const int64_t arow = min(r0 + c, a.n - 1);    // tile row l%16, as the A operand row
+            RowStat st[4];
+            uint32_t valid = 0;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const int64_t rk = r0 + 4 * g + k;
+                const uint32_t bit = (static_cast<uint32_t>(a.tile_mask[t * kTileDim + 4 * g + k]) >> c) & 1u;
+                valid |= bit << k;
+                st[k] = RowStat{0.f, 0.f};
+                if (bit) st[k] = a.stats[rk * a.H + h];
+            }
+            T::col_step(arow * HD + hoff, st, valid, kf, vf, dk, dv, a.Q, a.dO, qs, os, a.scale2, c, g);
+        }
+        for (int64_t e0 = rcb; e0 < rce; e0 += 16) {
+            const int64_t e = e0 + c;          // row l%16 of this pseudo-tile is residual edge e
+            int cc = -1;
+            int64_t dst = 0;
+            if (e < rce) {
+                dst = a.res_rowidx[e];
+                cc = row_in_block(a.res_colptr, c_lo, c_hi, e);
+            }
+            RowStat st[4];
+            uint32_t valid = 0;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const int lk = 4 * g + k;
+                const bool bit = __shfl(cc, lk) == c;
+                const int64_t dk_row = __shfl(static_cast<int>(dst), lk);
+                valid |= (bit ? 1u : 0u) << k;
+                st[k] = RowStat{0.f, 0.f};
+                if (bit) st[k] = a.stats[dk_row * a.H + h];
+            }
+            T::col_step(dst * HD + hoff, st, valid, kf, vf, dk, dv, a.Q, a.dO, qs, os, a.scale2, c, g);
+        }
+        if (j_ok) {
+#pragma unroll
+            for (int s = 0; s < T::NB; ++s) {
+                store_tile_rows(a.dK, j * HD + hoff + 16 * s + 4 * g, dk[s], a.oscale);
+                store_tile_rows(a.dV, j * HD + hoff + 16 * s + 4 * g, dv[s], 1.f);
+            }
+        }
+    }
+}
+
 }  // namespace sgat

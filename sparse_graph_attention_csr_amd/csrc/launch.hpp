@@ -51,6 +51,12 @@ int launch_gat_bwd(const Plan& p, int H, int D, int dt, const int32_t* colidx, c
 int launch_gt_bs_fwd(const Plan& p, int H, int D, const void* Q, const void* K, const void* V,
                      void* out, float* lse, hipStream_t s);
 
+// Block-sparse backward (bf16 only): dQ and (lse, Delta) per tile row, then
+// dK and dV per tile column. `stats` is the [n][H] (lse*log2 e, Delta) region.
+int launch_gt_bs_bwd(const Plan& p, int H, int D, const void* Q, const void* K, const void* V,
+                     const void* O, const float* lse, const void* dO, void* dQ, void* dK, void* dV,
+                     void* stats, hipStream_t s);
+
 // da = 0 (the empty sum, for a graph without nodes), by a kernel.
 int launch_da_zero(float* da, int HD, hipStream_t s);
 

@@ -28,4 +28,45 @@ int launch_gt_bs_fwd(const Plan& p, int H, int D, const void* Q, const void* K, 
                   dim3(kBlock), &a, s);
 }
 
+int launch_gt_bs_bwd(const Plan& p, int H, int D, const void* Q, const void* K, const void* V,
+                     const void* O, const float* lse, const void* dO, void* dQ, void* dK, void* dV,
+                     void* stats, hipStream_t s)
+{
+    BsBwdArgs a;
+    a.n = p.n;
+    a.n_blocks = (p.n + kTileDim - 1) / kTileDim;
+    a.H = H;
+    a.tile_rowptr = p.dptr<int64_t>(SGAT_ARR_TILE_ROWPTR);
+    a.tile_col = p.dptr<int32_t>(SGAT_ARR_TILE_COL);
+    a.tile_mask = p.dptr<uint16_t>(SGAT_ARR_TILE_MASK);
+    a.tile_row = p.dptr<int32_t>(SGAT_ARR_TILE_ROW);
+    a.tile_colptr = p.dptr<int64_t>(SGAT_ARR_TILE_COLPTR);
+    a.tile_bycol = p.dptr<int32_t>(SGAT_ARR_TILE_BYCOL);
+    a.res_rowptr = p.dptr<int64_t>(SGAT_ARR_RES_ROWPTR);
+    a.res_colidx = p.dptr<int32_t>(SGAT_ARR_RES_COLIDX);
+    a.res_colptr = p.dptr<int64_t>(SGAT_ARR_RES_COLPTR);
+    a.res_rowidx = p.dptr<int32_t>(SGAT_ARR_RES_ROWIDX);
+    a.Q = Q; a.K = K; a.V = V; a.O = O; a.dO = dO;
+    a.lse = lse;
+    a.stats = static_cast<RowStat*>(stats);
+    a.dQ = dQ; a.dK = dK; a.dV = dV;
+    a.scale2 = kLog2e / sqrtf(static_cast<float>(D));
+    a.oscale = 1.f / sqrtf(static_cast<float>(D));
+    const void *fr, *fc;
+    if (D == 32) {
+        fr = reinterpret_cast<const void*>(&gt_bs_bwd_rows<32>);
+        fc = reinterpret_cast<const void*>(&gt_bs_bwd_cols<32>);
+    } else if (D == 64) {
+        fr = reinterpret_cast<const void*>(&gt_bs_bwd_rows<64>);
+        fc = reinterpret_cast<const void*>(&gt_bs_bwd_cols<64>);
+    } else {
+        fr = reinterpret_cast<const void*>(&gt_bs_bwd_rows<128>);
+        fc = reinterpret_cast<const void*>(&gt_bs_bwd_cols<128>);
+    }
+    const dim3 grid(static_cast<unsigned>(wave_grid(a.n_blocks * kWavesPerBlock)));
+    int rc = launch("gt_bs_bwd_rows", fr, grid, dim3(kBlock), &a, s);
+    if (rc) return rc;
+    return launch("gt_bs_bwd_cols", fc, grid, dim3(kBlock), &a, s);
+}
+
 }  // namespace sgat

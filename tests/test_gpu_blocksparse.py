@@ -44,6 +44,28 @@ def run_tiles(r, q, k, v):
     return out, lse
 
 
+def run_tiles_bwd(r, q, k, v, out, lse, do):
+    import torch
+    B, g = r.B, r.g
+    n, H, D = q.shape
+    dq, dk, dv = (torch.empty_like(q) for _ in range(3))
+    ws = g.workspace(B.OP_GT_BWD, H, D, B.BF16)
+    B.gt_bwd(g.plan, g.rowptr, g.colidx, q, k, v, out, lse, do, dq, dk, dv, ws, use_tiles=True)
+    return dq, dk, dv
+
+
+def check_bwd(r, rp, ci, q, k, v, do, out, lse):
+    """Tile backward vs the oracle and vs the gather backward on the same inputs."""
+    Q, K, V, DO = dev(q), dev(k), dev(v), dev(do)
+    g = [host(x) for x in run_tiles_bwd(r, Q, K, V, out, lse, DO)]
+    ref = oracle.gt_bwd(rp, ci, q, k, v, do)
+    for x, y in zip(g, ref):
+        assert rel_err(x, y) <= TOL["bf16"]
+    gather = [host(x) for x in r.gt_bwd(Q, K, V, out, lse, DO)]
+    for x, y in zip(g, gather):
+        assert rel_err(x, y) <= TOL["bf16"]
+
+
 @pytest.mark.parametrize("D", [32, 64, 128])
 @pytest.mark.parametrize("H", [1, 4, 5])
 def test_tiles_match_oracle(H, D):
@@ -51,7 +73,7 @@ def test_tiles_match_oracle(H, D):
     rp, ci = community_graph(8, seed=H * 10 + D)
     n = rp.size - 1
     rng = np.random.default_rng(3)
-    q, k, v = (I.normal_tensor(rng, (n, H, D), I.BF16) for _ in range(3))
+    q, k, v, do = (I.normal_tensor(rng, (n, H, D), I.BF16) for _ in range(4))
     r = Runner(rp, ci, block_sparse=True)
     s = r.g.plan.stats()
     assert s["tiles"] > 0 and s["residual_edges"] > 0
@@ -61,6 +83,7 @@ def test_tiles_match_oracle(H, D):
     assert rel_err(host(lse), rl) <= TOL["bf16"]
     go, gl = r.gt_fwd(dev(q), dev(k), dev(v))
     assert rel_err(host(out), host(go)) <= TOL["bf16"]
+    check_bwd(r, rp, ci, q, k, v, do, out, lse)
 
 
 @pytest.mark.parametrize("tmin", [1, 8, 32, 200])
@@ -75,7 +98,7 @@ def test_tiles_thresholds_ragged_dups_empty(tmin):
     ci = np.where(ci < n, ci, ci % n).astype(np.int32)
     H, D = 4, 64
     rng = np.random.default_rng(4)
-    q, k, v = (I.normal_tensor(rng, (n, H, D), I.BF16) for _ in range(3))
+    q, k, v, do = (I.normal_tensor(rng, (n, H, D), I.BF16) for _ in range(4))
     r = Runner(rp, ci, block_sparse=True, tile_min_nnz=tmin)
     out, lse = run_tiles(r, dev(q), dev(k), dev(v))
     ro, rl = oracle.gt_fwd(rp, ci, q, k, v)
@@ -83,6 +106,7 @@ def test_tiles_thresholds_ragged_dups_empty(tmin):
     assert rel_err(host(lse), rl) <= TOL["bf16"]
     empty = np.diff(rp) == 0
     assert empty.any() and np.all(host(out)[empty] == 0)
+    check_bwd(r, rp, ci, q, k, v, do, out, lse)
 
 
 def test_tiles_random_graph_and_single_neighbour():
@@ -90,12 +114,13 @@ def test_tiles_random_graph_and_single_neighbour():
     rng = np.random.default_rng(5)
     rp, ci = I.random_csr(333, 30, rng, empty_frac=0.05, dup_frac=0.1)
     H, D = 3, 128
-    q, k, v = (I.normal_tensor(rng, (333, H, D), I.BF16) for _ in range(3))
+    q, k, v, do = (I.normal_tensor(rng, (333, H, D), I.BF16) for _ in range(4))
     r = Runner(rp, ci, block_sparse=True, tile_min_nnz=2)
     out, lse = run_tiles(r, dev(q), dev(k), dev(v))
     ro, rl = oracle.gt_fwd(rp, ci, q, k, v)
     assert rel_err(host(out), ro) <= TOL["bf16"]
     assert rel_err(host(lse), rl) <= TOL["bf16"]
+    check_bwd(r, rp, ci, q, k, v, do, out, lse)
     # every row with one in-edge: weight 1 exactly, out = that neighbour's V
     n = 200
     rp1 = np.arange(n + 1, dtype=np.int64)
@@ -111,11 +136,13 @@ def test_tiles_bitwise_deterministic():
     rp, ci = community_graph(4, seed=9)
     n = rp.size - 1
     rng = np.random.default_rng(6)
-    q, k, v = (dev(I.normal_tensor(rng, (n, 4, 128), I.BF16)) for _ in range(3))
+    q, k, v, do = (dev(I.normal_tensor(rng, (n, 4, 128), I.BF16)) for _ in range(4))
     r = Runner(rp, ci, block_sparse=True)
-    a = [host(x) for x in run_tiles(r, q, k, v)]
-    b = [host(x) for x in run_tiles(r, q, k, v)]
-    assert all(np.array_equal(x, y) for x, y in zip(a, b))
+    res = []
+    for _ in range(2):
+        out, lse = run_tiles(r, q, k, v)
+        res.append([host(x) for x in (out, lse, *run_tiles_bwd(r, q, k, v, out, lse, do))])
+    assert all(np.array_equal(x, y) for x, y in zip(*res))
 
 
 def test_tiles_rejected_without_layout_or_fp32():

@@ -104,6 +104,39 @@ def test_gt_community_full_size():
     run_gt("gt_community262k_h4d128_bf16")
 
 
+@pytest.mark.timeout(600)
+def test_gt_community_tiles_full_size():
+    """The community workload on the 16x16 tile (MFMA) path, forward and backward."""
+    import torch
+    name = "gt_community262k_h4d128_bf16"
+    note(f"{name} tiles: generating")
+    w = I.make_workload(name)
+    rp, ci = w["rowptr"], w["colidx"]
+    r = Runner(rp, ci, block_sparse=True)
+    st = r.g.plan.stats()
+    note(f"  tiles={st['tiles']} tile_edges={st['tile_edges']} residual={st['residual_edges']}")
+    q, k, v, do = dev(w["q"]), dev(w["k"]), dev(w["v"]), dev(w["dout"])
+    n, H, D = q.shape
+    B_ = r.B
+    out = torch.empty_like(q)
+    lse = torch.empty(n, H, dtype=torch.float32, device=q.device)
+    B_.gt_fwd(r.g.plan, r.g.rowptr, r.g.colidx, q, k, v, out, lse,
+              r.g.workspace(B_.OP_GT_FWD, H, D, B_.BF16), use_tiles=True)
+    dq, dk, dv = (torch.empty_like(q) for _ in range(3))
+    B_.gt_bwd(r.g.plan, r.g.rowptr, r.g.colidx, q, k, v, out, lse, do, dq, dk, dv,
+              r.g.workspace(B_.OP_GT_BWD, H, D, B_.BF16), use_tiles=True)
+    finite(out, dq, dk, dv)
+    dst, src, heavy, ctop = samples(rp, r.g.plan)
+    ro, rl = oracle.gt_fwd(rp, ci, w["q"], w["k"], w["v"], rows=dst)
+    check("out", pick(out, dst), ro, "bf16")
+    check("lse", pick(lse, dst), rl, "bf16")
+    rq, rk, rv = oracle.gt_bwd(rp, ci, w["q"], w["k"], w["v"], w["dout"], dst_rows=dst,
+                               src_rows=src)
+    check("dQ", pick(dq, dst), rq, "bf16")
+    check("dK", pick(dk, src), rk, "bf16")
+    check("dV", pick(dv, src), rv, "bf16")
+
+
 @pytest.mark.timeout(900)
 def test_gt_hubs_full_size():
     run_gt("gt_hubs2m_h8d64_bf16")
