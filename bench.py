@@ -92,10 +92,13 @@ def algorithmic_bytes(kernel: str, n: int, e: int, H: int, D: int, b: int,
     model = {
         # K_j, V_j and colidx per edge; Q_i read, out_i and lse_i written per node
         "gt_fwd_rows": (2 * R + 4, 2 * R + 4 * H + 8),
-        # K_j, V_j, colidx per edge; Q_i, dO_i, O_i, lse_i read, dQ_i and (lse, Delta) written
-        "gt_bwd_rows": (2 * R + 4, 4 * R + 12 * H + 8),
-        # Q_i, dO_i, (lse_i, Delta_i), rowidx per edge; K_j, V_j read, dK_j, dV_j written
-        "gt_bwd_cols": (2 * R + 8 * H + 4, 4 * R + 8),
+        # O_i, dO_i, lse_i read and (lse, Delta) written per node
+        "gt_bwd_delta": (0, 2 * R + 12 * H),
+        # Q_i, dO_i, (lse_i, Delta_i), rowidx, edge id read and dS written per edge;
+        # K_j, V_j read, dK_j, dV_j written per node
+        "gt_bwd_cols": (2 * R + 12 * H + 8, 4 * R + 8),
+        # K_j, colidx, dS per edge; dQ_i written per node
+        "gt_bwd_rows": (R + 4 + 4 * H, R + 8),
         # Xt_j and colidx per edge; Xs_i read, out_i, lse_i written
         "gat_fwd_rows": (R + 4, 2 * R + 4 * H + 8),
         # Xt_j, colidx per edge; Xs_i, dO_i, O_i, lse_i read, dXs_i, (lse, Delta) written

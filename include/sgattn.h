@@ -118,7 +118,8 @@ typedef enum sgat_array {
     SGAT_ARR_TILE_BYCOL = 13, /* int32 [tiles]: tile ids by block column, then row      */
     SGAT_ARR_RES_COLPTR = 14, /* int64 [n+1]: residual edges grouped by source          */
     SGAT_ARR_RES_ROWIDX = 15, /* int32 [residual_edges]: their destinations             */
-    SGAT_ARR_COUNT = 16
+    SGAT_ARR_COL_EDGE = 16,   /* int32 [nnz]: CSR edge id of each transposed-CSR entry  */
+    SGAT_ARR_COUNT = 17
 } sgat_array;
 
 /* One unit of work of the gather kernels: `len` consecutive edges starting at

@@ -84,7 +84,9 @@ def work_list(ptr: np.ndarray, chunk: int):
     return np.concatenate([chunks, whole]), splits, int(crow.size)
 
 
-def transpose(rowptr: np.ndarray, colidx: np.ndarray):
+def transpose(rowptr: np.ndarray, colidx: np.ndarray, edge_ids: bool = False):
+    """(colptr, rowidx) of the transposed CSR; with edge_ids also the CSR edge
+    id of every transposed entry."""
     rowptr = np.asarray(rowptr, dtype=np.int64)
     colidx = np.asarray(colidx, dtype=np.int64)
     n = rowptr.size - 1
@@ -92,6 +94,8 @@ def transpose(rowptr: np.ndarray, colidx: np.ndarray):
     order = np.argsort(colidx, kind="stable")
     colptr = np.zeros(n + 1, dtype=np.int64)
     np.cumsum(np.bincount(colidx, minlength=n), out=colptr[1:])
+    if edge_ids:
+        return colptr, dst[order].astype(np.int32), order.astype(np.int32)
     return colptr, dst[order].astype(np.int32)
 
 

@@ -116,6 +116,7 @@ Layout ws_layout(const Plan& p, int op, int H, int D)
         sz[1] = static_cast<size_t>(p.row_slots) * HD * 4;          // dQ partials
         sz[2] = static_cast<size_t>(p.col_slots) * HD * 4;          // dK partials
         sz[3] = static_cast<size_t>(p.col_slots) * HD * 4;          // dV partials
+        sz[4] = static_cast<size_t>(p.nnz) * H * 4;                 // dS per edge
         break;
     case SGAT_OP_GAT_BWD:
         sz[0] = static_cast<size_t>(p.n) * H * 8;                   // stats
@@ -241,7 +242,7 @@ int gt_bwd(const sgat_plan* plan, int64_t n, int64_t nnz, const int64_t* rowptr,
         return launch_gt_bs_bwd(plan->p, H, D, Q, K, V, out, lse, dout, dQ, dK, dV,
                                 at<void>(ws, L.off[0]), static_cast<hipStream_t>(stream));
     BwdWs w{at<void>(ws, L.off[0]), at<float>(ws, L.off[1]), at<float>(ws, L.off[2]),
-            at<float>(ws, L.off[3]), nullptr};
+            at<float>(ws, L.off[3]), nullptr, at<float>(ws, L.off[4])};
     return launch_gt_bwd(plan->p, H, D, dtype, colidx, Q, K, V, out, lse, dout, dQ, dK, dV, w,
                          static_cast<hipStream_t>(stream));
 }
@@ -283,7 +284,7 @@ int gat_bwd(const sgat_plan* plan, int64_t n, int64_t nnz, const int64_t* rowptr
     if ((rc = check_ws(plan->p, SGAT_OP_GAT_BWD, H, D, ws, ws_bytes, L))) return rc;
     if (n == 0) return launch_da_zero(da, H * D, static_cast<hipStream_t>(stream));
     BwdWs w{at<void>(ws, L.off[0]), at<float>(ws, L.off[1]), at<float>(ws, L.off[2]), nullptr,
-            at<float>(ws, L.off[4])};
+            at<float>(ws, L.off[4]), nullptr};
     return launch_gat_bwd(plan->p, H, D, dtype, colidx, x_dst, x_nbr, a, negative_slope, out, lse,
                           dout, dx_dst, dx_nbr, da, w, static_cast<hipStream_t>(stream));
 }

@@ -10,9 +10,13 @@
 //
 // The backward recomputes alpha_ij = exp(s_ij - lse_i) from the forward's
 // per-(node, head) log-sum-exp (same paragraph: recomputation from compact
-// statistics). The CSR pass produces dQ (or dXs and da) and the statistic
-// Delta_i = dout_i . out_i; the transposed-CSR pass produces dK, dV (or dXt)
-// by gathering over each source's out-edges, so no atomics are needed.
+// statistics), with Delta_i = dout_i . out_i. Gradients that belong to a
+// destination are summed over the CSR, those that belong to a source over the
+// transposed CSR, so no atomics are needed. Graph Transformer: the
+// transposed-CSR pass runs first; it holds K_j and V_j of its source, gathers
+// Q_i and dout_i, forms dS_ij and writes it (H floats per edge) for the CSR
+// pass, which then gathers only K_j for dQ. GATv2: the CSR pass (dXs, da,
+// Delta) runs first and the transposed pass (dXt) recomputes everything.
 #pragma once
 
 #include "device.hpp"
@@ -334,17 +338,51 @@ __device__ __forceinline__ void grad_store(const float (&x)[VEC], float scale,
     }
 }
 
+// Delta pre-pass of the Graph Transformer backward: (lse * log2 e, Delta) per
+// (node, head); EPW consecutive nodes per wave.
+struct DeltaArgs {
+    int64_t n_units, n;
+    int n_hg, H;
+    const void *O, *dO;
+    const float* lse;
+    RowStat* stats;
+};
+
+template <int DT, int D, int EPW>
+__global__ __launch_bounds__(kBlock) void bwd_delta(DeltaArgs a)
+{
+    using G = Geo<DT, D, EPW>;
+    const int64_t unit = logical_block() * kWavesPerBlock + wave_id();
+    if (unit >= a.n_units) return;
+    const int64_t ng = unit / a.n_hg;
+    const int hg = static_cast<int>(unit - ng * a.n_hg);
+    const G g(hg, a.H);
+    const int64_t node = ng * EPW + g.sub;
+    const bool ok = node < a.n && g.hvalid;
+    const int64_t HD = static_cast<int64_t>(a.H) * D;
+    Frag of = frag_zero(), dof = frag_zero();
+    if (ok) {
+        of = ldg<DT>(a.O, node * HD + g.col);
+        dof = ldg<DT>(a.dO, node * HD + g.col);
+    }
+    const float delta = head_sum<G::SPH>(dot<DT>(dof, of));
+    if (ok && g.leader) {
+        const int64_t k = node * a.H + g.head;
+        a.stats[k] = RowStat{a.lse[k] * kLog2e, delta};
+    }
+}
+
+// Graph Transformer CSR pass: dQ_i = (1/sqrt(D)) sum_j dS_ij K_j, with dS read
+// from the transposed pass's per-edge output (CSR edge order, [E][H]).
 struct GtBwdRowArgs {
     const sgat_work_item* items;
     int64_t n_units;
     int n_hg, H;
     const int32_t* colidx;
-    const void *Q, *K, *V, *O, *dO;
-    const float* lse;
-    RowStat* stats;
+    const void* K;
+    const float* ds;
     void* dQ;
     float* part;
-    float scale2;   // log2(e) / sqrt(D)
     float oscale;   // 1 / sqrt(D)
 };
 
@@ -360,50 +398,33 @@ __global__ __launch_bounds__(kBlock) void gt_bwd_rows(GtBwdRowArgs a)
     const sgat_work_item it = a.items[ii];
     const G g(hg, a.H);
     const int64_t HD = static_cast<int64_t>(a.H) * D;
-    const int64_t ro = static_cast<int64_t>(it.row) * HD + g.col;
-
-    Frag q = frag_zero(), dof = frag_zero(), of = frag_zero();
-    float lse2 = 0.f;
-    if (g.hvalid) {
-        q = ldg<DT>(a.Q, ro);
-        dof = ldg<DT>(a.dO, ro);
-        of = ldg<DT>(a.O, ro);
-        lse2 = a.lse[static_cast<int64_t>(it.row) * a.H + g.head] * kLog2e;
-    }
-    const float delta = head_sum<G::SPH>(dot<DT>(dof, of));
-    if ((it.flags & 1) && g.sub == 0 && g.hvalid && g.leader)
-        a.stats[static_cast<int64_t>(it.row) * a.H + g.head] = RowStat{lse2, delta};
 
     float dq[VEC] = {};
     const int32_t* ci = a.colidx + it.begin;
+    const float* dsr = a.ds + it.begin * a.H + g.head;
     for (int base = 0; base < it.len; base += kWave) {
         const int nb = min(kWave, it.len - base);
         const int cj = g.lane < nb ? ci[base + g.lane] : 0;
         for (int t = 0; t < nb; t += EPW * U) {
-            Frag kf[U], vf[U];
-            bool ok[U];
+            Frag kf[U];
+            float d[U];
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const int e = t + u * EPW + g.sub;
-                ok[u] = e < nb;
                 const int64_t j = bcast<EPW>(cj, e);
                 kf[u] = frag_zero();
-                vf[u] = frag_zero();
-                if (ok[u] && g.hvalid) {
+                d[u] = 0.f;
+                if (e < nb && g.hvalid) {
                     kf[u] = ldg<DT>(a.K, j * HD + g.col);
-                    vf[u] = ldg<DT>(a.V, j * HD + g.col);
+                    d[u] = dsr[static_cast<int64_t>(base + e) * a.H];
                 }
             }
 #pragma unroll
             for (int u = 0; u < U; ++u) {
-                const float s2 = head_sum<G::SPH>(dot<DT>(q, kf[u])) * a.scale2;
-                const float dp = head_sum<G::SPH>(dot<DT>(dof, vf[u]));
-                const float p = ok[u] ? fast_exp2(s2 - lse2) : 0.f;
-                const float ds = p * (dp - delta);
                 float kx[VEC];
                 to_f32<DT>(kf[u], kx);
 #pragma unroll
-                for (int k = 0; k < VEC; ++k) dq[k] = fmaf(ds, kx[k], dq[k]);
+                for (int k = 0; k < VEC; ++k) dq[k] = fmaf(d[u], kx[k], dq[k]);
             }
         }
     }
@@ -536,10 +557,12 @@ struct GtBwdColArgs {
     int64_t n_units;
     int n_hg, H;
     const int32_t* rowidx;
+    const int32_t* col_edge;   // CSR edge id of each transposed entry
     const void *Q, *K, *V, *dO;
     const RowStat* stats;
     void *dK, *dV;
     float *part_k, *part_v;
+    float* ds;                 // out: dS per (CSR edge, head)
     float scale2, oscale;
 };
 
@@ -563,18 +586,22 @@ __global__ __launch_bounds__(kBlock) void gt_bwd_cols(GtBwdColArgs a)
     }
     float dk[VEC] = {}, dv[VEC] = {};
     const int32_t* ri = a.rowidx + it.begin;
+    const int32_t* re = a.col_edge + it.begin;
     for (int base = 0; base < it.len; base += kWave) {
         const int nb = min(kWave, it.len - base);
         const int ci = g.lane < nb ? ri[base + g.lane] : 0;
+        const int ce = g.lane < nb ? re[base + g.lane] : 0;
         for (int t = 0; t < nb; t += EPW * U) {
             Frag qf[U], df[U];
             RowStat rs[U];
             bool ok[U];
+            int64_t eid[U];
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const int e = t + u * EPW + g.sub;
                 ok[u] = e < nb;
                 const int64_t i = bcast<EPW>(ci, e);
+                eid[u] = bcast<EPW>(ce, e);
                 qf[u] = frag_zero();
                 df[u] = frag_zero();
                 rs[u] = RowStat{0.f, 0.f};
@@ -590,6 +617,7 @@ __global__ __launch_bounds__(kBlock) void gt_bwd_cols(GtBwdColArgs a)
                 const float dp = head_sum<G::SPH>(dot<DT>(df[u], vj));
                 const float p = ok[u] ? fast_exp2(s2 - rs[u].lse2) : 0.f;
                 const float ds = p * (dp - rs[u].delta);
+                if (ok[u] && g.hvalid && g.leader) a.ds[eid[u] * a.H + g.head] = ds;
                 float qx[VEC], dx[VEC];
                 to_f32<DT>(qf[u], qx);
                 to_f32<DT>(df[u], dx);

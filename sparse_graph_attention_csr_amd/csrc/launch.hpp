@@ -31,6 +31,7 @@ struct BwdWs {
     float* part_col0;  // [col_slots][H*D]
     float* part_col1;  // [col_slots][H*D] (GT only)
     float* da_part;    // [gat_bwd_row_blocks][H*D] (GATv2 only)
+    float* ds;         // [nnz][H] dS per edge (Graph Transformer only)
 };
 
 int launch_gt_fwd(const Plan& p, int H, int D, int dt, const int32_t* colidx, const void* Q,

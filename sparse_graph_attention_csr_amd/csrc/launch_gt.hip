@@ -69,19 +69,14 @@ int launch_gt_bwd(const Plan& p, int H, int D, int dt, const int32_t* colidx, co
     const float oscale = 1.f / sqrtf(static_cast<float>(D));
     const int HD = H * D;
 
-    GtBwdRowArgs r;
-    r.items = p.dptr<sgat_work_item>(SGAT_ARR_ROW_ITEMS);
-    r.n_units = static_cast<int64_t>(p.row_items.size()) * dc.n_hg;
-    r.n_hg = dc.n_hg;
-    r.H = H;
-    r.colidx = colidx;
-    r.Q = Q; r.K = K; r.V = V; r.O = O; r.dO = dO;
-    r.lse = lse;
-    r.stats = static_cast<RowStat*>(ws.stats);
-    r.dQ = dQ;
-    r.part = ws.part_row;
-    r.scale2 = scale2;
-    r.oscale = oscale;
+    DeltaArgs d;
+    d.n = p.n;
+    d.n_units = (p.n + dc.epw - 1) / dc.epw * dc.n_hg;
+    d.n_hg = dc.n_hg;
+    d.H = H;
+    d.O = O; d.dO = dO;
+    d.lse = lse;
+    d.stats = static_cast<RowStat*>(ws.stats);
 
     GtBwdColArgs c;
     c.items = p.dptr<sgat_work_item>(SGAT_ARR_COL_ITEMS);
@@ -89,31 +84,41 @@ int launch_gt_bwd(const Plan& p, int H, int D, int dt, const int32_t* colidx, co
     c.n_hg = dc.n_hg;
     c.H = H;
     c.rowidx = p.dptr<int32_t>(SGAT_ARR_ROWIDX);
+    c.col_edge = p.dptr<int32_t>(SGAT_ARR_COL_EDGE);
     c.Q = Q; c.K = K; c.V = V; c.dO = dO;
     c.stats = static_cast<const RowStat*>(ws.stats);
     c.dK = dK; c.dV = dV;
     c.part_k = ws.part_col0;
     c.part_v = ws.part_col1;
+    c.ds = ws.ds;
     c.scale2 = scale2;
     c.oscale = oscale;
 
-    const void *fr = nullptr, *fc = nullptr;
+    GtBwdRowArgs r;
+    r.items = p.dptr<sgat_work_item>(SGAT_ARR_ROW_ITEMS);
+    r.n_units = static_cast<int64_t>(p.row_items.size()) * dc.n_hg;
+    r.n_hg = dc.n_hg;
+    r.H = H;
+    r.colidx = colidx;
+    r.K = K;
+    r.ds = ws.ds;
+    r.dQ = dQ;
+    r.part = ws.part_row;
+    r.oscale = oscale;
+
+    const void *fd = nullptr, *fr = nullptr, *fc = nullptr;
 #define X(DT_, D_, E_)                                                                 \
     if (dt == DT_ && D == D_ && dc.epw == E_) {                                        \
-        fr = reinterpret_cast<const void*>(&gt_bwd_rows<DT_, D_, E_, kUnrollBwd>);     \
+        fd = reinterpret_cast<const void*>(&bwd_delta<DT_, D_, E_>);                   \
+        fr = reinterpret_cast<const void*>(&gt_bwd_rows<DT_, D_, E_, kUnrollFwd>);     \
         fc = reinterpret_cast<const void*>(&gt_bwd_cols<DT_, D_, E_, kUnrollBwd>);     \
     }
     SGAT_GATHER_CONFIGS(X)
 #undef X
-    if (!fr || !fc) return SGAT_INVALID_ARGUMENT;
+    if (!fd || !fr || !fc) return SGAT_INVALID_ARGUMENT;
     int rc;
-    if (r.n_units > 0 &&
-        (rc = launch("gt_bwd_rows", fr, dim3(static_cast<unsigned>(wave_grid(r.n_units))),
-                     dim3(kBlock), &r, s)))
-        return rc;
-    if ((rc = merge_sum("gt_bwd_rows_merge", p.row_splits,
-                        p.dptr<sgat_split>(SGAT_ARR_ROW_SPLITS), HD, ws.part_row, oscale, dQ, dt,
-                        s)))
+    if ((rc = launch("gt_bwd_delta", fd, dim3(static_cast<unsigned>(wave_grid(d.n_units))),
+                     dim3(kBlock), &d, s)))
         return rc;
     if (c.n_units > 0 &&
         (rc = launch("gt_bwd_cols", fc, dim3(static_cast<unsigned>(wave_grid(c.n_units))),
@@ -123,7 +128,14 @@ int launch_gt_bwd(const Plan& p, int H, int D, int dt, const int32_t* colidx, co
     if ((rc = merge_sum("gt_bwd_cols_merge", p.col_splits, csp, HD, ws.part_col0, oscale, dK, dt,
                         s)))
         return rc;
-    return merge_sum("gt_bwd_cols_merge", p.col_splits, csp, HD, ws.part_col1, 1.f, dV, dt, s);
+    if ((rc = merge_sum("gt_bwd_cols_merge", p.col_splits, csp, HD, ws.part_col1, 1.f, dV, dt, s)))
+        return rc;
+    if (r.n_units > 0 &&
+        (rc = launch("gt_bwd_rows", fr, dim3(static_cast<unsigned>(wave_grid(r.n_units))),
+                     dim3(kBlock), &r, s)))
+        return rc;
+    return merge_sum("gt_bwd_rows_merge", p.row_splits, p.dptr<sgat_split>(SGAT_ARR_ROW_SPLITS),
+                     HD, ws.part_row, oscale, dQ, dt, s);
 }
 
 }  // namespace sgat

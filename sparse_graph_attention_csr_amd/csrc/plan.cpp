@@ -82,7 +82,8 @@ void build_work_list(int64_t n, const int64_t* ptr, int64_t chunk,
 }
 
 void build_transpose(int64_t n, const int64_t* rowptr, const int32_t* colidx,
-                     std::vector<int64_t>& colptr, std::vector<int32_t>& rowidx)
+                     std::vector<int64_t>& colptr, std::vector<int32_t>& rowidx,
+                     std::vector<int32_t>* edge_ids)
 {
     int64_t nnz = rowptr[n];
     colptr.assign(static_cast<size_t>(n) + 1, 0);
@@ -90,9 +91,13 @@ void build_transpose(int64_t n, const int64_t* rowptr, const int32_t* colidx,
     for (int64_t j = 0; j < n; ++j) colptr[j + 1] += colptr[j];
     std::vector<int64_t> fill(colptr.begin(), colptr.end() - 1);
     rowidx.assign(static_cast<size_t>(nnz), 0);
+    if (edge_ids) edge_ids->assign(static_cast<size_t>(nnz), 0);
     for (int64_t i = 0; i < n; ++i)
-        for (int64_t e = rowptr[i]; e < rowptr[i + 1]; ++e)
-            rowidx[static_cast<size_t>(fill[colidx[e]]++)] = static_cast<int32_t>(i);
+        for (int64_t e = rowptr[i]; e < rowptr[i + 1]; ++e) {
+            const size_t t = static_cast<size_t>(fill[colidx[e]]++);
+            rowidx[t] = static_cast<int32_t>(i);
+            if (edge_ids) (*edge_ids)[t] = static_cast<int32_t>(e);
+        }
 }
 
 void build_tiles(int64_t n, const int64_t* rowptr, const int32_t* colidx, int32_t min_nnz,
@@ -198,6 +203,7 @@ const void* Plan::host_array(int id) const
     case SGAT_ARR_TILE_BYCOL: return tile_bycol.data();
     case SGAT_ARR_RES_COLPTR: return res_colptr.data();
     case SGAT_ARR_RES_ROWIDX: return res_rowidx.data();
+    case SGAT_ARR_COL_EDGE: return col_edge.data();
     default: return nullptr;
     }
 }
@@ -220,6 +226,7 @@ void Plan::layout()
     bytes[SGAT_ARR_TILE_BYCOL] = tile_bycol.size() * sizeof(int32_t);
     bytes[SGAT_ARR_RES_COLPTR] = res_colptr.size() * sizeof(int64_t);
     bytes[SGAT_ARR_RES_ROWIDX] = res_rowidx.size() * sizeof(int32_t);
+    bytes[SGAT_ARR_COL_EDGE] = col_edge.size() * sizeof(int32_t);
     size_t off = 0;
     for (int a = 0; a < SGAT_ARR_COUNT; ++a) {
         offset[a] = off;
@@ -264,7 +271,7 @@ int sgat_plan_create(int64_t n, int64_t nnz, const int64_t* rowptr, const int32_
         for (int64_t i = 0; i < n; ++i)
             p.max_in_degree = std::max(p.max_in_degree, rowptr[i + 1] - rowptr[i]);
         sgat::build_work_list(n, rowptr, chunk, p.row_items, p.row_splits, p.row_slots);
-        sgat::build_transpose(n, rowptr, colidx, p.colptr, p.rowidx);
+        sgat::build_transpose(n, rowptr, colidx, p.colptr, p.rowidx, &p.col_edge);
         for (int64_t j = 0; j < n; ++j)
             p.max_out_degree = std::max(p.max_out_degree, p.colptr[j + 1] - p.colptr[j]);
         sgat::build_work_list(n, p.colptr.data(), chunk, p.col_items, p.col_splits, p.col_slots);

@@ -29,6 +29,7 @@ struct Plan {
 
     std::vector<int64_t> colptr;
     std::vector<int32_t> rowidx;
+    std::vector<int32_t> col_edge;      // CSR edge id of each transposed entry
     std::vector<sgat_work_item> col_items;
     std::vector<sgat_split> col_splits;
     int64_t col_slots = 0;
@@ -66,9 +67,11 @@ void build_work_list(int64_t n, const int64_t* ptr, int64_t chunk,
                      std::vector<sgat_work_item>& items, std::vector<sgat_split>& splits,
                      int64_t& nslots);
 
-// A3: transposed CSR by stable counting sort of edges by source.
+// A3: transposed CSR by stable counting sort of edges by source; with
+// `edge_ids` also the CSR edge id of every transposed entry.
 void build_transpose(int64_t n, const int64_t* rowptr, const int32_t* colidx,
-                     std::vector<int64_t>& colptr, std::vector<int32_t>& rowidx);
+                     std::vector<int64_t>& colptr, std::vector<int32_t>& rowidx,
+                     std::vector<int32_t>* edge_ids = nullptr);
 
 // A4: 16x16 dense tiles with at least `min_nnz` distinct edges, plus residual CSR.
 void build_tiles(int64_t n, const int64_t* rowptr, const int32_t* colidx, int32_t min_nnz,

@@ -16,9 +16,10 @@ def check_plan(rowptr, colidx, chunk, tmin=0, bs=False):
     items, splits, nslots = S.work_list(rowptr, C)
     assert p.export(B.ARR_ROW_ITEMS).tobytes() == items.tobytes()
     assert p.export(B.ARR_ROW_SPLITS).tobytes() == splits.tobytes()
-    colptr, rowidx = S.transpose(rowptr, colidx)
+    colptr, rowidx, col_edge = S.transpose(rowptr, colidx, edge_ids=True)
     assert np.array_equal(p.export(B.ARR_COLPTR), colptr)
     assert np.array_equal(p.export(B.ARR_ROWIDX), rowidx)
+    assert np.array_equal(p.export(B.ARR_COL_EDGE), col_edge)
     citems, csplits, cslots = S.work_list(colptr, C)
     assert p.export(B.ARR_COL_ITEMS).tobytes() == citems.tobytes()
     assert p.export(B.ARR_COL_SPLITS).tobytes() == csplits.tobytes()
@@ -64,6 +65,11 @@ def invariants(p, rowptr, colidx):
     a = np.sort(dst.astype(np.int64) * n + colidx)
     b = np.sort(rowidx.astype(np.int64) * n + np.repeat(np.arange(n), np.diff(colptr)))
     assert np.array_equal(a, b)
+    # each transposed entry names its CSR edge: same source and destination
+    ce = p.export(B.ARR_COL_EDGE)
+    assert np.array_equal(np.sort(ce), np.arange(E))
+    assert np.array_equal(colidx[ce], np.repeat(np.arange(n), np.diff(colptr)))
+    assert np.array_equal(dst[ce], rowidx)
 
 
 GRAPHS = {
