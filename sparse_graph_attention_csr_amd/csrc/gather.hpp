@@ -256,7 +256,18 @@ __global__ __launch_bounds__(kBlock) void gat_fwd_rows(GatFwdArgs a)
                            a.part_ml);
 }
 
-// Log-sum-exp merge of the chunks of split rows, chunk order fixed.
+// Merges of split rows. Grid: (split, block of channels). A block covers EB =
+// min(H*D, 256) channels with G = 256 / EB groups of threads; group q takes
+// chunks q, q+G, q+2G, ... in order, and group 0 combines the G group results
+// in group order, so the result is fixed for a given plan.
+__device__ __forceinline__ void merge_geometry(int HD, int& eb, int& grp, int& e)
+{
+    eb = HD < kBlock ? HD : kBlock;
+    grp = threadIdx.x / eb;
+    e = blockIdx.y * eb + static_cast<int>(threadIdx.x) % eb;
+}
+
+// Log-sum-exp merge of the chunks of split rows (forward).
 struct LseMergeArgs {
     const sgat_split* splits;
     int H, D;
@@ -268,54 +279,121 @@ struct LseMergeArgs {
 template <int DT>
 __global__ __launch_bounds__(kBlock) void lse_merge(LseMergeArgs a)
 {
+    __shared__ float red[3][kBlock];
     const sgat_split sp = a.splits[blockIdx.x];
     const int HD = a.H * a.D;
-    const float2* ml = reinterpret_cast<const float2*>(a.part_ml);
-    for (int e = threadIdx.x; e < HD; e += blockDim.x) {
-        const int h = e / a.D;
-        float M = kNegInf;
-        for (int k = 0; k < sp.nslots; ++k)
-            M = fmaxf(M, ml[static_cast<int64_t>(sp.first_slot + k) * a.H + h].x);
-        float L = 0.f, A = 0.f;
+    int eb, grp, e;
+    merge_geometry(HD, eb, grp, e);
+    const int G = kBlock / eb;
+    const bool live = e < HD && grp < G;
+    const int h = live ? e / a.D : 0;
+    const float2* ml = reinterpret_cast<const float2*>(a.part_ml) + static_cast<int64_t>(sp.first_slot) * a.H + h;
+    const float* pa = a.part_acc + static_cast<int64_t>(sp.first_slot) * HD + (live ? e : 0);
+    float M = kNegInf, L = 0.f, A = 0.f;
+    if (live) {
+        int k0 = grp;
+        for (; k0 + 7 * G < sp.nslots; k0 += 8 * G) {
+            float x[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) x[u] = ml[static_cast<int64_t>(k0 + u * G) * a.H].x;
+#pragma unroll
+            for (int u = 0; u < 8; ++u) M = fmaxf(M, x[u]);
+        }
+        for (; k0 < sp.nslots; k0 += G) M = fmaxf(M, ml[static_cast<int64_t>(k0) * a.H].x);
         if (M != kNegInf) {
-            for (int k = 0; k < sp.nslots; ++k) {
-                const int64_t s = sp.first_slot + k;
-                const float2 v = ml[s * a.H + h];
+            int k = grp;
+            for (; k + 7 * G < sp.nslots; k += 8 * G) {
+                float2 v[8];
+                float x[8];
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    v[u] = ml[static_cast<int64_t>(k + u * G) * a.H];
+                    x[u] = pa[static_cast<int64_t>(k + u * G) * HD];
+                }
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    const float c = v[u].x == kNegInf ? 0.f : fast_exp2(v[u].x - M);
+                    L = fmaf(v[u].y, c, L);
+                    A = fmaf(x[u], c, A);
+                }
+            }
+            for (; k < sp.nslots; k += G) {
+                const float2 v = ml[static_cast<int64_t>(k) * a.H];
                 const float c = v.x == kNegInf ? 0.f : fast_exp2(v.x - M);
                 L = fmaf(v.y, c, L);
-                A = fmaf(a.part_acc[s * HD + e], c, A);
+                A = fmaf(pa[static_cast<int64_t>(k) * HD], c, A);
             }
         }
-        const float o = L > 0.f ? A / L : 0.f;
-        const int64_t oi = static_cast<int64_t>(sp.row) * HD + e;
-        if constexpr (DT == SGAT_F32) static_cast<float*>(a.out)[oi] = o;
-        else static_cast<__bf16*>(a.out)[oi] = static_cast<__bf16>(o);
-        if (e % a.D == 0)
-            a.lse[static_cast<int64_t>(sp.row) * a.H + h] = L > 0.f ? (M + __log2f(L)) * kLn2 : kNegInf;
     }
+    red[0][threadIdx.x] = M;
+    red[1][threadIdx.x] = L;
+    red[2][threadIdx.x] = A;
+    __syncthreads();
+    if (!live || grp != 0) return;
+    float Mt = kNegInf;
+    for (int q = 0; q < G; ++q) Mt = fmaxf(Mt, red[0][q * eb + threadIdx.x]);
+    float Lt = 0.f, At = 0.f;
+    if (Mt != kNegInf) {
+        for (int q = 0; q < G; ++q) {
+            const float mq = red[0][q * eb + threadIdx.x];
+            const float c = mq == kNegInf ? 0.f : fast_exp2(mq - Mt);
+            Lt = fmaf(red[1][q * eb + threadIdx.x], c, Lt);
+            At = fmaf(red[2][q * eb + threadIdx.x], c, At);
+        }
+    }
+    const float o = Lt > 0.f ? At / Lt : 0.f;
+    const int64_t oi = static_cast<int64_t>(sp.row) * HD + e;
+    if constexpr (DT == SGAT_F32) static_cast<float*>(a.out)[oi] = o;
+    else static_cast<__bf16*>(a.out)[oi] = static_cast<__bf16>(o);
+    if (e % a.D == 0)
+        a.lse[static_cast<int64_t>(sp.row) * a.H + h] = Lt > 0.f ? (Mt + __log2f(Lt)) * kLn2 : kNegInf;
 }
 
-// Fixed-order sum of the partial gradients of split rows (or sources).
+// Fixed-order sum of the partial gradients of split rows (or sources), for
+// one or two gradient tensors sharing the split list.
 struct SumMergeArgs {
     const sgat_split* splits;
     int HD;
-    const float* part;
-    float scale;
-    void* out;
+    const float* part[2];
+    float scale[2];
+    void* out[2];
+    int n_out;
 };
 
 template <int DT>
 __global__ __launch_bounds__(kBlock) void sum_merge(SumMergeArgs a)
 {
+    __shared__ float red[kBlock];
     const sgat_split sp = a.splits[blockIdx.x];
-    for (int e = threadIdx.x; e < a.HD; e += blockDim.x) {
+    int eb, grp, e;
+    merge_geometry(a.HD, eb, grp, e);
+    const int G = kBlock / eb;
+    const bool live = e < a.HD && grp < G;
+    for (int o = 0; o < a.n_out; ++o) {
         float s = 0.f;
-        for (int k = 0; k < sp.nslots; ++k)
-            s += a.part[static_cast<int64_t>(sp.first_slot + k) * a.HD + e];
-        s *= a.scale;
-        const int64_t oi = static_cast<int64_t>(sp.row) * a.HD + e;
-        if constexpr (DT == SGAT_F32) static_cast<float*>(a.out)[oi] = s;
-        else static_cast<__bf16*>(a.out)[oi] = static_cast<__bf16>(s);
+        if (live) {
+            const float* p = a.part[o] + static_cast<int64_t>(sp.first_slot) * a.HD + e;
+            int k = grp;
+            for (; k + 7 * G < sp.nslots; k += 8 * G) {
+                float x[8];
+#pragma unroll
+                for (int u = 0; u < 8; ++u) x[u] = p[static_cast<int64_t>(k + u * G) * a.HD];
+#pragma unroll
+                for (int u = 0; u < 8; ++u) s += x[u];
+            }
+            for (; k < sp.nslots; k += G) s += p[static_cast<int64_t>(k) * a.HD];
+        }
+        red[threadIdx.x] = s;
+        __syncthreads();
+        if (live && grp == 0) {
+            float t = 0.f;
+            for (int q = 0; q < G; ++q) t += red[q * eb + threadIdx.x];
+            t *= a.scale[o];
+            const int64_t oi = static_cast<int64_t>(sp.row) * a.HD + e;
+            if constexpr (DT == SGAT_F32) static_cast<float*>(a.out[o])[oi] = t;
+            else static_cast<__bf16*>(a.out[o])[oi] = static_cast<__bf16>(t);
+        }
+        __syncthreads();
     }
 }
 

@@ -61,6 +61,12 @@ int launch_gt_bs_bwd(const Plan& p, int H, int D, const void* Q, const void* K, 
 // da = 0 (the empty sum, for a graph without nodes), by a kernel.
 int launch_da_zero(float* da, int HD, hipStream_t s);
 
+// Fixed-order sum of split-row partial gradients into one or two outputs
+// (part1 == nullptr: one), scaled, in the output dtype.
+int merge_sum(const char* name, const std::vector<sgat_split>& sp, const sgat_split* dsp, int HD,
+              const float* part0, float scale0, void* out0, const float* part1, float scale1,
+              void* out1, int dt, hipStream_t s);
+
 // Launch one kernel through hipLaunchKernel, bracketed by trace events when
 // tracing is on. Returns SGAT_OK or SGAT_HIP_ERROR.
 int launch(const char* name, const void* fn, dim3 grid, dim3 block, void* arg, hipStream_t s);

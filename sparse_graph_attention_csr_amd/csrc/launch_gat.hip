@@ -7,22 +7,44 @@
 
 namespace sgat {
 
+// Neighbour rows each wave gathers before their first use (compile-time
+// tunables; -DSGAT_UNROLL_FWD=... etc. override them).
+#ifndef SGAT_UNROLL_FWD
+#define SGAT_UNROLL_FWD 8
+#endif
+#ifndef SGAT_UNROLL_BWD
+#define SGAT_UNROLL_BWD 4
+#endif
+#ifndef SGAT_UNROLL_ROWS
+#define SGAT_UNROLL_ROWS 8
+#endif
+
 namespace {
-constexpr int kUnrollFwd = 8;
-constexpr int kUnrollBwd = 4;
+// With several edges per wave side by side, each unrolled step already holds
+// EPW neighbour rows, so fewer steps keep the same bytes in flight with fewer
+// registers.
+constexpr int unroll_fwd(int epw) { return epw >= 4 ? (SGAT_UNROLL_FWD + 3) / 4 : SGAT_UNROLL_FWD; }
+constexpr int unroll_bwd(int epw) { return epw >= 4 ? (SGAT_UNROLL_BWD + 1) / 2 : SGAT_UNROLL_BWD; }
 constexpr int kGatBwdMaxBlocks = 2048;
 }
 
-// Fixed-order sum of the per-workgroup da partials.
+// Fixed-order sum of the per-workgroup da partials: one workgroup per element
+// of da; thread t sums partials t, t+256, ... in order, then a fixed LDS tree
+// combines the 256 thread sums. The result does not depend on timing.
 __global__ __launch_bounds__(kBlock) void da_reduce(DaReduceArgs a)
 {
-    for (int e = blockIdx.x * blockDim.x + threadIdx.x; e < a.HD; e += gridDim.x * blockDim.x) {
-        float s = 0.f;
-        for (int b = 0; b < a.G; ++b) s += a.da_part[static_cast<int64_t>(b) * a.HD + e];
-        a.da[e] = s;
+    __shared__ float red[kBlock];
+    const int e = blockIdx.x;
+    float s = 0.f;
+    for (int b = threadIdx.x; b < a.G; b += kBlock) s += a.da_part[static_cast<int64_t>(b) * a.HD + e];
+    red[threadIdx.x] = s;
+    __syncthreads();
+    for (int w = kBlock / 2; w > 0; w >>= 1) {
+        if (static_cast<int>(threadIdx.x) < w) red[threadIdx.x] += red[threadIdx.x + w];
+        __syncthreads();
     }
+    if (threadIdx.x == 0) a.da[e] = red[0];
 }
-
 
 int gat_bwd_row_blocks(const Plan& p)
 {
@@ -34,7 +56,7 @@ int launch_da_zero(float* da, int HD, hipStream_t s)
 {
     DaReduceArgs d{nullptr, 0, HD, da};
     return launch("gat_bwd_da_reduce", reinterpret_cast<const void*>(&da_reduce),
-                  dim3(static_cast<unsigned>((HD + kBlock - 1) / kBlock)), dim3(kBlock), &d, s);
+                  dim3(static_cast<unsigned>(HD)), dim3(kBlock), &d, s);
 }
 
 int launch_gat_fwd(const Plan& p, int H, int D, int dt, const int32_t* colidx, const void* Xs,
@@ -57,7 +79,7 @@ int launch_gat_fwd(const Plan& p, int H, int D, int dt, const int32_t* colidx, c
     a.part_ml = ws.part_ml;
     const void* fn = nullptr;
 #define X(DT_, D_, E_) \
-    if (dt == DT_ && D == D_ && dc.epw == E_) fn = reinterpret_cast<const void*>(&gat_fwd_rows<DT_, D_, E_, kUnrollFwd>);
+    if (dt == DT_ && D == D_ && dc.epw == E_) fn = reinterpret_cast<const void*>(&gat_fwd_rows<DT_, D_, E_, unroll_fwd(E_)>);
     SGAT_GATHER_CONFIGS(X)
 #undef X
     if (!fn) return SGAT_INVALID_ARGUMENT;
@@ -71,7 +93,9 @@ int launch_gat_fwd(const Plan& p, int H, int D, int dt, const int32_t* colidx, c
                        out, lse};
         const void* mf = dt == SGAT_F32 ? reinterpret_cast<const void*>(&lse_merge<SGAT_F32>)
                                         : reinterpret_cast<const void*>(&lse_merge<SGAT_BF16>);
-        int rc = launch("gat_fwd_merge", mf, dim3(static_cast<unsigned>(p.row_splits.size())),
+        int rc = launch("gat_fwd_merge", mf,
+                        dim3(static_cast<unsigned>(p.row_splits.size()),
+                             static_cast<unsigned>((H * D + kBlock - 1) / kBlock)),
                         dim3(kBlock), &m, s);
         if (rc) return rc;
     }
@@ -117,40 +141,30 @@ int launch_gat_bwd(const Plan& p, int H, int D, int dt, const int32_t* colidx, c
     const void *fr = nullptr, *fc = nullptr;
 #define X(DT_, D_, E_)                                                                 \
     if (dt == DT_ && D == D_ && dc.epw == E_) {                                        \
-        fr = reinterpret_cast<const void*>(&gat_bwd_rows<DT_, D_, E_, kUnrollBwd>);    \
-        fc = reinterpret_cast<const void*>(&gat_bwd_cols<DT_, D_, E_, kUnrollBwd>);    \
+        fr = reinterpret_cast<const void*>(&gat_bwd_rows<DT_, D_, E_, unroll_bwd(E_)>);    \
+        fc = reinterpret_cast<const void*>(&gat_bwd_cols<DT_, D_, E_, unroll_bwd(E_)>);    \
     }
     SGAT_GATHER_CONFIGS(X)
 #undef X
     if (!fr || !fc) return SGAT_INVALID_ARGUMENT;
-    const void* msum = dt == SGAT_F32 ? reinterpret_cast<const void*>(&sum_merge<SGAT_F32>)
-                                      : reinterpret_cast<const void*>(&sum_merge<SGAT_BF16>);
     int rc;
     // the row pass always runs: it writes the da partials of every workgroup
     if ((rc = launch("gat_bwd_rows", fr, dim3(static_cast<unsigned>(gx), static_cast<unsigned>(dc.n_hg)),
                      dim3(kBlock), &r, s)))
         return rc;
-    if (!p.row_splits.empty()) {
-        SumMergeArgs m{p.dptr<sgat_split>(SGAT_ARR_ROW_SPLITS), HD, ws.part_row, 1.f, dXs};
-        if ((rc = launch("gat_bwd_rows_merge", msum, dim3(static_cast<unsigned>(p.row_splits.size())),
-                         dim3(kBlock), &m, s)))
-            return rc;
-    }
+    if ((rc = merge_sum("gat_bwd_rows_merge", p.row_splits, p.dptr<sgat_split>(SGAT_ARR_ROW_SPLITS),
+                        HD, ws.part_row, 1.f, dXs, nullptr, 0.f, nullptr, dt, s)))
+        return rc;
     DaReduceArgs d{ws.da_part, gx, HD, da};
     if ((rc = launch("gat_bwd_da_reduce", reinterpret_cast<const void*>(&da_reduce),
-                     dim3(static_cast<unsigned>((HD + kBlock - 1) / kBlock)), dim3(kBlock), &d, s)))
+                     dim3(static_cast<unsigned>(HD)), dim3(kBlock), &d, s)))
         return rc;
     if (c.n_units > 0 &&
         (rc = launch("gat_bwd_cols", fc, dim3(static_cast<unsigned>(wave_grid(c.n_units))),
                      dim3(kBlock), &c, s)))
         return rc;
-    if (!p.col_splits.empty()) {
-        SumMergeArgs m{p.dptr<sgat_split>(SGAT_ARR_COL_SPLITS), HD, ws.part_col0, 1.f, dXt};
-        if ((rc = launch("gat_bwd_cols_merge", msum, dim3(static_cast<unsigned>(p.col_splits.size())),
-                         dim3(kBlock), &m, s)))
-            return rc;
-    }
-    return SGAT_OK;
+    return merge_sum("gat_bwd_cols_merge", p.col_splits, p.dptr<sgat_split>(SGAT_ARR_COL_SPLITS),
+                     HD, ws.part_col0, 1.f, dXt, nullptr, 0.f, nullptr, dt, s);
 }
 
 }  // namespace sgat

@@ -5,9 +5,25 @@
 
 namespace sgat {
 
+// Neighbour rows each wave gathers before their first use (compile-time
+// tunables; -DSGAT_UNROLL_FWD=... etc. override them).
+#ifndef SGAT_UNROLL_FWD
+#define SGAT_UNROLL_FWD 8
+#endif
+#ifndef SGAT_UNROLL_BWD
+#define SGAT_UNROLL_BWD 4
+#endif
+#ifndef SGAT_UNROLL_ROWS
+#define SGAT_UNROLL_ROWS 8
+#endif
+
 namespace {
-constexpr int kUnrollFwd = 8;
-constexpr int kUnrollBwd = 4;
+// With several edges per wave side by side, each unrolled step already holds
+// EPW neighbour rows, so fewer steps keep the same bytes in flight with fewer
+// registers.
+constexpr int unroll_fwd(int epw) { return epw >= 4 ? (SGAT_UNROLL_FWD + 3) / 4 : SGAT_UNROLL_FWD; }
+constexpr int unroll_bwd(int epw) { return epw >= 4 ? (SGAT_UNROLL_BWD + 1) / 2 : SGAT_UNROLL_BWD; }
+constexpr int unroll_rows(int epw) { return epw >= 4 ? (SGAT_UNROLL_ROWS + 1) / 2 : SGAT_UNROLL_ROWS; }
 }
 
 int launch_gt_fwd(const Plan& p, int H, int D, int dt, const int32_t* colidx, const void* Q,
@@ -29,7 +45,7 @@ int launch_gt_fwd(const Plan& p, int H, int D, int dt, const int32_t* colidx, co
     a.scale2 = kLog2e / sqrtf(static_cast<float>(D));
     const void* fn = nullptr;
 #define X(DT_, D_, E_) \
-    if (dt == DT_ && D == D_ && dc.epw == E_) fn = reinterpret_cast<const void*>(&gt_fwd_rows<DT_, D_, E_, kUnrollFwd>);
+    if (dt == DT_ && D == D_ && dc.epw == E_) fn = reinterpret_cast<const void*>(&gt_fwd_rows<DT_, D_, E_, unroll_fwd(E_)>);
     SGAT_GATHER_CONFIGS(X)
 #undef X
     if (!fn) return SGAT_INVALID_ARGUMENT;
@@ -43,21 +59,31 @@ int launch_gt_fwd(const Plan& p, int H, int D, int dt, const int32_t* colidx, co
                        out, lse};
         const void* mf = dt == SGAT_F32 ? reinterpret_cast<const void*>(&lse_merge<SGAT_F32>)
                                         : reinterpret_cast<const void*>(&lse_merge<SGAT_BF16>);
-        int rc = launch("gt_fwd_merge", mf, dim3(static_cast<unsigned>(p.row_splits.size())),
+        int rc = launch("gt_fwd_merge", mf,
+                        dim3(static_cast<unsigned>(p.row_splits.size()),
+                             static_cast<unsigned>((H * D + kBlock - 1) / kBlock)),
                         dim3(kBlock), &m, s);
         if (rc) return rc;
     }
     return SGAT_OK;
 }
 
-static int merge_sum(const char* name, const std::vector<sgat_split>& sp, const sgat_split* dsp,
-                     int HD, const float* part, float scale, void* out, int dt, hipStream_t s)
+int merge_sum(const char* name, const std::vector<sgat_split>& sp, const sgat_split* dsp, int HD,
+              const float* part0, float scale0, void* out0, const float* part1, float scale1,
+              void* out1, int dt, hipStream_t s)
 {
     if (sp.empty()) return SGAT_OK;
-    SumMergeArgs m{dsp, HD, part, scale, out};
+    SumMergeArgs m;
+    m.splits = dsp;
+    m.HD = HD;
+    m.part[0] = part0; m.scale[0] = scale0; m.out[0] = out0;
+    m.part[1] = part1; m.scale[1] = scale1; m.out[1] = out1;
+    m.n_out = part1 ? 2 : 1;
     const void* mf = dt == SGAT_F32 ? reinterpret_cast<const void*>(&sum_merge<SGAT_F32>)
                                     : reinterpret_cast<const void*>(&sum_merge<SGAT_BF16>);
-    return launch(name, mf, dim3(static_cast<unsigned>(sp.size())), dim3(kBlock), &m, s);
+    return launch(name, mf,
+                  dim3(static_cast<unsigned>(sp.size()), static_cast<unsigned>((HD + kBlock - 1) / kBlock)),
+                  dim3(kBlock), &m, s);
 }
 
 int launch_gt_bwd(const Plan& p, int H, int D, int dt, const int32_t* colidx, const void* Q,
@@ -110,8 +136,8 @@ int launch_gt_bwd(const Plan& p, int H, int D, int dt, const int32_t* colidx, co
 #define X(DT_, D_, E_)                                                                 \
     if (dt == DT_ && D == D_ && dc.epw == E_) {                                        \
         fd = reinterpret_cast<const void*>(&bwd_delta<DT_, D_, E_>);                   \
-        fr = reinterpret_cast<const void*>(&gt_bwd_rows<DT_, D_, E_, kUnrollFwd>);     \
-        fc = reinterpret_cast<const void*>(&gt_bwd_cols<DT_, D_, E_, kUnrollBwd>);     \
+        fr = reinterpret_cast<const void*>(&gt_bwd_rows<DT_, D_, E_, unroll_rows(E_)>);     \
+        fc = reinterpret_cast<const void*>(&gt_bwd_cols<DT_, D_, E_, unroll_bwd(E_)>);     \
     }
     SGAT_GATHER_CONFIGS(X)
 #undef X
@@ -124,18 +150,15 @@ int launch_gt_bwd(const Plan& p, int H, int D, int dt, const int32_t* colidx, co
         (rc = launch("gt_bwd_cols", fc, dim3(static_cast<unsigned>(wave_grid(c.n_units))),
                      dim3(kBlock), &c, s)))
         return rc;
-    const sgat_split* csp = p.dptr<sgat_split>(SGAT_ARR_COL_SPLITS);
-    if ((rc = merge_sum("gt_bwd_cols_merge", p.col_splits, csp, HD, ws.part_col0, oscale, dK, dt,
-                        s)))
-        return rc;
-    if ((rc = merge_sum("gt_bwd_cols_merge", p.col_splits, csp, HD, ws.part_col1, 1.f, dV, dt, s)))
+    if ((rc = merge_sum("gt_bwd_cols_merge", p.col_splits, p.dptr<sgat_split>(SGAT_ARR_COL_SPLITS),
+                        HD, ws.part_col0, oscale, dK, ws.part_col1, 1.f, dV, dt, s)))
         return rc;
     if (r.n_units > 0 &&
         (rc = launch("gt_bwd_rows", fr, dim3(static_cast<unsigned>(wave_grid(r.n_units))),
                      dim3(kBlock), &r, s)))
         return rc;
     return merge_sum("gt_bwd_rows_merge", p.row_splits, p.dptr<sgat_split>(SGAT_ARR_ROW_SPLITS),
-                     HD, ws.part_row, oscale, dQ, dt, s);
+                     HD, ws.part_row, oscale, dQ, nullptr, 0.f, nullptr, dt, s);
 }
 
 }  // namespace sgat
