@@ -17,6 +17,10 @@
 // through a per-wave LDS tile. Edges outside dense tiles (the residual CSR)
 // are packed 16 at a time into gathered "pseudo-tiles" whose column c is one
 // residual edge, so they go through the same softmax.
+//
+// Every kernel walks its tiles software-pipelined: the loads of tile k+1 are
+// issued before tile k is computed, so each wave keeps one tile of gathers in
+// flight while its matrix and softmax work runs.
 #pragma once
 
 #include "gather.hpp"
@@ -55,137 +59,226 @@ struct BsFwdArgs {
 };
 
 template <int D>
-struct TileFwd {
-    static constexpr int KS = D / 32;     // k-steps of the score product
+struct Shape {
+    static constexpr int KS = D / 32;     // k-steps of a 16x16xD score product
     static constexpr int NB = D / 16;     // 16-channel output blocks
-    static constexpr int SPL = D / 32;    // 16-byte V segments per lane
+    static constexpr int SPL = D / 32;    // 16-byte segments of a 16-row tile per lane
     static constexpr int LDW = D + 16;    // LDS row stride (elements): 4 rows hit distinct banks
+};
 
-    // One tile of 16 columns for one head. `base` is the element offset of the
-    // (node, head) row of column l%16; `valid` holds the edge bits of this
-    // lane's entries (row l%16, columns 4g..4g+3).
-    static __device__ __forceinline__ void step(int64_t base, uint32_t valid,
-                                                const bf16x8_t (&qf)[KS], float& m, float& lsum,
-                                                f32x4_t (&acc)[NB], const void* K, const void* V,
-                                                uint16_t* vs, float scale2, int i, int g)
+// Start offsets of rows 1..15 of a 16-row (or 16-source) block in a pointer
+// array, loaded once per block (rows past the end start at ptr[hi]).
+struct BlockStarts {
+    int64_t v[kTileDim];
+    __device__ __forceinline__ void load(const int64_t* ptr, int64_t lo, int64_t hi)
     {
-        Frag kf[KS];
-        uint4 vr[SPL];
 #pragma unroll
-        for (int s = 0; s < KS; ++s) kf[s] = ldg<SGAT_BF16>(K, base + 32 * s + 8 * g);
+        for (int q = 1; q < kTileDim; ++q) v[q] = ptr[lo + q < hi ? lo + q : hi];
+    }
+    // position of edge e among the block's rows
+    __device__ __forceinline__ int row_of(int64_t e) const
+    {
+        int r = 0;
 #pragma unroll
-        for (int q = 0; q < SPL; ++q)
-            vr[q] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(V) + base +
-                                                    8 * (g + 4 * q));
-        f32x4_t st = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int s = 0; s < KS; ++s)
-            st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kf[s]),
-                                                         qf[s], st, 0, 0, 0);
-#pragma unroll
-        for (int q = 0; q < SPL; ++q)
-            *reinterpret_cast<uint4*>(vs + i * LDW + 8 * (g + 4 * q)) = vr[q];
+        for (int q = 1; q < kTileDim; ++q) r += v[q] <= e ? 1 : 0;
+        return r;
+    }
+};
 
-        float sv[4];
-        float rmax = kNegInf;
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            sv[k] = ((valid >> k) & 1u) ? st[k] * scale2 : kNegInf;
-            rmax = fmaxf(rmax, sv[k]);
+// Tiles of one 16-row block, in order: its dense tiles, then its residual
+// edges in pseudo-tiles of 16. Tile k is described by a RowRef: the node of
+// column l%16 and this lane's 4 edge bits (row l%16, columns 4g..4g+3).
+// fetch() issues the raw loads of a description, decode() builds it; k is
+// uniform across the wave.
+struct RowRef {
+    int64_t src;
+    uint32_t valid;
+};
+
+struct RowTiles {
+    int64_t n, tb, nd, rb, re;
+    const int32_t* tile_col;
+    const uint16_t* tile_mask;
+    const int32_t* res_colidx;
+    BlockStarts starts;
+
+    __device__ __forceinline__ int64_t count() const { return nd + (re - rb + 15) / 16; }
+
+    __device__ __forceinline__ void fetch(int64_t k, int i, int32_t& col, uint32_t& word) const
+    {
+        if (k < nd) {
+            const int64_t t = tb + k;
+            col = tile_col[t];
+            word = tile_mask[t * kTileDim + i];
+        } else {
+            const int64_t e = rb + (k - nd) * 16 + i;
+            col = e < re ? res_colidx[e] : 0;
+            word = 0;
         }
-        rmax = fmaxf(rmax, __shfl_xor(rmax, 16));
-        rmax = fmaxf(rmax, __shfl_xor(rmax, 32));
-        const float mn = fmaxf(m, rmax);
-        const float corr = mn == kNegInf ? 1.f : fast_exp2(m - mn);
-        float p[4], ps = 0.f;
+    }
+
+    __device__ __forceinline__ RowRef decode(int64_t k, int i, int g, int32_t col, uint32_t word) const
+    {
+        RowRef r;
+        if (k < nd) {
+            r.src = min(static_cast<int64_t>(col) * kTileDim + i, n - 1);
+            r.valid = (word >> (4 * g)) & 0xFu;
+        } else {
+            const int64_t e = rb + (k - nd) * 16 + i;   // column i is residual edge e
+            const int rr = e < re ? starts.row_of(e) : -1;
+            r.src = col;
+            r.valid = 0;
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            p[k] = ((valid >> k) & 1u) ? fast_exp2(sv[k] - mn) : 0.f;
-            ps += p[k];
+            for (int q = 0; q < 4; ++q) r.valid |= (__shfl(rr, 4 * g + q) == i ? 1u : 0u) << q;
         }
-        ps += __shfl_xor(ps, 16);
-        ps += __shfl_xor(ps, 32);
-        lsum = lsum * corr + ps;
-        m = mn;
-        const s16x4_t pb = {bf16_bits(p[0]), bf16_bits(p[1]), bf16_bits(p[2]), bf16_bits(p[3])};
-        __builtin_amdgcn_wave_barrier();
-#pragma unroll
-        for (int s = 0; s < NB; ++s) {
-            s16x4_t va;
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk)
-                va[kk] = static_cast<short>(vs[(4 * g + kk) * LDW + 16 * s + i]);
-            acc[s] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pb, acc[s] * corr, 0, 0, 0);
-        }
-        __builtin_amdgcn_wave_barrier();
+        return r;
     }
 };
 
 template <int D>
+struct FwdTile {
+    Frag kf[Shape<D>::KS];
+    uint4 vr[Shape<D>::SPL];
+    __device__ __forceinline__ void load(const void* K, const void* V, int64_t base, int g)
+    {
+#pragma unroll
+        for (int s = 0; s < Shape<D>::KS; ++s) kf[s] = ldg<SGAT_BF16>(K, base + 32 * s + 8 * g);
+#pragma unroll
+        for (int q = 0; q < Shape<D>::SPL; ++q)
+            vr[q] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(V) + base +
+                                                    8 * (g + 4 * q));
+    }
+};
+
+// One forward tile for one head: masked online-softmax update of (m, lsum)
+// and O^T += V^T P^T.
+template <int D>
+__device__ __forceinline__ void fwd_compute(const FwdTile<D>& tl, uint32_t valid,
+                                            const bf16x8_t (&qf)[Shape<D>::KS], float& m,
+                                            float& lsum, f32x4_t (&acc)[Shape<D>::NB],
+                                            uint16_t* vs, float scale2, int i, int g)
+{
+    using S = Shape<D>;
+    f32x4_t st = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < S::KS; ++s)
+        st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, tl.kf[s]), qf[s],
+                                                     st, 0, 0, 0);
+#pragma unroll
+    for (int q = 0; q < S::SPL; ++q)
+        *reinterpret_cast<uint4*>(vs + i * S::LDW + 8 * (g + 4 * q)) = tl.vr[q];
+
+    float sv[4];
+    float rmax = kNegInf;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        sv[k] = ((valid >> k) & 1u) ? st[k] * scale2 : kNegInf;
+        rmax = fmaxf(rmax, sv[k]);
+    }
+    rmax = fmaxf(rmax, __shfl_xor(rmax, 16));
+    rmax = fmaxf(rmax, __shfl_xor(rmax, 32));
+    const float mn = fmaxf(m, rmax);
+    const float corr = mn == kNegInf ? 1.f : fast_exp2(m - mn);
+    float p[4], ps = 0.f;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        p[k] = ((valid >> k) & 1u) ? fast_exp2(sv[k] - mn) : 0.f;
+        ps += p[k];
+    }
+    ps += __shfl_xor(ps, 16);
+    ps += __shfl_xor(ps, 32);
+    lsum = lsum * corr + ps;
+    m = mn;
+    const s16x4_t pb = {bf16_bits(p[0]), bf16_bits(p[1]), bf16_bits(p[2]), bf16_bits(p[3])};
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int s = 0; s < S::NB; ++s) {
+        s16x4_t va;
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk)
+            va[kk] = static_cast<short>(vs[(4 * g + kk) * S::LDW + 16 * s + i]);
+        acc[s] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pb, acc[s] * corr, 0, 0, 0);
+    }
+    __builtin_amdgcn_wave_barrier();
+}
+
+__device__ __forceinline__ void store_tile_rows(void* dst, int64_t off, const f32x4_t& v, float sc)
+{
+    uint2 w;
+    w.x = pack_bf16x2(v[0] * sc, v[1] * sc);
+    w.y = pack_bf16x2(v[2] * sc, v[3] * sc);
+    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(dst) + off) = w;
+}
+
+template <int D>
 __global__ __launch_bounds__(kBlock) void gt_bs_fwd(BsFwdArgs a)
 {
-    using T = TileFwd<D>;
-    __shared__ __attribute__((aligned(16))) uint16_t vs_all[kWavesPerBlock][16 * T::LDW];
+    using S = Shape<D>;
+    __shared__ __attribute__((aligned(16))) uint16_t vs_all[kWavesPerBlock][16 * S::LDW];
     const int64_t br = logical_block();
     if (br >= a.n_tile_rows) return;          // the whole workgroup leaves; no barrier follows
     const int w = wave_id();
     const int l = threadIdx.x & 63, i = l & 15, g = l >> 4;
     const int64_t HD = static_cast<int64_t>(a.H) * D;
+    RowTiles tiles;
     const int64_t r_lo = br * kTileDim;
     const int64_t r_hi = r_lo + kTileDim < a.n ? r_lo + kTileDim : a.n;
+    tiles.n = a.n;
+    tiles.tb = a.tile_rowptr[br];
+    tiles.nd = a.tile_rowptr[br + 1] - tiles.tb;
+    tiles.rb = a.res_rowptr[r_lo];
+    tiles.re = a.res_rowptr[r_hi];
+    tiles.tile_col = a.tile_col;
+    tiles.tile_mask = a.tile_mask;
+    tiles.res_colidx = a.res_colidx;
+    tiles.starts.load(a.res_rowptr, r_lo, r_hi);
+    const int64_t nt = tiles.count();
     const int64_t row = r_lo + i;
     const bool row_ok = row < a.n;
-    const int64_t tb = a.tile_rowptr[br], te = a.tile_rowptr[br + 1];
-    const int64_t rb = a.res_rowptr[r_lo], re = a.res_rowptr[r_hi];
     uint16_t* vs = vs_all[w];
 
     for (int h = w; h < a.H; h += kWavesPerBlock) {
         const int64_t hoff = static_cast<int64_t>(h) * D;
-        bf16x8_t qf[T::KS];
+        bf16x8_t qf[S::KS];
 #pragma unroll
-        for (int s = 0; s < T::KS; ++s) {
+        for (int s = 0; s < S::KS; ++s) {
             qf[s] = bf16x8_t{};
             if (row_ok) qf[s] = ld_bf16x8(a.Q, row * HD + hoff + 32 * s + 8 * g);
         }
         float m = kNegInf, lsum = 0.f;
-        f32x4_t acc[T::NB];
+        f32x4_t acc[S::NB];
 #pragma unroll
-        for (int s = 0; s < T::NB; ++s) acc[s] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        for (int s = 0; s < S::NB; ++s) acc[s] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-        for (int64_t t = tb; t < te; ++t) {
-            const int64_t src = min(static_cast<int64_t>(a.tile_col[t]) * kTileDim + i, a.n - 1);
-            const uint32_t valid = (static_cast<uint32_t>(a.tile_mask[t * kTileDim + i]) >> (4 * g)) & 0xFu;
-            T::step(src * HD + hoff, valid, qf, m, lsum, acc, a.K, a.V, vs, a.scale2, i, g);
+        // pipeline: descriptions two tiles ahead, data one tile ahead
+        FwdTile<D> next;
+        RowRef rnext{0, 0};
+        int32_t col2 = 0;
+        uint32_t word2 = 0;
+        if (nt > 0) {
+            int32_t c0;
+            uint32_t w0;
+            tiles.fetch(0, i, c0, w0);
+            rnext = tiles.decode(0, i, g, c0, w0);
+            next.load(a.K, a.V, rnext.src * HD + hoff, g);
         }
-        for (int64_t e0 = rb; e0 < re; e0 += 16) {
-            const int64_t e = e0 + i;       // column i of this pseudo-tile is residual edge e
-            int rr = -1;
-            int64_t src = 0;
-            if (e < re) {
-                src = a.res_colidx[e];
-                rr = 0;
-                for (int r = 1; r < kTileDim; ++r) {
-                    const int64_t q = r_lo + r < r_hi ? r_lo + r : r_hi;
-                    rr += a.res_rowptr[q] <= e ? 1 : 0;
-                }
+        if (nt > 1) tiles.fetch(1, i, col2, word2);
+        for (int64_t k = 0; k < nt; ++k) {
+            const FwdTile<D> cur = next;
+            const uint32_t valid = rnext.valid;
+            if (k + 1 < nt) {
+                rnext = tiles.decode(k + 1, i, g, col2, word2);
+                if (k + 2 < nt) tiles.fetch(k + 2, i, col2, word2);
+                next.load(a.K, a.V, rnext.src * HD + hoff, g);
             }
-            uint32_t valid = 0;
-#pragma unroll
-            for (int k = 0; k < 4; ++k)
-                valid |= (__shfl(rr, 4 * g + k) == i ? 1u : 0u) << k;
-            T::step(src * HD + hoff, valid, qf, m, lsum, acc, a.K, a.V, vs, a.scale2, i, g);
+            fwd_compute<D>(cur, valid, qf, m, lsum, acc, vs, a.scale2, i, g);
         }
 
         if (row_ok) {
             const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
 #pragma unroll
-            for (int s = 0; s < T::NB; ++s) {
-                uint2 v;
-                v.x = pack_bf16x2(acc[s][0] * inv, acc[s][1] * inv);
-                v.y = pack_bf16x2(acc[s][2] * inv, acc[s][3] * inv);
-                *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + row * HD + hoff + 16 * s +
-                                          4 * g) = v;
-            }
+            for (int s = 0; s < S::NB; ++s)
+                store_tile_rows(a.out, row * HD + hoff + 16 * s + 4 * g, acc[s], inv);
             if (g == 0)
                 a.lse[row * a.H + h] = lsum > 0.f ? (m + __log2f(lsum)) * kLn2 : kNegInf;
         }
@@ -218,153 +311,91 @@ struct BsBwdArgs {
 };
 
 template <int D>
-struct TileBwd {
-    static constexpr int KS = D / 32;
-    static constexpr int NB = D / 16;
-    static constexpr int LDW = D + 16;
-
-    // Tile-row step: rows i = l%16 of the block, columns c = 4g..4g+3 in this
-    // lane. `base` = element offset of (source of column l%16, head).
-    static __device__ __forceinline__ void row_step(int64_t base, uint32_t valid,
-                                                    const bf16x8_t (&qf)[KS],
-                                                    const bf16x8_t (&df)[KS], float lse2,
-                                                    float delta, f32x4_t (&acc)[NB],
-                                                    const void* K, const void* V, uint16_t* ks,
-                                                    float scale2, int i, int g)
+struct RowBwdTile {
+    Frag kf[Shape<D>::KS], vf[Shape<D>::KS];
+    __device__ __forceinline__ void load(const void* K, const void* V, int64_t base, int g)
     {
-        Frag kf[KS], vf[KS];
 #pragma unroll
-        for (int s = 0; s < KS; ++s) {
+        for (int s = 0; s < Shape<D>::KS; ++s) {
             kf[s] = ldg<SGAT_BF16>(K, base + 32 * s + 8 * g);
             vf[s] = ldg<SGAT_BF16>(V, base + 32 * s + 8 * g);
         }
-        f32x4_t st = {0.f, 0.f, 0.f, 0.f}, dp = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int s = 0; s < KS; ++s) {
-            st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kf[s]), qf[s],
-                                                         st, 0, 0, 0);
-            dp = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, vf[s]), df[s],
-                                                         dp, 0, 0, 0);
-        }
-#pragma unroll
-        for (int s = 0; s < KS; ++s)
-            *reinterpret_cast<Frag*>(ks + i * LDW + 32 * s + 8 * g) = kf[s];
-        short dsb[4];
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const float p = ((valid >> k) & 1u) ? fast_exp2(st[k] * scale2 - lse2) : 0.f;
-            dsb[k] = bf16_bits(p * (dp[k] - delta));
-        }
-        const s16x4_t b = {dsb[0], dsb[1], dsb[2], dsb[3]};
-        __builtin_amdgcn_wave_barrier();
-#pragma unroll
-        for (int s = 0; s < NB; ++s) {
-            s16x4_t ka;
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk)
-                ka[kk] = static_cast<short>(ks[(4 * g + kk) * LDW + 16 * s + i]);
-            acc[s] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ka, b, acc[s], 0, 0, 0);
-        }
-        __builtin_amdgcn_wave_barrier();
-    }
-
-    // Tile-column step: columns c = l%16 (sources of the block), rows
-    // 4g..4g+3 of the tile in this lane. `qbase` = element offset of (the
-    // destination of tile row l%16, head); st[k] = statistics of row 4g+k.
-    static __device__ __forceinline__ void col_step(int64_t qbase, const RowStat (&st)[4],
-                                                    uint32_t valid, const bf16x8_t (&kf)[KS],
-                                                    const bf16x8_t (&vf)[KS], f32x4_t (&dk)[NB],
-                                                    f32x4_t (&dv)[NB], const void* Q,
-                                                    const void* dO, uint16_t* qs, uint16_t* os,
-                                                    float scale2, int c, int g)
-    {
-        Frag qa[KS], oa[KS];
-#pragma unroll
-        for (int s = 0; s < KS; ++s) {
-            qa[s] = ldg<SGAT_BF16>(Q, qbase + 32 * s + 8 * g);
-            oa[s] = ldg<SGAT_BF16>(dO, qbase + 32 * s + 8 * g);
-        }
-        f32x4_t sc = {0.f, 0.f, 0.f, 0.f}, dp = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int s = 0; s < KS; ++s) {
-            sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, qa[s]), kf[s],
-                                                         sc, 0, 0, 0);
-            dp = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, oa[s]), vf[s],
-                                                         dp, 0, 0, 0);
-        }
-#pragma unroll
-        for (int s = 0; s < KS; ++s) {
-            *reinterpret_cast<Frag*>(qs + c * LDW + 32 * s + 8 * g) = qa[s];
-            *reinterpret_cast<Frag*>(os + c * LDW + 32 * s + 8 * g) = oa[s];
-        }
-        short pb[4], db[4];
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const float p = ((valid >> k) & 1u) ? fast_exp2(sc[k] * scale2 - st[k].lse2) : 0.f;
-            pb[k] = bf16_bits(p);
-            db[k] = bf16_bits(p * (dp[k] - st[k].delta));
-        }
-        const s16x4_t P = {pb[0], pb[1], pb[2], pb[3]};
-        const s16x4_t S = {db[0], db[1], db[2], db[3]};
-        __builtin_amdgcn_wave_barrier();
-#pragma unroll
-        for (int s = 0; s < NB; ++s) {
-            s16x4_t qt, ot;
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk) {
-                qt[kk] = static_cast<short>(qs[(4 * g + kk) * LDW + 16 * s + c]);
-                ot[kk] = static_cast<short>(os[(4 * g + kk) * LDW + 16 * s + c]);
-            }
-            dk[s] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(qt, S, dk[s], 0, 0, 0);
-            dv[s] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ot, P, dv[s], 0, 0, 0);
-        }
-        __builtin_amdgcn_wave_barrier();
     }
 };
 
-__device__ __forceinline__ void store_tile_rows(void* dst, int64_t off, const f32x4_t& v, float sc)
+// Tile-row step: rows i = l%16, columns 4g..4g+3 in this lane;
+// dS = P (dP - Delta_i) and dQ^T += K^T dS^T (K transposed through LDS).
+template <int D>
+__device__ __forceinline__ void row_bwd_compute(const RowBwdTile<D>& tl, uint32_t valid,
+                                                const bf16x8_t (&qf)[Shape<D>::KS],
+                                                const bf16x8_t (&df)[Shape<D>::KS], float lse2,
+                                                float delta, f32x4_t (&acc)[Shape<D>::NB],
+                                                uint16_t* ks, float scale2, int i, int g)
 {
-    uint2 w;
-    w.x = pack_bf16x2(v[0] * sc, v[1] * sc);
-    w.y = pack_bf16x2(v[2] * sc, v[3] * sc);
-    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(dst) + off) = w;
-}
-
-// Position of edge e among the 16 rows of a block, from the block's pointers.
-__device__ __forceinline__ int row_in_block(const int64_t* ptr, int64_t lo, int64_t hi, int64_t e)
-{
-    int r = 0;
-    for (int q = 1; q < kTileDim; ++q) {
-        const int64_t x = lo + q < hi ? lo + q : hi;
-        r += ptr[x] <= e ? 1 : 0;
+    using S = Shape<D>;
+    f32x4_t st = {0.f, 0.f, 0.f, 0.f}, dp = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < S::KS; ++s) {
+        st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, tl.kf[s]), qf[s],
+                                                     st, 0, 0, 0);
+        dp = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, tl.vf[s]), df[s],
+                                                     dp, 0, 0, 0);
     }
-    return r;
+#pragma unroll
+    for (int s = 0; s < S::KS; ++s)
+        *reinterpret_cast<Frag*>(ks + i * S::LDW + 32 * s + 8 * g) = tl.kf[s];
+    short dsb[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const float p = ((valid >> k) & 1u) ? fast_exp2(st[k] * scale2 - lse2) : 0.f;
+        dsb[k] = bf16_bits(p * (dp[k] - delta));
+    }
+    const s16x4_t b = {dsb[0], dsb[1], dsb[2], dsb[3]};
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int s = 0; s < S::NB; ++s) {
+        s16x4_t ka;
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk)
+            ka[kk] = static_cast<short>(ks[(4 * g + kk) * S::LDW + 16 * s + i]);
+        acc[s] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ka, b, acc[s], 0, 0, 0);
+    }
+    __builtin_amdgcn_wave_barrier();
 }
 
 template <int D>
 __global__ __launch_bounds__(kBlock) void gt_bs_bwd_rows(BsBwdArgs a)
 {
-    using T = TileBwd<D>;
-    __shared__ __attribute__((aligned(16))) uint16_t ks_all[kWavesPerBlock][16 * T::LDW];
+    using S = Shape<D>;
+    __shared__ __attribute__((aligned(16))) uint16_t ks_all[kWavesPerBlock][16 * S::LDW];
     const int64_t br = logical_block();
     if (br >= a.n_blocks) return;
     const int w = wave_id();
     const int l = threadIdx.x & 63, i = l & 15, g = l >> 4;
     const int64_t HD = static_cast<int64_t>(a.H) * D;
+    RowTiles tiles;
     const int64_t r_lo = br * kTileDim;
     const int64_t r_hi = r_lo + kTileDim < a.n ? r_lo + kTileDim : a.n;
+    tiles.n = a.n;
+    tiles.tb = a.tile_rowptr[br];
+    tiles.nd = a.tile_rowptr[br + 1] - tiles.tb;
+    tiles.rb = a.res_rowptr[r_lo];
+    tiles.re = a.res_rowptr[r_hi];
+    tiles.tile_col = a.tile_col;
+    tiles.tile_mask = a.tile_mask;
+    tiles.res_colidx = a.res_colidx;
+    tiles.starts.load(a.res_rowptr, r_lo, r_hi);
+    const int64_t nt = tiles.count();
     const int64_t row = r_lo + i;
     const bool row_ok = row < a.n;
-    const int64_t tb = a.tile_rowptr[br], te = a.tile_rowptr[br + 1];
-    const int64_t rb = a.res_rowptr[r_lo], re = a.res_rowptr[r_hi];
     uint16_t* ks = ks_all[w];
 
     for (int h = w; h < a.H; h += kWavesPerBlock) {
         const int64_t hoff = static_cast<int64_t>(h) * D;
-        bf16x8_t qf[T::KS], df[T::KS];
+        bf16x8_t qf[S::KS], df[S::KS];
         float dsum = 0.f, lse2 = 0.f;
 #pragma unroll
-        for (int s = 0; s < T::KS; ++s) {
+        for (int s = 0; s < S::KS; ++s) {
             qf[s] = bf16x8_t{};
             df[s] = bf16x8_t{};
             if (row_ok) {
@@ -379,61 +410,205 @@ __global__ __launch_bounds__(kBlock) void gt_bs_bwd_rows(BsBwdArgs a)
         dsum += __shfl_xor(dsum, 32);
         if (row_ok) lse2 = a.lse[row * a.H + h] * kLog2e;
         if (row_ok && g == 0) a.stats[row * a.H + h] = RowStat{lse2, dsum};
-        f32x4_t acc[T::NB];
+        f32x4_t acc[S::NB];
 #pragma unroll
-        for (int s = 0; s < T::NB; ++s) acc[s] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        for (int s = 0; s < S::NB; ++s) acc[s] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-        for (int64_t t = tb; t < te; ++t) {
-            const int64_t src = min(static_cast<int64_t>(a.tile_col[t]) * kTileDim + i, a.n - 1);
-            const uint32_t valid = (static_cast<uint32_t>(a.tile_mask[t * kTileDim + i]) >> (4 * g)) & 0xFu;
-            T::row_step(src * HD + hoff, valid, qf, df, lse2, dsum, acc, a.K, a.V, ks, a.scale2, i, g);
+        // pipeline: descriptions two tiles ahead, data one tile ahead
+        RowBwdTile<D> next;
+        RowRef rnext{0, 0};
+        int32_t col2 = 0;
+        uint32_t word2 = 0;
+        if (nt > 0) {
+            int32_t c0;
+            uint32_t w0;
+            tiles.fetch(0, i, c0, w0);
+            rnext = tiles.decode(0, i, g, c0, w0);
+            next.load(a.K, a.V, rnext.src * HD + hoff, g);
         }
-        for (int64_t e0 = rb; e0 < re; e0 += 16) {
-            const int64_t e = e0 + i;
-            int rr = -1;
-            int64_t src = 0;
-            if (e < re) {
-                src = a.res_colidx[e];
-                rr = row_in_block(a.res_rowptr, r_lo, r_hi, e);
+        if (nt > 1) tiles.fetch(1, i, col2, word2);
+        for (int64_t k = 0; k < nt; ++k) {
+            const RowBwdTile<D> cur = next;
+            const uint32_t valid = rnext.valid;
+            if (k + 1 < nt) {
+                rnext = tiles.decode(k + 1, i, g, col2, word2);
+                if (k + 2 < nt) tiles.fetch(k + 2, i, col2, word2);
+                next.load(a.K, a.V, rnext.src * HD + hoff, g);
             }
-            uint32_t valid = 0;
-#pragma unroll
-            for (int k = 0; k < 4; ++k) valid |= (__shfl(rr, 4 * g + k) == i ? 1u : 0u) << k;
-            T::row_step(src * HD + hoff, valid, qf, df, lse2, dsum, acc, a.K, a.V, ks, a.scale2, i, g);
+            row_bwd_compute<D>(cur, valid, qf, df, lse2, dsum, acc, ks, a.scale2, i, g);
         }
         if (row_ok) {
 #pragma unroll
-            for (int s = 0; s < T::NB; ++s)
+            for (int s = 0; s < S::NB; ++s)
                 store_tile_rows(a.dQ, row * HD + hoff + 16 * s + 4 * g, acc[s], a.oscale);
         }
     }
 }
 
+// Tiles of one 16-source block, in order: its dense tiles (by block row),
+// then its residual edges (by source) in pseudo-tiles of 16. The lane's A
+// operand row is tile row l%16; its four entries are rows 4g..4g+3 of
+// column l%16. fetch() issues the raw description loads of a tile (used two
+// tiles later), ColBwdTile::load() its data (used one tile later).
+struct ColTiles {
+    int64_t n, tcb, nd, rcb, rce;
+    int H, h;
+    const int32_t* tile_bycol;
+    const int32_t* tile_row;
+    const uint16_t* tile_mask;
+    const int32_t* res_rowidx;
+    const RowStat* stats;
+    BlockStarts starts;
+
+    __device__ __forceinline__ int64_t count() const { return nd + (rce - rcb + 15) / 16; }
+
+    // dense tile: t = tile id; residual pseudo-tile: dst = destination of row l%16
+    __device__ __forceinline__ void fetch(int64_t k, int c, int32_t& t, int32_t& dst) const
+    {
+        if (k < nd) {
+            t = tile_bycol[tcb + k];
+            dst = 0;
+        } else {
+            const int64_t e = rcb + (k - nd) * 16 + c;
+            t = 0;
+            dst = e < rce ? res_rowidx[e] : 0;
+        }
+    }
+};
+
+template <int D>
+struct ColBwdTile {
+    Frag qa[Shape<D>::KS], oa[Shape<D>::KS];
+    RowStat st[4];
+    uint32_t valid;
+
+    __device__ __forceinline__ void load(const ColTiles& T, int64_t k, int32_t t, int32_t dst,
+                                         const void* Q, const void* dO, int64_t HD, int64_t hoff,
+                                         int c, int g)
+    {
+        int64_t arow = 0;
+        valid = 0;
+        if (k < T.nd) {
+            const int64_t r0 = static_cast<int64_t>(T.tile_row[t]) * kTileDim;
+            arow = min(r0 + c, T.n - 1);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const uint32_t bit =
+                    (static_cast<uint32_t>(T.tile_mask[static_cast<int64_t>(t) * kTileDim + 4 * g + q]) >> c) & 1u;
+                valid |= bit << q;
+                st[q] = RowStat{0.f, 0.f};
+                if (bit) st[q] = T.stats[(r0 + 4 * g + q) * T.H + T.h];
+            }
+        } else {
+            const int64_t e = T.rcb + (k - T.nd) * 16 + c;   // row c of this pseudo-tile is edge e
+            const int cc = e < T.rce ? T.starts.row_of(e) : -1;
+            arow = dst;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int lq = 4 * g + q;
+                const bool bit = __shfl(cc, lq) == c;
+                const int64_t dr = __shfl(dst, lq);
+                valid |= (bit ? 1u : 0u) << q;
+                st[q] = RowStat{0.f, 0.f};
+                if (bit) st[q] = T.stats[dr * T.H + T.h];
+            }
+        }
+        const int64_t qbase = arow * HD + hoff;
+#pragma unroll
+        for (int s = 0; s < Shape<D>::KS; ++s) {
+            qa[s] = ldg<SGAT_BF16>(Q, qbase + 32 * s + 8 * g);
+            oa[s] = ldg<SGAT_BF16>(dO, qbase + 32 * s + 8 * g);
+        }
+    }
+};
+
+// Tile-column step: S = Q K^T and dP = dO V^T in the lane layout of rows
+// 4g..4g+3, column l%16; dK^T += Q^T dS, dV^T += dO^T P (Q and dO transposed
+// through LDS).
+template <int D>
+__device__ __forceinline__ void col_bwd_compute(const ColBwdTile<D>& tl,
+                                                const bf16x8_t (&kf)[Shape<D>::KS],
+                                                const bf16x8_t (&vf)[Shape<D>::KS],
+                                                f32x4_t (&dk)[Shape<D>::NB],
+                                                f32x4_t (&dv)[Shape<D>::NB], uint16_t* qs,
+                                                uint16_t* os, float scale2, int c, int g)
+{
+    using S = Shape<D>;
+    f32x4_t sc = {0.f, 0.f, 0.f, 0.f}, dp = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < S::KS; ++s) {
+        sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, tl.qa[s]), kf[s],
+                                                     sc, 0, 0, 0);
+        dp = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, tl.oa[s]), vf[s],
+                                                     dp, 0, 0, 0);
+    }
+#pragma unroll
+    for (int s = 0; s < S::KS; ++s) {
+        *reinterpret_cast<Frag*>(qs + c * S::LDW + 32 * s + 8 * g) = tl.qa[s];
+        *reinterpret_cast<Frag*>(os + c * S::LDW + 32 * s + 8 * g) = tl.oa[s];
+    }
+    short pb[4], db[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const float p = ((tl.valid >> k) & 1u) ? fast_exp2(sc[k] * scale2 - tl.st[k].lse2) : 0.f;
+        pb[k] = bf16_bits(p);
+        db[k] = bf16_bits(p * (dp[k] - tl.st[k].delta));
+    }
+    const s16x4_t P = {pb[0], pb[1], pb[2], pb[3]};
+    const s16x4_t Sd = {db[0], db[1], db[2], db[3]};
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int s = 0; s < S::NB; ++s) {
+        s16x4_t qt, ot;
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            qt[kk] = static_cast<short>(qs[(4 * g + kk) * S::LDW + 16 * s + c]);
+            ot[kk] = static_cast<short>(os[(4 * g + kk) * S::LDW + 16 * s + c]);
+        }
+        dk[s] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(qt, Sd, dk[s], 0, 0, 0);
+        dv[s] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ot, P, dv[s], 0, 0, 0);
+    }
+    __builtin_amdgcn_wave_barrier();
+}
+
 template <int D>
 __global__ __launch_bounds__(kBlock) void gt_bs_bwd_cols(BsBwdArgs a)
 {
-    using T = TileBwd<D>;
-    __shared__ __attribute__((aligned(16))) uint16_t qs_all[kWavesPerBlock][16 * T::LDW];
-    __shared__ __attribute__((aligned(16))) uint16_t os_all[kWavesPerBlock][16 * T::LDW];
+    using S = Shape<D>;
+    __shared__ __attribute__((aligned(16))) uint16_t qs_all[kWavesPerBlock][16 * S::LDW];
+    __shared__ __attribute__((aligned(16))) uint16_t os_all[kWavesPerBlock][16 * S::LDW];
     const int64_t bc = logical_block();
     if (bc >= a.n_blocks) return;
     const int w = wave_id();
     const int l = threadIdx.x & 63, c = l & 15, g = l >> 4;
     const int64_t HD = static_cast<int64_t>(a.H) * D;
+    ColTiles T;
     const int64_t c_lo = bc * kTileDim;
     const int64_t c_hi = c_lo + kTileDim < a.n ? c_lo + kTileDim : a.n;
+    T.n = a.n;
+    T.tcb = a.tile_colptr[bc];
+    T.nd = a.tile_colptr[bc + 1] - T.tcb;
+    T.rcb = a.res_colptr[c_lo];
+    T.rce = a.res_colptr[c_hi];
+    T.H = a.H;
+    T.tile_bycol = a.tile_bycol;
+    T.tile_row = a.tile_row;
+    T.tile_mask = a.tile_mask;
+    T.res_rowidx = a.res_rowidx;
+    T.stats = a.stats;
+    T.starts.load(a.res_colptr, c_lo, c_hi);
+    const int64_t nt = T.count();
     const int64_t j = c_lo + c;
     const bool j_ok = j < a.n;
-    const int64_t tcb = a.tile_colptr[bc], tce = a.tile_colptr[bc + 1];
-    const int64_t rcb = a.res_colptr[c_lo], rce = a.res_colptr[c_hi];
     uint16_t* qs = qs_all[w];
     uint16_t* os = os_all[w];
 
     for (int h = w; h < a.H; h += kWavesPerBlock) {
+        T.h = h;
         const int64_t hoff = static_cast<int64_t>(h) * D;
-        bf16x8_t kf[T::KS], vf[T::KS];
+        bf16x8_t kf[S::KS], vf[S::KS];
 #pragma unroll
-        for (int s = 0; s < T::KS; ++s) {
+        for (int s = 0; s < S::KS; ++s) {
             kf[s] = bf16x8_t{};
             vf[s] = bf16x8_t{};
             if (j_ok) {
@@ -441,52 +616,33 @@ __global__ __launch_bounds__(kBlock) void gt_bs_bwd_cols(BsBwdArgs a)
                 vf[s] = ld_bf16x8(a.V, j * HD + hoff + 32 * s + 8 * g);
             }
         }
-        f32x4_t dk[T::NB], dv[T::NB];
+        f32x4_t dk[S::NB], dv[S::NB];
 #pragma unroll
-        for (int s = 0; s < T::NB; ++s) {
+        for (int s = 0; s < S::NB; ++s) {
             dk[s] = f32x4_t{0.f, 0.f, 0.f, 0.f};
             dv[s] = f32x4_t{0.f, 0.f, 0.f, 0.f};
         }
-        for (int64_t q = tcb; q < tce; ++q) {
-            const int64_t t = a.tile_bycol[q];
-            const int64_t r0 = static_cast<int64_t>(a.tile_row[t]) * kTileDim;
-            const int64_t arow = min(r0 + c, a.n - 1);    // tile row l%16, as the A operand row
-            RowStat st[4];
-            uint32_t valid = 0;
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                const int64_t rk = r0 + 4 * g + k;
-                const uint32_t bit = (static_cast<uint32_t>(a.tile_mask[t * kTileDim + 4 * g + k]) >> c) & 1u;
-                valid |= bit << k;
-                st[k] = RowStat{0.f, 0.f};
-                if (bit) st[k] = a.stats[rk * a.H + h];
-            }
-            T::col_step(arow * HD + hoff, st, valid, kf, vf, dk, dv, a.Q, a.dO, qs, os, a.scale2, c, g);
+        // pipeline: descriptions two tiles ahead, data one tile ahead
+        ColBwdTile<D> next;
+        int32_t t2 = 0, d2 = 0;
+        if (nt > 0) {
+            int32_t t0, d0;
+            T.fetch(0, c, t0, d0);
+            next.load(T, 0, t0, d0, a.Q, a.dO, HD, hoff, c, g);
         }
-        for (int64_t e0 = rcb; e0 < rce; e0 += 16) {
-            const int64_t e = e0 + c;          // row l%16 of this pseudo-tile is residual edge e
-            int cc = -1;
-            int64_t dst = 0;
-            if (e < rce) {
-                dst = a.res_rowidx[e];
-                cc = row_in_block(a.res_colptr, c_lo, c_hi, e);
+        if (nt > 1) T.fetch(1, c, t2, d2);
+        for (int64_t k = 0; k < nt; ++k) {
+            const ColBwdTile<D> cur = next;
+            if (k + 1 < nt) {
+                const int32_t t1 = t2, d1 = d2;
+                if (k + 2 < nt) T.fetch(k + 2, c, t2, d2);
+                next.load(T, k + 1, t1, d1, a.Q, a.dO, HD, hoff, c, g);
             }
-            RowStat st[4];
-            uint32_t valid = 0;
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                const int lk = 4 * g + k;
-                const bool bit = __shfl(cc, lk) == c;
-                const int64_t dk_row = __shfl(static_cast<int>(dst), lk);
-                valid |= (bit ? 1u : 0u) << k;
-                st[k] = RowStat{0.f, 0.f};
-                if (bit) st[k] = a.stats[dk_row * a.H + h];
-            }
-            T::col_step(dst * HD + hoff, st, valid, kf, vf, dk, dv, a.Q, a.dO, qs, os, a.scale2, c, g);
+            col_bwd_compute<D>(cur, kf, vf, dk, dv, qs, os, a.scale2, c, g);
         }
         if (j_ok) {
 #pragma unroll
-            for (int s = 0; s < T::NB; ++s) {
+            for (int s = 0; s < S::NB; ++s) {
                 store_tile_rows(a.dK, j * HD + hoff + 16 * s + 4 * g, dk[s], a.oscale);
                 store_tile_rows(a.dV, j * HD + hoff + 16 * s + 4 * g, dv[s], 1.f);
             }
