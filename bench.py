@@ -179,7 +179,9 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--tiles", action="store_true",
-                    help="Graph Transformer forward on the 16x16 tile (MFMA) path")
+                    help="Graph Transformer forward and backward on the 16x16 tile (MFMA) path")
+    ap.add_argument("--reorder", default="none", choices=["none", "random", "degree", "rcm"],
+                    help="relabel the nodes before timing (graph reordering study)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB three times "
                          "(calibrates the HBM byte counters) and exit")
@@ -209,6 +211,8 @@ def main():
         return
     spec = I.WORKLOADS[args.workload]
     w = I.make_workload(args.workload)
+    if args.reorder != "none":
+        w = I.relabel(w, I.node_order(w["rowptr"], w["colidx"], args.reorder))
     rp, ci = w["rowptr"], w["colidx"]
     n, e = rp.size - 1, int(rp[-1])
     H, D = spec.heads, spec.dim
@@ -321,7 +325,8 @@ def main():
         "data": "synthetic (seeded generator, seed 0)",
         "config": {"workload": args.workload, "graph": spec.graph, "nodes": n, "edges": e,
                    "heads": H, "head_dim": D, "passes": spec.passes,
-                   "chunk": g.plan.stats()["chunk"], "tiles": bool(args.tiles)},
+                   "chunk": g.plan.stats()["chunk"], "tiles": bool(args.tiles),
+                   "reorder": args.reorder},
         "roofline": roofline,
         "kernels": kernels,
         "plan_ms": round(plan_ms, 1),

@@ -392,3 +392,52 @@ def degree_stats(rowptr: np.ndarray) -> dict:
         "p99": float(np.percentile(deg, 99)), "p999": float(np.percentile(deg, 99.9)),
         "max": int(deg.max()), "mean": float(deg.mean()),
     }
+
+
+# ----------------------------------------------------------------------------
+# node orderings (graph reordering study)
+# ----------------------------------------------------------------------------
+
+ORDERINGS = ("none", "random", "degree", "rcm")
+
+
+def node_order(rowptr: np.ndarray, colidx: np.ndarray, kind: str, seed: int = 0) -> np.ndarray:
+    """order[k] = the old id of the node placed at new position k.
+
+    "none": the ids as generated; "random": a seeded uniform permutation;
+    "degree": in-degree descending (ties by id); "rcm": reverse Cuthill-McKee
+    on the structure of A + A^T.
+    """
+    n = rowptr.size - 1
+    if kind == "none":
+        return np.arange(n, dtype=np.int64)
+    if kind == "random":
+        return np.random.default_rng(seed).permutation(n).astype(np.int64)
+    if kind == "degree":
+        return np.argsort(-np.diff(rowptr), kind="stable").astype(np.int64)
+    if kind == "rcm":
+        import scipy.sparse as sp
+        from scipy.sparse.csgraph import reverse_cuthill_mckee
+        A = sp.csr_matrix((np.ones(colidx.size, dtype=np.int8), colidx, rowptr), shape=(n, n))
+        return np.asarray(reverse_cuthill_mckee(A, symmetric_mode=False), dtype=np.int64)
+    raise KeyError(kind)
+
+
+def relabel(w: dict, order: np.ndarray) -> dict:
+    """The same workload with node order[k] renamed k: the graph is rebuilt
+    (rows ascending, sources ascending, every edge and repeat kept) and every
+    per-node tensor permuted; per-head parameters are unchanged."""
+    rp, ci = w["rowptr"], w["colidx"]
+    n = rp.size - 1
+    new_id = np.empty(n, dtype=np.int64)
+    new_id[order] = np.arange(n, dtype=np.int64)
+    dst = np.repeat(np.arange(n, dtype=np.int64), np.diff(rp))
+    rp2, ci2 = csr_from_edges(n, new_id[dst], new_id[ci.astype(np.int64)], self_loops=False,
+                              dedup=False)
+    out = dict(w)
+    out["rowptr"], out["colidx"] = rp2, ci2
+    out["order"] = order
+    for key in ("q", "k", "v", "xs", "xt", "dout"):
+        if key in w:
+            out[key] = np.ascontiguousarray(w[key][order])
+    return out
