@@ -182,6 +182,8 @@ def main():
                     help="Graph Transformer forward and backward on the 16x16 tile (MFMA) path")
     ap.add_argument("--reorder", default="none", choices=["none", "random", "degree", "rcm"],
                     help="relabel the nodes before timing (graph reordering study)")
+    ap.add_argument("--locality", type=int, default=0, choices=[0, 1],
+                    help="1: the plan orders rows of a degree bin by Cuthill-McKee rank")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB three times "
                          "(calibrates the HBM byte counters) and exit")
@@ -220,7 +222,8 @@ def main():
     nbytes = 2 if dt == B.BF16 else 4
 
     t0 = time.perf_counter()
-    g = B.DeviceGraph(rp, ci, device=dev, chunk=args.chunk, block_sparse=args.tiles)
+    g = B.DeviceGraph(rp, ci, device=dev, chunk=args.chunk, block_sparse=args.tiles,
+                      locality=bool(args.locality))
     tw = tile_work(g.plan) if args.tiles else None
     torch.cuda.synchronize()
     plan_ms = (time.perf_counter() - t0) * 1e3
@@ -326,7 +329,7 @@ def main():
         "config": {"workload": args.workload, "graph": spec.graph, "nodes": n, "edges": e,
                    "heads": H, "head_dim": D, "passes": spec.passes,
                    "chunk": g.plan.stats()["chunk"], "tiles": bool(args.tiles),
-                   "reorder": args.reorder},
+                   "reorder": args.reorder, "locality": args.locality},
         "roofline": roofline,
         "kernels": kernels,
         "plan_ms": round(plan_ms, 1),

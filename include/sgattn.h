@@ -86,6 +86,11 @@ typedef struct sgat_plan_opts {
     int32_t tile_min_nnz; /* A 16x16 block of the adjacency with at least this many
                              distinct edges becomes a dense tile. Default 32. */
     int32_t block_sparse; /* 1: also build the 16x16 tile layout and residual CSR. */
+    int32_t locality;     /* 0: rows of a degree bin in ascending id; 1: in Cuthill-McKee
+                             order of the undirected graph, so rows that share
+                             neighbours run close together in time (more L2 reuse
+                             of gathered rows). Results are the same up to rounding. */
+    int32_t reserved;     /* must be 0 */
 } sgat_plan_opts;
 
 /* Summary of a plan (all counts are exact). */

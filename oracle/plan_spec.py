@@ -48,7 +48,51 @@ def floor_log2(deg: np.ndarray) -> np.ndarray:
     return b            # -1 for deg == 0
 
 
-def work_list(ptr: np.ndarray, chunk: int):
+def cuthill_mckee_rank(rowptr: np.ndarray, colidx: np.ndarray) -> np.ndarray:
+    """Cuthill-McKee rank of each node of the undirected simple graph under the
+    CSR (in- and out-neighbours, no self-loops, no repeats). Components start
+    from the unvisited node of least degree (then least id); a visited node's
+    unvisited neighbours are appended by (degree, id)."""
+    rowptr = np.asarray(rowptr, dtype=np.int64)
+    n = rowptr.size - 1
+    dst = np.repeat(np.arange(n, dtype=np.int64), np.diff(rowptr))
+    src = np.asarray(colidx, dtype=np.int64)
+    keep = dst != src
+    a = np.concatenate([dst[keep], src[keep]])
+    b = np.concatenate([src[keep], dst[keep]])
+    code = np.unique(a * max(n, 1) + b)
+    u = code // max(n, 1)
+    v = code - u * max(n, 1)
+    deg = np.bincount(u, minlength=n).astype(np.int64)
+    adj = [[] for _ in range(n)]
+    for x, y in zip(u.tolist(), v.tolist()):
+        adj[x].append(y)
+    for x in range(n):
+        adj[x].sort(key=lambda y: (deg[y], y))
+    seeds = sorted(range(n), key=lambda y: (deg[y], y))
+    seen = np.zeros(n, dtype=bool)
+    order = []
+    for s0 in seeds:
+        if seen[s0]:
+            continue
+        seen[s0] = True
+        head = len(order)
+        order.append(s0)
+        while head < len(order):
+            x = order[head]
+            head += 1
+            for y in adj[x]:
+                if not seen[y]:
+                    seen[y] = True
+                    order.append(y)
+    rank = np.empty(n, dtype=np.int32)
+    rank[np.asarray(order, dtype=np.int64)] = np.arange(n, dtype=np.int32)
+    return rank
+
+
+def work_list(ptr: np.ndarray, chunk: int, rank: np.ndarray | None = None):
+    """Work items and split records; whole rows of a bin by ascending rank
+    (ascending id without one)."""
     ptr = np.asarray(ptr, dtype=np.int64)
     n = ptr.size - 1
     deg = np.diff(ptr)
@@ -73,7 +117,8 @@ def work_list(ptr: np.ndarray, chunk: int):
 
     light = rows[deg <= chunk]
     b = floor_log2(deg[light])
-    order = np.lexsort((light, -b))       # bin descending, then row ascending
+    key2 = light if rank is None else np.asarray(rank, dtype=np.int64)[light]
+    order = np.lexsort((key2, -b))        # bin descending, then rank (or row) ascending
     light = light[order]
     whole = np.zeros(light.size, dtype=WORK_ITEM)
     whole["begin"] = ptr[light]

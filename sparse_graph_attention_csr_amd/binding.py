@@ -53,7 +53,8 @@ class SgatError(RuntimeError):
 
 class PlanOpts(ctypes.Structure):
     _fields_ = [("chunk", ctypes.c_int64), ("tile_min_nnz", ctypes.c_int32),
-                ("block_sparse", ctypes.c_int32)]
+                ("block_sparse", ctypes.c_int32), ("locality", ctypes.c_int32),
+                ("reserved", ctypes.c_int32)]
 
 
 class PlanStats(ctypes.Structure):
@@ -166,12 +167,13 @@ class Plan:
     """Host plan of one CSR graph (sgat_plan_create / _upload / _destroy)."""
 
     def __init__(self, rowptr, colidx, chunk: int = 0, tile_min_nnz: int = 0,
-                 block_sparse: bool = False):
+                 block_sparse: bool = False, locality: bool = False):
         rowptr = np.ascontiguousarray(rowptr, dtype=np.int64)
         colidx = np.ascontiguousarray(colidx, dtype=np.int32)
         self.n = int(rowptr.size - 1)
         self.nnz = int(colidx.size)
-        opts = PlanOpts(int(chunk), int(tile_min_nnz), int(bool(block_sparse)))
+        opts = PlanOpts(int(chunk), int(tile_min_nnz), int(bool(block_sparse)),
+                        int(bool(locality)), 0)
         h = ctypes.c_void_p()
         _check("sgat_plan_create",
                lib().sgat_plan_create(self.n, self.nnz, rowptr.ctypes.data, colidx.ctypes.data,
@@ -305,10 +307,10 @@ class DeviceGraph:
     """
 
     def __init__(self, rowptr, colidx, device="cuda", chunk: int = 0, tile_min_nnz: int = 0,
-                 block_sparse: bool = False, stream=None):
+                 block_sparse: bool = False, locality: bool = False, stream=None):
         import torch
         self.plan = Plan(rowptr, colidx, chunk=chunk, tile_min_nnz=tile_min_nnz,
-                         block_sparse=block_sparse)
+                         block_sparse=block_sparse, locality=locality)
         self.n, self.nnz = self.plan.n, self.plan.nnz
         self.device = torch.device(device)
         self.rowptr = torch.from_numpy(np.ascontiguousarray(rowptr, dtype=np.int64)).to(self.device)

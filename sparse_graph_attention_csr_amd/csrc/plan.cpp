@@ -40,7 +40,7 @@ static int degree_bin(int64_t deg)
 
 void build_work_list(int64_t n, const int64_t* ptr, int64_t chunk,
                      std::vector<sgat_work_item>& items, std::vector<sgat_split>& splits,
-                     int64_t& nslots)
+                     int64_t& nslots, const int32_t* rank)
 {
     items.clear();
     splits.clear();
@@ -61,7 +61,12 @@ void build_work_list(int64_t n, const int64_t* ptr, int64_t chunk,
         nslots += nk;
     }
     // 2. whole rows, by degree bin floor(log2(deg)) descending, empty rows
-    //    last, ascending row id inside a bin (a counting sort)
+    //    last; inside a bin ascending rank, or ascending id (a counting sort)
+    std::vector<int32_t> by_rank;
+    if (rank) {
+        by_rank.assign(static_cast<size_t>(n), 0);
+        for (int64_t i = 0; i < n; ++i) by_rank[static_cast<size_t>(rank[i])] = static_cast<int32_t>(i);
+    }
     std::vector<int64_t> count(65, 0);
     for (int64_t i = 0; i < n; ++i) {
         int64_t deg = ptr[i + 1] - ptr[i];
@@ -72,13 +77,69 @@ void build_work_list(int64_t n, const int64_t* ptr, int64_t chunk,
     for (int s = 1; s < 65; ++s) start[s] = start[s - 1] + count[s - 1];
     size_t base = items.size();
     items.resize(base + static_cast<size_t>(start[64] + count[64]));
-    for (int64_t i = 0; i < n; ++i) {
+    for (int64_t q = 0; q < n; ++q) {
+        const int64_t i = rank ? by_rank[static_cast<size_t>(q)] : q;
         int64_t deg = ptr[i + 1] - ptr[i];
         if (deg > chunk) continue;
         int s = 64 - (degree_bin(deg) + 1);
         items[base + static_cast<size_t>(start[s]++)] =
             {ptr[i], static_cast<int32_t>(deg), static_cast<int32_t>(i), -1, 1};
     }
+}
+
+std::vector<int32_t> cuthill_mckee_rank(int64_t n, const int64_t* rowptr, const int32_t* colidx,
+                                        const int64_t* colptr, const int32_t* rowidx)
+{
+    // undirected simple adjacency: in- and out-neighbours, sorted, unique, no self
+    std::vector<int64_t> aptr(static_cast<size_t>(n) + 1, 0);
+    std::vector<int32_t> adj;
+    adj.reserve(static_cast<size_t>(rowptr[n]) * 2);
+    std::vector<int32_t> tmp;
+    for (int64_t v = 0; v < n; ++v) {
+        tmp.clear();
+        for (int64_t e = rowptr[v]; e < rowptr[v + 1]; ++e)
+            if (colidx[e] != v) tmp.push_back(colidx[e]);
+        for (int64_t e = colptr[v]; e < colptr[v + 1]; ++e)
+            if (rowidx[e] != v) tmp.push_back(rowidx[e]);
+        std::sort(tmp.begin(), tmp.end());
+        tmp.erase(std::unique(tmp.begin(), tmp.end()), tmp.end());
+        adj.insert(adj.end(), tmp.begin(), tmp.end());
+        aptr[static_cast<size_t>(v) + 1] = static_cast<int64_t>(adj.size());
+    }
+    std::vector<int64_t> deg(static_cast<size_t>(n));
+    for (int64_t v = 0; v < n; ++v) deg[static_cast<size_t>(v)] = aptr[v + 1] - aptr[v];
+    auto less = [&](int32_t a, int32_t b) {
+        return deg[static_cast<size_t>(a)] != deg[static_cast<size_t>(b)]
+                   ? deg[static_cast<size_t>(a)] < deg[static_cast<size_t>(b)]
+                   : a < b;
+    };
+    for (int64_t v = 0; v < n; ++v)
+        std::sort(adj.begin() + aptr[v], adj.begin() + aptr[v + 1], less);
+    std::vector<int32_t> seeds(static_cast<size_t>(n));
+    for (int64_t v = 0; v < n; ++v) seeds[static_cast<size_t>(v)] = static_cast<int32_t>(v);
+    std::stable_sort(seeds.begin(), seeds.end(), less);
+    std::vector<unsigned char> seen(static_cast<size_t>(n), 0);
+    std::vector<int32_t> order;
+    order.reserve(static_cast<size_t>(n));
+    for (int32_t s0 : seeds) {
+        if (seen[static_cast<size_t>(s0)]) continue;
+        seen[static_cast<size_t>(s0)] = 1;
+        size_t head = order.size();
+        order.push_back(s0);
+        while (head < order.size()) {
+            const int32_t v = order[head++];
+            for (int64_t e = aptr[v]; e < aptr[v + 1]; ++e) {
+                const int32_t u = adj[static_cast<size_t>(e)];
+                if (!seen[static_cast<size_t>(u)]) {
+                    seen[static_cast<size_t>(u)] = 1;
+                    order.push_back(u);
+                }
+            }
+        }
+    }
+    std::vector<int32_t> rank(static_cast<size_t>(n));
+    for (size_t k = 0; k < order.size(); ++k) rank[static_cast<size_t>(order[k])] = static_cast<int32_t>(k);
+    return rank;
 }
 
 void build_transpose(int64_t n, const int64_t* rowptr, const int32_t* colidx,
@@ -250,14 +311,17 @@ int sgat_plan_create(int64_t n, int64_t nnz, const int64_t* rowptr, const int32_
     if (rc != SGAT_OK) return rc;
     int64_t chunk = sgat::kDefaultChunk;
     int32_t tmin = sgat::kDefaultTileMinNnz;
-    bool bs = false;
+    bool bs = false, loc = false;
     if (opts) {
         if (opts->chunk < 0 || opts->chunk > INT32_MAX) return SGAT_INVALID_ARGUMENT;
         if (opts->tile_min_nnz < 0 || opts->tile_min_nnz > 256) return SGAT_INVALID_ARGUMENT;
         if (opts->block_sparse != 0 && opts->block_sparse != 1) return SGAT_INVALID_ARGUMENT;
+        if (opts->locality != 0 && opts->locality != 1) return SGAT_INVALID_ARGUMENT;
+        if (opts->reserved != 0) return SGAT_INVALID_ARGUMENT;
         if (opts->chunk > 0) chunk = opts->chunk;
         if (opts->tile_min_nnz > 0) tmin = opts->tile_min_nnz;
         bs = opts->block_sparse == 1;
+        loc = opts->locality == 1;
     }
     sgat_plan* h = new (std::nothrow) sgat_plan;
     if (!h) return SGAT_OUT_OF_HOST_MEMORY;
@@ -268,13 +332,17 @@ int sgat_plan_create(int64_t n, int64_t nnz, const int64_t* rowptr, const int32_
         p.chunk = chunk;
         p.tile_min_nnz = tmin;
         p.block_sparse = bs;
+        p.locality = loc;
         for (int64_t i = 0; i < n; ++i)
             p.max_in_degree = std::max(p.max_in_degree, rowptr[i + 1] - rowptr[i]);
-        sgat::build_work_list(n, rowptr, chunk, p.row_items, p.row_splits, p.row_slots);
         sgat::build_transpose(n, rowptr, colidx, p.colptr, p.rowidx, &p.col_edge);
         for (int64_t j = 0; j < n; ++j)
             p.max_out_degree = std::max(p.max_out_degree, p.colptr[j + 1] - p.colptr[j]);
-        sgat::build_work_list(n, p.colptr.data(), chunk, p.col_items, p.col_splits, p.col_slots);
+        std::vector<int32_t> rank;
+        if (loc) rank = sgat::cuthill_mckee_rank(n, rowptr, colidx, p.colptr.data(), p.rowidx.data());
+        const int32_t* rk = loc ? rank.data() : nullptr;
+        sgat::build_work_list(n, rowptr, chunk, p.row_items, p.row_splits, p.row_slots, rk);
+        sgat::build_work_list(n, p.colptr.data(), chunk, p.col_items, p.col_splits, p.col_slots, rk);
         if (bs) {
             sgat::build_tiles(n, rowptr, colidx, tmin, p.tile_rowptr, p.tile_col, p.tile_mask,
                               p.res_rowptr, p.res_colidx, p.tile_edges);

@@ -21,6 +21,7 @@ struct Plan {
     int64_t chunk = kDefaultChunk;
     int32_t tile_min_nnz = kDefaultTileMinNnz;
     bool block_sparse = false;
+    bool locality = false;
     int64_t max_in_degree = 0, max_out_degree = 0;
 
     std::vector<sgat_work_item> row_items;
@@ -62,10 +63,16 @@ struct Plan {
 // A1: returns SGAT_OK or SGAT_INVALID_CSR / SGAT_INVALID_ARGUMENT.
 int validate_csr(int64_t n, int64_t nnz, const int64_t* rowptr, const int32_t* colidx);
 
-// A2: degree-binned work list over any CSR-like pointer array.
+// A2: degree-binned work list over any CSR-like pointer array. Whole rows of
+// one bin come in ascending `rank` (ascending id when rank is null).
 void build_work_list(int64_t n, const int64_t* ptr, int64_t chunk,
                      std::vector<sgat_work_item>& items, std::vector<sgat_split>& splits,
-                     int64_t& nslots);
+                     int64_t& nslots, const int32_t* rank = nullptr);
+
+// Cuthill-McKee rank of every node of the undirected simple graph underlying
+// the CSR (in- and out-neighbours, self-loops and repeats dropped).
+std::vector<int32_t> cuthill_mckee_rank(int64_t n, const int64_t* rowptr, const int32_t* colidx,
+                                        const int64_t* colptr, const int32_t* rowidx);
 
 // A3: transposed CSR by stable counting sort of edges by source; with
 // `edge_ids` also the CSR edge id of every transposed entry.

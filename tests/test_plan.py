@@ -10,17 +10,18 @@ from sparse_graph_attention_csr_amd import binding as B
 from sparse_graph_attention_csr_amd import inputs as I
 
 
-def check_plan(rowptr, colidx, chunk, tmin=0, bs=False):
-    p = B.Plan(rowptr, colidx, chunk=chunk, tile_min_nnz=tmin, block_sparse=bs)
+def check_plan(rowptr, colidx, chunk, tmin=0, bs=False, loc=False):
+    p = B.Plan(rowptr, colidx, chunk=chunk, tile_min_nnz=tmin, block_sparse=bs, locality=loc)
     C = p.stats()["chunk"]
-    items, splits, nslots = S.work_list(rowptr, C)
+    rank = S.cuthill_mckee_rank(rowptr, colidx) if loc else None
+    items, splits, nslots = S.work_list(rowptr, C, rank)
     assert p.export(B.ARR_ROW_ITEMS).tobytes() == items.tobytes()
     assert p.export(B.ARR_ROW_SPLITS).tobytes() == splits.tobytes()
     colptr, rowidx, col_edge = S.transpose(rowptr, colidx, edge_ids=True)
     assert np.array_equal(p.export(B.ARR_COLPTR), colptr)
     assert np.array_equal(p.export(B.ARR_ROWIDX), rowidx)
     assert np.array_equal(p.export(B.ARR_COL_EDGE), col_edge)
-    citems, csplits, cslots = S.work_list(colptr, C)
+    citems, csplits, cslots = S.work_list(colptr, C, rank)
     assert p.export(B.ARR_COL_ITEMS).tobytes() == citems.tobytes()
     assert p.export(B.ARR_COL_SPLITS).tobytes() == csplits.tobytes()
     st_ = p.stats()
@@ -82,10 +83,25 @@ GRAPHS = {
 
 @pytest.mark.parametrize("name", list(GRAPHS))
 @pytest.mark.parametrize("chunk", [1, 7, 16, 0])
-def test_plan_matches_spec(name, chunk):
-    rp, ci = I.random_csr(rng=np.random.default_rng(hash(name) % 1000), **GRAPHS[name])
-    p = check_plan(rp, ci, chunk, tmin=3, bs=True)
+@pytest.mark.parametrize("loc", [False, True])
+def test_plan_matches_spec(name, chunk, loc):
+    rp, ci = I.random_csr(rng=np.random.default_rng(sum(map(ord, name))), **GRAPHS[name])
+    p = check_plan(rp, ci, chunk, tmin=3, bs=True, loc=loc)
     invariants(p, rp, ci)
+
+
+def test_cuthill_mckee_visits_components_breadth_first():
+    # two components: a path 0-1-2-3 and a star 4-(5,6,7); self-loops ignored
+    rows = [[1], [0, 2], [1, 3, 3], [2, 3], [5, 6, 7], [4], [4], [4, 7]]
+    rp = np.zeros(len(rows) + 1, dtype=np.int64)
+    rp[1:] = np.cumsum([len(r) for r in rows])
+    ci = np.array([j for r in rows for j in r], dtype=np.int32)
+    rank = S.cuthill_mckee_rank(rp, ci)
+    order = np.argsort(rank)
+    # least degree first (node 0, degree 1; ties by id), then breadth first
+    assert order.tolist()[:4] == [0, 1, 2, 3]
+    assert set(order.tolist()[4:]) == {4, 5, 6, 7} and order[4] == 5
+    check_plan(rp, ci, 0, loc=True)
 
 
 def test_plan_on_workload_graph():
@@ -119,7 +135,7 @@ def test_dense_community_tiles():
        seed=st.integers(0, 2**31 - 1))
 def test_plan_property(n, max_deg, chunk, tmin, empty, dup, seed):
     rp, ci = I.random_csr(n, max_deg, np.random.default_rng(seed), empty_frac=empty, dup_frac=dup)
-    p = check_plan(rp, ci, chunk, tmin=tmin, bs=True)
+    p = check_plan(rp, ci, chunk, tmin=tmin, bs=True, loc=bool(seed & 1))
     invariants(p, rp, ci)
     s = p.stats()
     assert s["tile_edges"] + s["residual_edges"] == ci.size
