@@ -32,15 +32,19 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK = 2.5e15   # dense bf16 matrix-core flop/s
 DEFAULT_WORKLOAD = "gt_powerlaw200k_h4d128_bf16"
-KERNEL_SOURCES = ["sparse_graph_attention_csr_amd/csrc/device.hpp",
-                  "sparse_graph_attention_csr_amd/csrc/gather.hpp",
-                  "sparse_graph_attention_csr_amd/csrc/launch_gt.hip",
-                  "sparse_graph_attention_csr_amd/csrc/launch_gat.hip"]
+_CSRC = "sparse_graph_attention_csr_amd/csrc/"
+# the sources each kernel family is compiled from (a counter summary is valid
+# only for the sources it was taken on)
+KERNEL_SOURCES = {
+    "gather": [_CSRC + f for f in ("device.hpp", "gather.hpp", "launch.hpp", "launch_gt.hip",
+                                   "launch_gat.hip")],
+    "tiles": [_CSRC + f for f in ("device.hpp", "blocksparse.hpp", "launch.hpp", "launch_bs.hip")],
+}
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(kernel: str) -> str:
     h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
+    for p in KERNEL_SOURCES["tiles" if kernel.startswith("gt_bs_") else "gather"]:
         with open(os.path.join(ROOT, p), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -121,7 +125,7 @@ def read_traffic(kernel: str, workload: str):
     txt = open(path).read()
     m = re.search(r"kernel_source_hash:\s*(\w+)", txt)
     t = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", txt)
-    if not m or not t or m.group(1) != kernel_source_hash():
+    if not m or not t or m.group(1) != kernel_source_hash(kernel):
         return None
     return float(t.group(1))
 
@@ -169,6 +173,73 @@ def cpu_baseline(w, seconds: float):
                       f"{spec.passes}, fp64, {t:.1f} s"}
 
 
+def compare_unfused(spec, g, fused_step, fused_owned, inputs, fused_out, bwd, fused_ms,
+                    steps, warmup):
+    """Latency and peak device memory of one step of the unfused PyTorch
+    formulation against the fused library on the same resident inputs.
+
+    Memory counts what a step needs beyond the inputs and the device CSR, which
+    both share: for the fused library the plan, workspaces, outputs and
+    gradients (all allocated once, reused every step) plus anything allocated
+    during a step; for the unfused formulation the peak of torch's allocator
+    over a step (edge lists, per-edge tensors kept for autograd, outputs and
+    gradients)."""
+    import torch
+
+    import bench_unfused as U
+
+    def nbytes(t):
+        return t.numel() * t.element_size()
+
+    torch.cuda.synchronize()
+    base = torch.cuda.memory_allocated()
+    torch.cuda.reset_peak_memory_stats()
+    fused_step()
+    torch.cuda.synchronize()
+    fused_bytes = sum(nbytes(t) for t in fused_owned) + torch.cuda.max_memory_allocated() - base
+
+    E, H, D = g.colidx.numel(), spec.heads, spec.dim
+    est = E * H * D * (16 if inputs[0].element_size() == 2 else 28)
+    free = torch.cuda.mem_get_info()[0]
+    if est > 0.8 * free:
+        return {"skipped": f"estimated unfused peak {est / 2**30:.0f} GiB exceeds the free "
+                           f"device memory ({free / 2**30:.0f} GiB)"}
+
+    def unfused_step():
+        leaves = [t.detach().requires_grad_(bwd) for t in inputs[:3]]
+        dst, src = U.edge_index(g.rowptr, g.colidx)
+        if spec.op == "gt":
+            o, _ = U.gt(dst, src, *leaves)
+        else:
+            o, _ = U.gatv2(dst, src, *leaves, 0.2)
+        if bwd:
+            o.backward(inputs[3])
+        return o.detach(), [t.grad for t in leaves]
+
+    torch.cuda.synchronize()
+    base = torch.cuda.memory_allocated()
+    torch.cuda.reset_peak_memory_stats()
+    o, grads = unfused_step()
+    torch.cuda.synchronize()
+    unfused_bytes = torch.cuda.max_memory_allocated() - base
+    diff = ((o.float() - fused_out.float()).abs().max() / fused_out.float().abs().max()).item()
+    del o, grads
+    for _ in range(warmup):
+        unfused_step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        unfused_step()
+    torch.cuda.synchronize()
+    unfused_ms = (time.perf_counter() - t0) * 1e3 / steps
+    return {"ms_per_step": round(unfused_ms, 3), "fused_ms_per_step": round(fused_ms, 3),
+            "latency_ratio": round(unfused_ms / fused_ms, 2),
+            "peak_mib": round(unfused_bytes / 2**20, 1),
+            "fused_mib": round(fused_bytes / 2**20, 1),
+            "memory_ratio": round(unfused_bytes / fused_bytes, 2),
+            "output_max_rel_diff": diff}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -184,6 +255,9 @@ def main():
                     help="relabel the nodes before timing (graph reordering study)")
     ap.add_argument("--locality", type=int, default=0, choices=[0, 1],
                     help="1: the plan orders rows of a degree bin by Cuthill-McKee rank")
+    ap.add_argument("--compare-unfused", action="store_true",
+                    help="also time the unfused PyTorch formulation (bench_unfused.py) and "
+                         "report latency and peak-memory ratios")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB three times "
                          "(calibrates the HBM byte counters) and exit")
@@ -244,6 +318,9 @@ def main():
             dQ, dK, dV = (torch.empty_like(Q) for _ in range(3))
             wsb = g.workspace(B.OP_GT_BWD, H, D, dt)
 
+        owned = [out, lse, wsf] + ([dQ, dK, dV, wsb] if bwd else [])
+        inputs = [Q, K, V] + ([dO] if bwd else [])
+
         def step():
             B.gt_fwd(g.plan, g.rowptr, g.colidx, Q, K, V, out, lse, wsf, use_tiles=args.tiles)
             if bwd:
@@ -260,6 +337,9 @@ def main():
             dXs, dXt = torch.empty_like(Xs), torch.empty_like(Xs)
             dA = torch.empty(H, D, dtype=torch.float32, device=dev)
             wsb = g.workspace(B.OP_GAT_BWD, H, D, dt)
+
+        owned = [out, lse, wsf] + ([dXs, dXt, dA, wsb] if bwd else [])
+        inputs = [Xs, Xt, A] + ([dO] if bwd else [])
 
         def step():
             B.gat_fwd(g.plan, g.rowptr, g.colidx, Xs, Xt, A, 0.2, out, lse, wsf)
@@ -334,6 +414,9 @@ def main():
         "kernels": kernels,
         "plan_ms": round(plan_ms, 1),
     }
+    if args.compare_unfused:
+        line["unfused"] = compare_unfused(spec, g, step, owned + [g.plan_buf], inputs, out,
+                                          bwd, ms_per_step, args.steps, args.warmup)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
     print(json.dumps(line), flush=True)
