@@ -6,7 +6,8 @@ Python binding) never loads it, and it shares no code with them.
 
 ``oracle.c`` computes the plain definition of Graph Transformer and GATv2
 attention over a CSR neighbourhood in fp64 (forward and the softmax-Jacobian
-backward); ``plan_spec.py`` is an independent numpy statement of the integer
+backward), and of min/max reduction aggregation (forward with its winning
+edges, and the backward that routes each gradient to its winner); ``plan_spec.py`` is an independent numpy statement of the integer
 preprocessing arrays (work lists, transposed CSR, 16x16 tiles).
 
 Inputs may be numpy float32, float64 or uint16 (bf16 bit patterns); they are
@@ -55,7 +56,10 @@ def _load():
                                       i64, vp, vp, i64, vp, vp, vp]
         lib.oracle_gat_bwd.argtypes = [i64, vp, vp, i32, i32, i32, vp, vp, vp, dbl, vp,
                                        i64, vp, vp, i64, vp, vp, vp]
-        for f in (lib.oracle_gt_fwd, lib.oracle_gat_fwd, lib.oracle_gt_bwd, lib.oracle_gat_bwd):
+        lib.oracle_reduce_fwd.argtypes = [i64, vp, vp, i32, i32, i32, vp, i64, vp, vp, vp]
+        lib.oracle_reduce_bwd.argtypes = [i64, vp, vp, i32, i32, vp, vp, vp]
+        for f in (lib.oracle_gt_fwd, lib.oracle_gat_fwd, lib.oracle_gt_bwd, lib.oracle_gat_bwd,
+                  lib.oracle_reduce_fwd, lib.oracle_reduce_bwd):
             f.restype = i32
         _lib = lib
     return _lib
@@ -161,3 +165,47 @@ def gat_bwd(rowptr, colidx, xs, xt, a, dout, slope=0.2, dst_rows=None, src_rows=
                                   float(slope), _p(dout), nd, _p(sd), _p(dxs), nss, _p(ss),
                                   _p(dxt), _p(da)), "oracle_gat_bwd")
     return dxs, dxt, da
+
+
+_OPS = {"min": 0, "max": 1}
+
+
+def _features2(x):
+    x = np.ascontiguousarray(x)
+    if x.dtype not in _DT:
+        raise TypeError(f"unsupported dtype {x.dtype}")
+    if x.ndim != 2:
+        raise ValueError("reduction features must be [N, F]")
+    return x, _DT[x.dtype]
+
+
+def reduce_fwd(rowptr, colidx, x, op="min", rows=None):
+    """Min or max aggregation of the source rows x [N, F] over each row's
+    in-edges: (out fp64, arg int64), both [rows or N, F]. arg holds the CSR
+    position of the winning edge (the first one on ties), -1 for empty rows,
+    whose out is 0."""
+    rowptr, colidx = _graph(rowptr, colidx)
+    x, dt = _features2(x)
+    n, F = x.shape
+    s, ns = _sel(rows)
+    cnt = ns if s is not None else n
+    out = np.empty((cnt, F), dtype=np.float64)
+    arg = np.empty((cnt, F), dtype=np.int64)
+    _check(_load().oracle_reduce_fwd(n, _p(rowptr), _p(colidx), F, dt, _OPS[op], _p(x), ns,
+                                     _p(s), _p(out), _p(arg)), "oracle_reduce_fwd")
+    return out, arg
+
+
+def reduce_bwd(rowptr, colidx, arg, dout):
+    """Backward of L = sum(out * dout) for the aggregation whose winners are
+    ``arg`` [N, F] (as reduce_fwd returns over all rows): dX fp64 [N, F]."""
+    rowptr, colidx = _graph(rowptr, colidx)
+    dout, dt = _features2(dout)
+    n, F = dout.shape
+    arg = np.ascontiguousarray(arg, dtype=np.int64)
+    if arg.shape != (n, F):
+        raise ValueError("arg must be [N, F]")
+    dx = np.empty((n, F), dtype=np.float64)
+    _check(_load().oracle_reduce_bwd(n, _p(rowptr), _p(colidx), F, dt, _p(arg), _p(dout),
+                                     _p(dx)), "oracle_reduce_bwd")
+    return dx

@@ -1,5 +1,6 @@
 /*
- * fp64 CPU oracle for fused graph attention over a CSR neighbourhood.
+ * fp64 CPU oracle for fused graph attention over a CSR neighbourhood, and for
+ * min/max reduction aggregation over the same neighbourhood (last section).
  *
  * TEST INFRASTRUCTURE ONLY. Nothing on the product path may link, load or call
  * this file: only the tests, the smoke check and the benchmark's CPU-baseline
@@ -410,5 +411,69 @@ int oracle_gat_bwd(int64_t n, const int64_t* rowptr, const int32_t* colidx, int 
         }
     }
     free(colptr); free(eid); free(erow); free(alpha); free(dE);
+    return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* reduction aggregation: min / max pooling over the in-neighbours            */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * The reduction-based aggregation family (IO-aware layers abstract; Yandex
+ * Research blog, paragraph on aggregation layers: min/max pooling). Readings:
+ * the message of edge j -> i is the source row X[j] (F features); for every
+ * destination i and feature f the result is the extreme value over the row's
+ * edges; the winning edge is the first one in CSR order whose value is
+ * strictly below (min) or above (max) every earlier value of the row, so ties
+ * go to the lowest position; an empty row gives 0 and no winner (arg -1).
+ * op 0 = min, op 1 = max.
+ */
+int oracle_reduce_fwd(int64_t n, const int64_t* rowptr, const int32_t* colidx, int F, int dtype,
+                      int op, const void* X, int64_t nsel, const int64_t* sel, double* out,
+                      int64_t* arg)
+{
+    int rc = check_csr(n, rowptr, colidx);
+    if (rc) return rc;
+    if (F < 1 || (op != 0 && op != 1)) return 1;
+    int64_t cnt = sel ? nsel : n;
+#pragma omp parallel for schedule(dynamic, 16)
+    for (int64_t r = 0; r < cnt; ++r) {
+        int64_t i = sel ? sel[r] : r;
+        double* v = out + r * F;
+        int64_t* w = arg + r * F;
+        for (int f = 0; f < F; ++f) { v[f] = 0.0; w[f] = -1; }
+        for (int64_t e = rowptr[i]; e < rowptr[i + 1]; ++e) {
+            int64_t j = colidx[e];
+            for (int f = 0; f < F; ++f) {
+                double x = ld(X, dtype, j * F + f);
+                int better = op == 0 ? x < v[f] : x > v[f];
+                if (w[f] < 0 || better) { v[f] = x; w[f] = e; }
+            }
+        }
+    }
+    return 0;
+}
+
+/*
+ * Backward of L = sum(out * dout). out[i,f] = X[colidx[arg[i,f]], f], so each
+ * (i, f) with a winner passes dout[i,f] to feature f of the winning edge's
+ * source: dX[j,f] = sum of dout[i,f] over those (i, f). `arg` is the
+ * forward's winner array over all n rows; an entry that is neither -1 nor an
+ * edge of its own row is rejected (return 1).
+ */
+int oracle_reduce_bwd(int64_t n, const int64_t* rowptr, const int32_t* colidx, int F, int dtype,
+                      const int64_t* arg, const void* dout, double* dX)
+{
+    int rc = check_csr(n, rowptr, colidx);
+    if (rc) return rc;
+    if (F < 1) return 1;
+    for (int64_t k = 0; k < n * F; ++k) dX[k] = 0.0;
+    for (int64_t i = 0; i < n; ++i)
+        for (int f = 0; f < F; ++f) {
+            int64_t e = arg[i * F + f];
+            if (e < 0) continue;
+            if (e < rowptr[i] || e >= rowptr[i + 1]) return 1;
+            dX[(int64_t)colidx[e] * F + f] += ld(dout, dtype, i * F + f);
+        }
     return 0;
 }

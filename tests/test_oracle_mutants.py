@@ -2,8 +2,10 @@
 
 Each mutant is oracle.c with one plausible error: a dropped term or scale, a
 wrong sign, a transposed operand or index, a wrong LeakyReLU branch, a wrong
-empty-row convention. It is compiled into a temporary directory and run
-through the pin tests of test_oracle.py; every mutant must fail at least one.
+empty-row convention, a wrong tie rule or gradient route of the min/max
+aggregation. It is compiled into a temporary directory and run
+through the pin tests of test_oracle.py and test_oracle_reduce.py; every
+mutant must fail at least one.
 The oracle under test/oracle.c itself is never modified.
 """
 import importlib.util
@@ -13,6 +15,7 @@ import subprocess
 import pytest
 
 from tests import test_oracle as T
+from tests import test_oracle_reduce as TR
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 SRC = os.path.join(ROOT, "oracle", "oracle.c")
@@ -56,6 +59,20 @@ MUTANTS = [
      "g[d] += dE[e * H + h] * lrelu_grad(z, slope);\n"),
     ("transposed CSR stores rows for edge ids", "eid[fill[colidx[e]]++] = e;",
      "eid[fill[colidx[e]]++] = e > 0 ? e - 1 : e;"),
+    ("reduction ties go to the last edge", "int better = op == 0 ? x < v[f] : x > v[f];",
+     "int better = op == 0 ? x <= v[f] : x >= v[f];"),
+    ("max uses the min comparison", "int better = op == 0 ? x < v[f] : x > v[f];",
+     "int better = x < v[f];"),
+    ("empty reduction row gives +inf", "{ v[f] = 0.0; w[f] = -1; }",
+     "{ v[f] = INFINITY; w[f] = -1; }"),
+    ("first edge not taken unconditionally", "if (w[f] < 0 || better) { v[f] = x; w[f] = e; }",
+     "if (better) { v[f] = x; w[f] = e; }"),
+    ("reduction gradient routed to the destination",
+     "dX[(int64_t)colidx[e] * F + f] += ld(dout, dtype, i * F + f);",
+     "dX[i * F + f] += ld(dout, dtype, i * F + f);"),
+    ("reduction gradient reads the source's dout",
+     "dX[(int64_t)colidx[e] * F + f] += ld(dout, dtype, i * F + f);",
+     "dX[(int64_t)colidx[e] * F + f] += ld(dout, dtype, (int64_t)colidx[e] * F + f);"),
 ]
 
 # pins run against every mutant: (test function, keyword arguments)
@@ -69,6 +86,11 @@ PINS = [
     (T.test_gt_backward_finite_differences, {}),
     (T.test_gat_backward_finite_differences, {}),
     (T.test_empty_rows, {}),
+    (TR.test_reduce_golden_ties, {"op": "min"}),
+    (TR.test_reduce_golden_ties, {"op": "max"}),
+    (TR.test_reduce_matches_numpy_first_occurrence, {"op": "min", "dtype": "f64"}),
+    (TR.test_reduce_matches_numpy_first_occurrence, {"op": "max", "dtype": "f64"}),
+    (TR.test_reduce_backward_matches_dense_autograd, {"op": "min"}),
 ]
 
 
