@@ -39,12 +39,19 @@ KERNEL_SOURCES = {
     "gather": [_CSRC + f for f in ("device.hpp", "gather.hpp", "launch.hpp", "launch_gt.hip",
                                    "launch_gat.hip")],
     "tiles": [_CSRC + f for f in ("device.hpp", "blocksparse.hpp", "launch.hpp", "launch_bs.hip")],
+    "reduce": [_CSRC + f for f in ("device.hpp", "reduce.hpp", "launch.hpp", "launch_reduce.hip")],
 }
+
+
+def kernel_family(kernel: str) -> str:
+    if kernel.startswith("gt_bs_"):
+        return "tiles"
+    return "reduce" if kernel.startswith("reduce_") else "gather"
 
 
 def kernel_source_hash(kernel: str) -> str:
     h = hashlib.sha256()
-    for p in KERNEL_SOURCES["tiles" if kernel.startswith("gt_bs_") else "gather"]:
+    for p in KERNEL_SOURCES[kernel_family(kernel)]:
         with open(os.path.join(ROOT, p), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -109,6 +116,12 @@ def algorithmic_bytes(kernel: str, n: int, e: int, H: int, D: int, b: int,
         "gat_bwd_rows": (R + 4, 4 * R + 12 * H + 8),
         # Xs_i, dO_i, (lse_i, Delta_i), rowidx per edge; Xt_j read, dXt_j written
         "gat_bwd_cols": (2 * R + 8 * H + 4, 2 * R + 8),
+        # min/max aggregation (H = 1, D = F): X_j and colidx per edge; out_i and
+        # the int32 winners arg_i written per node
+        "reduce_fwd_rows": (R + 4, R + 4 * D),
+        # arg_i, rowidx and edge id per edge; dO_i read once (where its winners
+        # are) and dX_j written per node
+        "reduce_bwd_cols": (4 * D + 8, 2 * R),
     }.get(kernel)
     if model is None:
         return None
@@ -138,13 +151,20 @@ def cpu_baseline(w, seconds: float):
     import oracle
     spec = w["spec"]
     rp, ci = w["rowptr"], w["colidx"]
+    n = rp.size - 1
 
     def run(r):
         sub = rp.copy()
         sub[r + 1:] = rp[r]
         e = int(sub[-1])
         t0 = time.perf_counter()
-        if spec.op == "gt":
+        if spec.op == "reduce":
+            _, arg = oracle.reduce_fwd(sub, ci[:e], w["x"], "min", rows=np.arange(r))
+            if spec.passes == "fwd+bwd":
+                full = np.full((n, spec.dim), -1, dtype=np.int64)
+                full[:r] = arg
+                oracle.reduce_bwd(sub, ci[:e], full, w["dout"])
+        elif spec.op == "gt":
             oracle.gt_fwd(sub, ci[:e], w["q"], w["k"], w["v"], rows=np.arange(r))
             if spec.passes == "fwd+bwd":
                 oracle.gt_bwd(sub, ci[:e], w["q"], w["k"], w["v"], w["dout"],
@@ -156,7 +176,7 @@ def cpu_baseline(w, seconds: float):
                                dst_rows=np.arange(r), src_rows=np.unique(ci[:e]))
         return e, time.perf_counter() - t0
 
-    n = rp.size - 1
+
     r = min(n, 2000)
     e, t = run(r)
     while t < seconds / 8 and r < n:        # grow the probe until it is long enough to scale
@@ -205,15 +225,19 @@ def compare_unfused(spec, g, fused_step, fused_owned, inputs, fused_out, bwd, fu
         return {"skipped": f"estimated unfused peak {est / 2**30:.0f} GiB exceeds the free "
                            f"device memory ({free / 2**30:.0f} GiB)"}
 
+    n_in = 1 if spec.op == "reduce" else 3
+
     def unfused_step():
-        leaves = [t.detach().requires_grad_(bwd) for t in inputs[:3]]
+        leaves = [t.detach().requires_grad_(bwd) for t in inputs[:n_in]]
         dst, src = U.edge_index(g.rowptr, g.colidx)
-        if spec.op == "gt":
+        if spec.op == "reduce":
+            o = U.minmax(dst, src, leaves[0], "min")
+        elif spec.op == "gt":
             o, _ = U.gt(dst, src, *leaves)
         else:
             o, _ = U.gatv2(dst, src, *leaves, 0.2)
         if bwd:
-            o.backward(inputs[3])
+            o.backward(inputs[n_in])
         return o.detach(), [t.grad for t in leaves]
 
     torch.cuda.synchronize()
@@ -307,8 +331,25 @@ def main():
             return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
         return torch.from_numpy(a).to(dev)
 
-    lse = torch.empty(n, H, dtype=torch.float32, device=dev)
-    if spec.op == "gt":
+    lse = torch.empty(n, H, dtype=torch.float32, device=dev) if spec.op != "reduce" else None
+    if spec.op == "reduce":
+        X = todev(w["x"])
+        out = torch.empty_like(X)
+        bwd = spec.passes == "fwd+bwd"
+        arg = torch.empty((n, D), dtype=torch.int32, device=dev) if bwd else None
+        wsf = g.workspace(B.OP_REDUCE_FWD, 1, D, dt)
+        if bwd:
+            dO = todev(w["dout"])
+            dX = torch.empty_like(X)
+            wsb = g.workspace(B.OP_REDUCE_BWD, 1, D, dt)
+        owned = [out, wsf] + ([arg, dX, wsb] if bwd else [])
+        inputs = [X] + ([dO] if bwd else [])
+
+        def step():
+            B.reduce_fwd(g.plan, g.rowptr, g.colidx, X, "min", out, arg, wsf)
+            if bwd:
+                B.reduce_bwd(g.plan, g.rowptr, g.colidx, arg, dO, dX, wsb)
+    elif spec.op == "gt":
         Q, K, V = todev(w["q"]), todev(w["k"]), todev(w["v"])
         out = torch.empty_like(Q)
         wsf = g.workspace(B.OP_GT_FWD, H, D, dt)

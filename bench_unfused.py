@@ -1,4 +1,5 @@
-"""Unfused comparison formulation of the two attention layers, in plain PyTorch.
+"""Unfused comparison formulations, in plain PyTorch: the two attention layers
+and min/max aggregation.
 
 This is the baseline that ``bench.py --compare-unfused`` times and measures
 the peak memory of, beside the fused library. It is the message-passing form
@@ -64,3 +65,14 @@ def gatv2(dst, src, x_dst, x_nbr, a, negative_slope=0.2):
     out = torch.zeros((n, H, D), dtype=acc, device=x_dst.device)
     out = out.index_add(0, dst, alpha[..., None] * x_nbr[src])
     return out.to(x_dst.dtype), lse
+
+
+def minmax(dst, src, x, op="min"):
+    """Min or max aggregation: gather x[src] per edge, scatter-reduce into the
+    destinations (rows without edges keep 0). torch's backward of the
+    scatter reduction splits a gradient evenly between tied edges; with
+    distinct values it is the winner's alone, as in the fused library."""
+    n, F = x.shape
+    out = torch.zeros((n, F), dtype=x.dtype, device=x.device)
+    return out.scatter_reduce(0, dst[:, None].expand(-1, F), x[src],
+                              "amin" if op == "min" else "amax", include_self=False)

@@ -74,8 +74,12 @@ typedef enum sgat_op {
     SGAT_OP_GT_FWD = 0,
     SGAT_OP_GT_BWD = 1,
     SGAT_OP_GAT_FWD = 2,
-    SGAT_OP_GAT_BWD = 3
+    SGAT_OP_GAT_BWD = 3,
+    SGAT_OP_REDUCE_FWD = 4,   /* workspace queries pass H = 1 and D = F */
+    SGAT_OP_REDUCE_BWD = 5
 } sgat_op;
+
+typedef enum sgat_reduce { SGAT_REDUCE_MIN = 0, SGAT_REDUCE_MAX = 1 } sgat_reduce;
 
 /* Preprocessing options (0 selects the default for every field). */
 typedef struct sgat_plan_opts {
@@ -152,7 +156,8 @@ typedef struct sgat_plan sgat_plan;
 
 /* ---- plan: preprocessing on the host (integer only, deterministic) -------- */
 
-/* Validate the CSR (n >= 0, nnz >= 0, n < 2^31, rowptr[0] = 0, rowptr monotone,
+/* Validate the CSR (n >= 0, nnz >= 0, n < 2^31, nnz < 2^31 (edge positions
+ * are stored as int32), rowptr[0] = 0, rowptr monotone,
  * rowptr[n] = nnz, 0 <= colidx < n) and build the plan: degree-binned work
  * lists for the CSR and for its transpose, with heavy rows and heavy sources
  * split into chunks (degree-aware parallelisation of high-degree nodes: Yandex
@@ -183,7 +188,8 @@ int sgat_plan_export(const sgat_plan* plan, int array_id, void* host_dst, size_t
 /* Frees the host side of the plan (never the caller's device buffer). NULL is a no-op. */
 void sgat_plan_destroy(sgat_plan* plan);
 
-/* Workspace bytes that `op` needs for this plan, H, D and dtype. */
+/* Workspace bytes that `op` needs for this plan, H, D and dtype (for the
+ * reduction ops H = 1 and D = F). */
 int sgat_workspace_bytes(const sgat_plan* plan, int op, int H, int D, int dtype, size_t* bytes);
 
 /* ---- Graph Transformer: score s_ij = <Q_i, K_j> / sqrt(D) ------------------- */
@@ -232,6 +238,36 @@ int gat_bwd(const sgat_plan* plan, int64_t n, int64_t nnz,
             const float* a, float negative_slope,
             const void* out, const float* lse, const void* dout,
             void* dx_dst, void* dx_nbr, float* da, void* ws, size_t ws_bytes, void* stream);
+
+/* ---- min/max aggregation: out[i,f] = min or max over edges j -> i of X[j,f] -- */
+
+/* Reduction-based aggregation (IO-aware layers abstract: the reduction kernel
+ * family; Yandex Research blog, paragraph on aggregation layers: min/max
+ * pooling, with degree-aware parallelisation of high-degree nodes). The
+ * message of edge j -> i is the source row X[j]; op = SGAT_REDUCE_MIN or
+ * SGAT_REDUCE_MAX. X and out: [n, F] row-major, fp32 or bf16, 16-byte aligned;
+ * F a multiple of 4 (fp32) or 8 (bf16), at most 2048. Comparisons are exact,
+ * so out holds the input bits of the winning edge: the first CSR position of
+ * the row attaining the extreme (ties go to the lowest position). arg, if not
+ * NULL: int32 [n, F], 16-byte aligned, receives that position, -1 for empty
+ * rows (whose out is 0). Rows longer than the plan's chunk are split across
+ * wavefronts and their partial winners combined in chunk order. NaN inputs
+ * give unspecified results. */
+int reduce_fwd(const sgat_plan* plan, int64_t n, int64_t nnz,
+               const int64_t* rowptr, const int32_t* colidx,
+               int F, int dtype, int op, const void* X, void* out, int32_t* arg,
+               void* ws, size_t ws_bytes, void* stream);
+
+/* Backward of L = sum(out * dout): dX[j,f] = sum of dout[i,f] over the (i, f)
+ * whose winner arg[i,f] is an edge j -> i. arg is the reduce_fwd output for
+ * this plan and F (its content is not re-checked); dout and dX [n, F] in the
+ * dtype, dX overwritten. Accumulated over the transposed CSR in fixed order
+ * (sources with many out-edges split and summed in chunk order), so no
+ * atomics are used. */
+int reduce_bwd(const sgat_plan* plan, int64_t n, int64_t nnz,
+               const int64_t* rowptr, const int32_t* colidx,
+               int F, int dtype, const int32_t* arg, const void* dout, void* dX,
+               void* ws, size_t ws_bytes, void* stream);
 
 /* ---- diagnostics ----------------------------------------------------------- */
 

@@ -468,12 +468,23 @@ int oracle_reduce_bwd(int64_t n, const int64_t* rowptr, const int32_t* colidx, i
     if (rc) return rc;
     if (F < 1) return 1;
     for (int64_t k = 0; k < n * F; ++k) dX[k] = 0.0;
-    for (int64_t i = 0; i < n; ++i)
-        for (int f = 0; f < F; ++f) {
-            int64_t e = arg[i * F + f];
-            if (e < 0) continue;
-            if (e < rowptr[i] || e >= rowptr[i + 1]) return 1;
-            dX[(int64_t)colidx[e] * F + f] += ld(dout, dtype, i * F + f);
-        }
-    return 0;
+    /* Threads own disjoint feature blocks; each sums its entries in row order. */
+    const int FB = 16;
+    int bad = 0;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int f0 = 0; f0 < F; f0 += FB) {
+        int f1 = f0 + FB < F ? f0 + FB : F;
+        for (int64_t i = 0; i < n; ++i)
+            for (int f = f0; f < f1; ++f) {
+                int64_t e = arg[i * F + f];
+                if (e < 0) continue;
+                if (e < rowptr[i] || e >= rowptr[i + 1]) {
+#pragma omp atomic write
+                    bad = 1;
+                    continue;
+                }
+                dX[(int64_t)colidx[e] * F + f] += ld(dout, dtype, i * F + f);
+            }
+    }
+    return bad;
 }

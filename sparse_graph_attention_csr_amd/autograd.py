@@ -4,8 +4,11 @@ fused AT-GNN kernels are used from PyTorch).
 ``gt_attention`` and ``gatv2_attention`` are differentiable functions whose
 forward and backward are the library's gt_fwd/gt_bwd and gat_fwd/gat_bwd;
 ``GraphTransformerAttention`` and ``GATv2Attention`` are layers that add the
-input projections (plain torch Linear layers) around them. Only argument
-marshalling happens here: every step of the attention runs in libsgattn.so.
+input projections (plain torch Linear layers) around them.
+``minmax_aggregate`` / ``MinMaxAggregation`` are min or max pooling over the
+in-neighbours (reduce_fwd / reduce_bwd; IO-aware layers abstract: the
+reduction-based aggregation family). Only argument marshalling happens here:
+every step runs in libsgattn.so.
 """
 from __future__ import annotations
 
@@ -125,3 +128,52 @@ class GATv2Attention(torch.nn.Module):
         out = gatv2_attention(graph, self.dst(x).view(shape), self.nbr(x).view(shape), self.a,
                               self.negative_slope)
         return out.reshape(n, self.heads * self.head_dim)
+
+
+class _ReduceFunction(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, graph, x, op):
+        x = x.contiguous()
+        n, F = x.shape
+        out = torch.empty_like(x)
+        arg = (torch.empty((n, F), dtype=torch.int32, device=x.device)
+               if ctx.needs_input_grad[1] else None)
+        B.reduce_fwd(graph.plan, graph.rowptr, graph.colidx, x, op, out, arg,
+                     graph.workspace(B.OP_REDUCE_FWD, 1, F, _dt(x)))
+        ctx.graph = graph
+        if arg is not None:
+            ctx.save_for_backward(arg)
+        return out
+
+    @staticmethod
+    def backward(ctx, dout):
+        (arg,) = ctx.saved_tensors
+        g = ctx.graph
+        dout = dout.contiguous()
+        n, F = dout.shape
+        dx = torch.empty_like(dout)
+        B.reduce_bwd(g.plan, g.rowptr, g.colidx, arg, dout, dx,
+                     g.workspace(B.OP_REDUCE_BWD, 1, F, _dt(dout)))
+        return None, dx, None
+
+
+def minmax_aggregate(graph: B.DeviceGraph, x, op: str = "min"):
+    """out[i] = elementwise min (or max) of x[j] over the in-neighbours j of i;
+    x [N, F] fp32 or bf16; rows without in-edges give 0. The gradient goes to
+    the winning edge's source (the first edge of the row on ties)."""
+    if op not in B.REDUCE_OPS:
+        raise ValueError("op must be 'min' or 'max'")
+    return _ReduceFunction.apply(graph, x, B.REDUCE_OPS[op])
+
+
+class MinMaxAggregation(torch.nn.Module):
+    """Min or max pooling over the in-neighbours of every node."""
+
+    def __init__(self, op: str = "min"):
+        super().__init__()
+        if op not in B.REDUCE_OPS:
+            raise ValueError("op must be 'min' or 'max'")
+        self.op = op
+
+    def forward(self, graph: B.DeviceGraph, x: torch.Tensor) -> torch.Tensor:
+        return minmax_aggregate(graph, x, self.op)

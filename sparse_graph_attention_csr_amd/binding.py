@@ -2,7 +2,8 @@
 
 Argument marshalling only: every step of the computation runs in the HIP
 library. torch tensors supply device memory and the stream; the functions
-``gt_fwd``, ``gt_bwd``, ``gat_fwd`` and ``gat_bwd`` mirror the C entry points
+``gt_fwd``, ``gt_bwd``, ``gat_fwd``, ``gat_bwd``, ``reduce_fwd`` and
+``reduce_bwd`` mirror the C entry points
 of the same names in include/sgattn.h, and raise :class:`SgatError` on a
 non-zero status. There is no fallback: if the library is missing, loading it
 raises.
@@ -17,7 +18,9 @@ import numpy as np
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsgattn.so")
 
 F32, BF16 = 0, 1
-OP_GT_FWD, OP_GT_BWD, OP_GAT_FWD, OP_GAT_BWD = 0, 1, 2, 3
+OP_GT_FWD, OP_GT_BWD, OP_GAT_FWD, OP_GAT_BWD, OP_REDUCE_FWD, OP_REDUCE_BWD = range(6)
+REDUCE_MIN, REDUCE_MAX = 0, 1
+REDUCE_OPS = {"min": REDUCE_MIN, "max": REDUCE_MAX}
 
 (ARR_ROW_ITEMS, ARR_ROW_SPLITS, ARR_COLPTR, ARR_ROWIDX, ARR_COL_ITEMS, ARR_COL_SPLITS,
  ARR_TILE_ROWPTR, ARR_TILE_COL, ARR_TILE_MASK, ARR_RES_ROWPTR, ARR_RES_COLIDX,
@@ -85,6 +88,9 @@ _SIGS = {
                        _vp, _sz, _vp]),
     "gat_bwd": (_i32, [_vp, _i64, _i64, _vp, _vp, _i32, _i32, _i32, _vp, _vp, _vp, _f, _vp, _vp,
                        _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "reduce_fwd": (_i32, [_vp, _i64, _i64, _vp, _vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _sz,
+                          _vp]),
+    "reduce_bwd": (_i32, [_vp, _i64, _i64, _vp, _vp, _i32, _i32, _vp, _vp, _vp, _vp, _sz, _vp]),
     "sgat_status_string": (ctypes.c_char_p, [_i32]),
     "sgat_trace_enable": (_i32, [_i32]),
     "sgat_trace_clear": (_i32, []),
@@ -270,6 +276,30 @@ def gat_bwd(plan: Plan, rowptr, colidx, x_dst, x_nbr, a, negative_slope, out, ls
         _ptr(x_dst), _ptr(x_nbr), _ptr(a), float(negative_slope), _ptr(out), _ptr(lse),
         _ptr(dout), _ptr(dx_dst), _ptr(dx_nbr), _ptr(da), _ptr(ws),
         0 if ws is None else ws.numel(), _stream(stream)))
+
+
+def _shape2(t):
+    if t.dim() != 2:
+        raise ValueError("aggregation tensors are [N, F]")
+    return t.shape
+
+
+def reduce_fwd(plan: Plan, rowptr, colidx, x, op, out, arg, ws, stream=None):
+    """op: REDUCE_MIN / REDUCE_MAX (or "min" / "max"); arg may be None."""
+    n, F = _shape2(x)
+    op = REDUCE_OPS.get(op, op)
+    _check("reduce_fwd", lib().reduce_fwd(
+        plan.handle, plan.n, plan.nnz, _ptr(rowptr), _ptr(colidx), F, _dtype_code(x), int(op),
+        _ptr(x), _ptr(out), _ptr(arg), _ptr(ws), 0 if ws is None else ws.numel(),
+        _stream(stream)))
+
+
+def reduce_bwd(plan: Plan, rowptr, colidx, arg, dout, dx, ws, stream=None):
+    n, F = _shape2(dout)
+    _check("reduce_bwd", lib().reduce_bwd(
+        plan.handle, plan.n, plan.nnz, _ptr(rowptr), _ptr(colidx), F, _dtype_code(dout),
+        _ptr(arg), _ptr(dout), _ptr(dx), _ptr(ws), 0 if ws is None else ws.numel(),
+        _stream(stream)))
 
 
 # ---------------------------------------------------------------------------

@@ -21,7 +21,8 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libsgattn.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["plan.cpp", "api.cpp", "launch_gt.hip", "launch_gat.hip", "launch_bs.hip"]
+SOURCES = ["plan.cpp", "api.cpp", "launch_gt.hip", "launch_gat.hip", "launch_bs.hip",
+           "launch_reduce.hip"]
 
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++20", "-fPIC", "-Wall", "-Wno-unused-result",

@@ -88,6 +88,17 @@ int check_common(const sgat_plan* plan, int64_t n, int64_t nnz, const int64_t* r
     return SGAT_OK;
 }
 
+int check_reduce(const sgat_plan* plan, int64_t n, int64_t nnz, const int64_t* rowptr,
+                 const int32_t* colidx, int F, int dt)
+{
+    if (!plan) return SGAT_INVALID_ARGUMENT;
+    if (!reduce_supported(dt, F)) return SGAT_INVALID_ARGUMENT;
+    if (n != plan->p.n || nnz != plan->p.nnz) return SGAT_PLAN_MISMATCH;
+    if (!plan->p.uploaded) return SGAT_NOT_UPLOADED;
+    if (!rowptr || (nnz > 0 && !colidx)) return SGAT_INVALID_ARGUMENT;
+    return SGAT_OK;
+}
+
 int check_tensor(const void* p, int64_t n)
 {
     if (n == 0) return SGAT_OK;
@@ -123,6 +134,13 @@ Layout ws_layout(const Plan& p, int op, int H, int D)
         sz[1] = static_cast<size_t>(p.row_slots) * HD * 4;          // dXs partials
         sz[2] = static_cast<size_t>(p.col_slots) * HD * 4;          // dXt partials
         sz[4] = static_cast<size_t>(gat_bwd_row_blocks(p)) * HD * 4; // da partials
+        break;
+    case SGAT_OP_REDUCE_FWD:                                        // H = 1, D = F
+        sz[0] = static_cast<size_t>(p.row_slots) * HD * 4;          // partial values
+        sz[1] = static_cast<size_t>(p.row_slots) * HD * 4;          // partial winners
+        break;
+    case SGAT_OP_REDUCE_BWD:
+        sz[0] = static_cast<size_t>(p.col_slots) * HD * 4;          // dX partials
         break;
     default:
         break;
@@ -193,9 +211,13 @@ int sgat_plan_upload(sgat_plan* plan, void* dev_buf, size_t bytes, void* stream)
 int sgat_workspace_bytes(const sgat_plan* plan, int op, int H, int D, int dtype, size_t* bytes)
 {
     if (!plan || !bytes) return SGAT_INVALID_ARGUMENT;
-    if (op < SGAT_OP_GT_FWD || op > SGAT_OP_GAT_BWD) return SGAT_INVALID_ARGUMENT;
-    if (H < 1 || H > 16 || (D != 32 && D != 64 && D != 128)) return SGAT_INVALID_ARGUMENT;
-    if (dtype != SGAT_F32 && dtype != SGAT_BF16) return SGAT_INVALID_ARGUMENT;
+    if (op < SGAT_OP_GT_FWD || op > SGAT_OP_REDUCE_BWD) return SGAT_INVALID_ARGUMENT;
+    if (op >= SGAT_OP_REDUCE_FWD) {
+        if (H != 1 || !reduce_supported(dtype, D)) return SGAT_INVALID_ARGUMENT;
+    } else {
+        if (H < 1 || H > 16 || (D != 32 && D != 64 && D != 128)) return SGAT_INVALID_ARGUMENT;
+        if (dtype != SGAT_F32 && dtype != SGAT_BF16) return SGAT_INVALID_ARGUMENT;
+    }
     *bytes = ws_layout(plan->p, op, H, D).total;
     return SGAT_OK;
 }
@@ -287,6 +309,38 @@ int gat_bwd(const sgat_plan* plan, int64_t n, int64_t nnz, const int64_t* rowptr
             at<float>(ws, L.off[4]), nullptr};
     return launch_gat_bwd(plan->p, H, D, dtype, colidx, x_dst, x_nbr, a, negative_slope, out, lse,
                           dout, dx_dst, dx_nbr, da, w, static_cast<hipStream_t>(stream));
+}
+
+int reduce_fwd(const sgat_plan* plan, int64_t n, int64_t nnz, const int64_t* rowptr,
+               const int32_t* colidx, int F, int dtype, int op, const void* X, void* out,
+               int32_t* arg, void* ws, size_t ws_bytes, void* stream)
+{
+    int rc = check_reduce(plan, n, nnz, rowptr, colidx, F, dtype);
+    if (rc) return rc;
+    if (op != SGAT_REDUCE_MIN && op != SGAT_REDUCE_MAX) return SGAT_INVALID_ARGUMENT;
+    for (const void* t : {X, static_cast<const void*>(out)})
+        if ((rc = check_tensor(t, n))) return rc;
+    if (arg && !aligned(arg, 16)) return SGAT_INVALID_ARGUMENT;
+    Layout L;
+    if ((rc = check_ws(plan->p, SGAT_OP_REDUCE_FWD, 1, F, ws, ws_bytes, L))) return rc;
+    if (n == 0) return SGAT_OK;
+    return launch_reduce_fwd(plan->p, F, dtype, op, colidx, X, out, arg, at<float>(ws, L.off[0]),
+                             at<int32_t>(ws, L.off[1]), static_cast<hipStream_t>(stream));
+}
+
+int reduce_bwd(const sgat_plan* plan, int64_t n, int64_t nnz, const int64_t* rowptr,
+               const int32_t* colidx, int F, int dtype, const int32_t* arg, const void* dout,
+               void* dX, void* ws, size_t ws_bytes, void* stream)
+{
+    int rc = check_reduce(plan, n, nnz, rowptr, colidx, F, dtype);
+    if (rc) return rc;
+    for (const void* t : {static_cast<const void*>(arg), dout, static_cast<const void*>(dX)})
+        if ((rc = check_tensor(t, n))) return rc;
+    Layout L;
+    if ((rc = check_ws(plan->p, SGAT_OP_REDUCE_BWD, 1, F, ws, ws_bytes, L))) return rc;
+    if (n == 0) return SGAT_OK;
+    return launch_reduce_bwd(plan->p, F, dtype, arg, dout, dX, at<float>(ws, L.off[0]),
+                             static_cast<hipStream_t>(stream));
 }
 
 int sgat_trace_enable(int on)

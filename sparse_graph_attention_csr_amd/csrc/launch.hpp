@@ -58,6 +58,18 @@ int launch_gt_bs_bwd(const Plan& p, int H, int D, const void* Q, const void* K, 
                      const void* O, const float* lse, const void* dO, void* dQ, void* dK, void* dV,
                      void* stats, hipStream_t s);
 
+// Min/max aggregation: lanes per edge and fragments per lane for F features.
+constexpr int kReduceMaxF = 2048;
+struct ReduceGeom {
+    int lpe, nf;
+};
+ReduceGeom reduce_geometry(int dt, int F);
+bool reduce_supported(int dt, int F);
+int launch_reduce_fwd(const Plan& p, int F, int dt, int op, const int32_t* colidx, const void* X,
+                      void* out, int32_t* arg, float* part_val, int32_t* part_pos, hipStream_t s);
+int launch_reduce_bwd(const Plan& p, int F, int dt, const int32_t* arg, const void* dO, void* dX,
+                      float* part, hipStream_t s);
+
 // da = 0 (the empty sum, for a graph without nodes), by a kernel.
 int launch_da_zero(float* da, int HD, hipStream_t s);
 

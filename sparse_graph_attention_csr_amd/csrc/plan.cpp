@@ -21,7 +21,7 @@ namespace sgat {
 
 int validate_csr(int64_t n, int64_t nnz, const int64_t* rowptr, const int32_t* colidx)
 {
-    if (n < 0 || nnz < 0 || n > INT32_MAX) return SGAT_INVALID_ARGUMENT;
+    if (n < 0 || nnz < 0 || n > INT32_MAX || nnz > INT32_MAX) return SGAT_INVALID_ARGUMENT;
     if (!rowptr || (nnz > 0 && !colidx)) return SGAT_INVALID_ARGUMENT;
     if (rowptr[0] != 0) return SGAT_INVALID_CSR;
     for (int64_t i = 0; i < n; ++i)

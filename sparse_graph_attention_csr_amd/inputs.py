@@ -266,7 +266,7 @@ def hub_pairs(n: int, mean: float, n_hubs: int, hub_in: int, hub_out: int,
 @dataclasses.dataclass(frozen=True)
 class Workload:
     name: str
-    op: str            # "gt" or "gat"
+    op: str            # "gt", "gat" or "reduce" (min aggregation; heads = 1, dim = F)
     passes: str        # "fwd" or "fwd+bwd"
     n: int
     heads: int
@@ -291,6 +291,9 @@ WORKLOADS = {
     "gt_hubs2m_h8d64_bf16": Workload(
         "gt_hubs2m_h8d64_bf16", "gt", "fwd+bwd", 2_000_000, 8, 64, BF16,
         "Erdos-Renyi mean in-degree 10 plus 64 hubs (200000 in-edges, 50000 out-edges each), plus self-loops"),
+    "minagg_powerlaw500k_d512_f32": Workload(
+        "minagg_powerlaw500k_d512_f32", "reduce", "fwd+bwd", 500_000, 1, 512, F32,
+        "Chung-Lu power law, exponent 2.3, mean in-degree 20, plus self-loops"),
 }
 
 # The workload order used when a list of all of them is wanted.
@@ -306,7 +309,7 @@ def make_graph(name: str, seed: int = 0):
         dst, src = er_pairs(w.n, 8 * w.n, rng)
     elif name == "gt_powerlaw200k_h4d128_bf16":
         dst, src = chung_lu_pairs(w.n, 2.1, 15.0, 20_000, rng)
-    elif name == "gatv2_powerlaw500k_h2d64_bf16":
+    elif name in ("gatv2_powerlaw500k_h2d64_bf16", "minagg_powerlaw500k_d512_f32"):
         dst, src = chung_lu_pairs(w.n, 2.3, 20.0, None, rng)
     elif name == "gt_community262k_h4d128_bf16":
         dst, src = community_pairs(4096, 64, 0.5, 2, rng)
@@ -325,12 +328,15 @@ def make_tensors(name: str, seed: int = 0, with_grad: bool = True) -> dict:
     Graph Transformer: q, k, v (and dout), each [N, H, D].
     GATv2: xs (indexed by destination), xt (gathered by neighbour), a [H, D]
     in fp32 drawn N(0, 1/D), and dout.
+    Min aggregation: x (and dout), each [N, F].
     """
     w = WORKLOADS[name]
     st = _streams(seed)
-    shape = (w.n, w.heads, w.dim)
+    shape = (w.n, w.heads, w.dim) if w.op != "reduce" else (w.n, w.dim)
     t = {}
-    if w.op == "gt":
+    if w.op == "reduce":
+        t["x"] = normal_tensor(st["q"], shape, w.dtype)
+    elif w.op == "gt":
         t["q"] = normal_tensor(st["q"], shape, w.dtype)
         t["k"] = normal_tensor(st["k"], shape, w.dtype)
         t["v"] = normal_tensor(st["v"], shape, w.dtype)

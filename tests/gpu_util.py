@@ -103,3 +103,22 @@ class Runner:
         ws = g.workspace(B.OP_GAT_BWD, H, D, B._dtype_code(xs))
         B.gat_bwd(g.plan, g.rowptr, g.colidx, xs, xt, a, slope, out, lse, dout, dxs, dxt, da, ws)
         return dxs, dxt, da
+
+    def reduce_fwd(self, x, op="min", with_arg=True):
+        import torch
+        B, g = self.B, self.g
+        n, F = x.shape
+        out = torch.empty_like(x)
+        arg = torch.empty((n, F), dtype=torch.int32, device=x.device) if with_arg else None
+        ws = g.workspace(B.OP_REDUCE_FWD, 1, F, B._dtype_code(x))
+        B.reduce_fwd(g.plan, g.rowptr, g.colidx, x, op, out, arg, ws)
+        return out, arg
+
+    def reduce_bwd(self, arg, dout):
+        import torch
+        B, g = self.B, self.g
+        n, F = dout.shape
+        dx = torch.empty_like(dout)
+        ws = g.workspace(B.OP_REDUCE_BWD, 1, F, B._dtype_code(dout))
+        B.reduce_bwd(g.plan, g.rowptr, g.colidx, arg, dout, dx, ws)
+        return dx

@@ -129,3 +129,47 @@ def test_trace_api_without_launches():
     B.trace_clear()
     assert B.trace_read() == []
     B.trace_enable(False)
+
+
+def test_reduce_argument_checks(plan):
+    L = B.lib()
+    n, nnz = plan.n, plan.nnz
+
+    def fwd(F=512, dt=1, op=0, h=plan.handle, n_=n, arg=FAKE, x=FAKE):
+        return L.reduce_fwd(h, n_, nnz, FAKE, FAKE, F, dt, op, x, FAKE, arg, FAKE, 1 << 30, None)
+
+    assert fwd(h=None) == 1
+    assert fwd(F=0) == 1
+    assert fwd(F=12) == 1                 # bf16 rows must be whole 16-byte fragments
+    assert fwd(F=12, dt=0) == 6           # fp32: multiple of 4 is fine (then: not uploaded)
+    assert fwd(F=4096) == 1               # above the maximum
+    assert fwd(dt=2) == 1
+    assert fwd(n_=n + 1) == 4
+    assert fwd() == 6                     # not uploaded
+    assert L.reduce_bwd(plan.handle, n, nnz, FAKE, FAKE, 64, 0, FAKE, FAKE, FAKE, FAKE, 1 << 30,
+                        None) == 6
+    assert L.reduce_bwd(plan.handle, n, nnz, FAKE, FAKE, 66, 0, FAKE, FAKE, FAKE, FAKE, 1 << 30,
+                        None) == 1
+
+
+def test_reduce_workspace_bytes(plan):
+    s = plan.stats()
+    F = 512
+    fwd = plan.workspace_bytes(B.OP_REDUCE_FWD, 1, F, B.BF16)
+    assert fwd == 2 * (-(-s["row_slots"] * F * 4 // 256) * 256)
+    bwd = plan.workspace_bytes(B.OP_REDUCE_BWD, 1, F, B.F32)
+    assert bwd == -(-s["col_slots"] * F * 4 // 256) * 256
+    with pytest.raises(B.SgatError):
+        plan.workspace_bytes(B.OP_REDUCE_FWD, 2, F, B.BF16)      # H must be 1
+    with pytest.raises(B.SgatError):
+        plan.workspace_bytes(B.OP_REDUCE_FWD, 1, 4100, B.F32)
+
+
+def test_plan_rejects_nnz_beyond_int32():
+    """Edge positions are int32: nnz >= 2^31 is refused before any array is read."""
+    rp = np.array([0, 1 << 31], dtype=np.int64)
+    ci = np.zeros(1, dtype=np.int32)
+    out = ctypes.c_void_p()
+    assert B.lib().sgat_plan_create(1, 1 << 31, rp.ctypes.data, ci.ctypes.data, None,
+                                    ctypes.byref(out)) == 1
+    assert not out.value

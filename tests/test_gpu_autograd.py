@@ -131,3 +131,26 @@ def test_gt_attention_tiles_bf16():
     rq, rk, rv = oracle.gt_bwd(rp, ci, q, k, v, do)
     for t, r in ((Q, rq), (K, rk), (V, rv)):
         assert rel_err(t.grad.float().cpu().numpy(), r) <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("op", ["min", "max"])
+def test_minmax_aggregate_gradients(op):
+    import torch
+    from sparse_graph_attention_csr_amd import binding as B
+    from sparse_graph_attention_csr_amd.autograd import MinMaxAggregation
+    note(f"autograd {op} aggregation")
+    rp, ci = graph(9)
+    n, F = rp.size - 1, 96
+    rng = np.random.default_rng(10)
+    x = rng.standard_normal((n, F)).astype(np.float32)
+    do = rng.standard_normal((n, F)).astype(np.float32)
+    g = B.DeviceGraph(rp, ci, chunk=64)
+    X = torch.tensor(x, device="cuda", requires_grad=True)
+    out = MinMaxAggregation(op)(g, X)
+    (out * torch.tensor(do, device="cuda")).sum().backward()
+    ro, ra = oracle.reduce_fwd(rp, ci, x, op)
+    assert np.array_equal(out.detach().cpu().numpy().astype(np.float64), ro)
+    assert rel_err(X.grad.cpu().numpy(), oracle.reduce_bwd(rp, ci, ra, do)) <= 1e-6
+    with torch.no_grad():                   # no winners kept when no gradient is needed
+        o2 = MinMaxAggregation(op)(g, X)
+    assert torch.equal(o2, out.detach())

@@ -1,5 +1,5 @@
-"""The unfused comparison formulation computes the same function as the fused
-library: run on the CPU in fp64, its forward and its torch.autograd backward
+"""The unfused comparison formulations compute the same functions as the fused
+library: run on the CPU in fp64, their forwards and torch.autograd backwards
 match the fp64 oracle (so the latency and peak-memory ratios compare like
 with like). CPU only."""
 import numpy as np
@@ -52,3 +52,22 @@ def test_unfused_gatv2_matches_oracle(oracle_mod):
     np.testing.assert_allclose(out.detach().numpy(), ro, rtol=0, atol=1e-12)
     for t, r in zip((Xs, Xt, A), oracle_mod.gat_bwd(rp, ci, xs, xt, a, do, 0.2)):
         np.testing.assert_allclose(t.grad.numpy(), r, rtol=0, atol=1e-10)
+
+
+@pytest.mark.parametrize("op", ["min", "max"])
+def test_unfused_minmax_matches_oracle(oracle_mod, op):
+    rp, ci = graph(4)
+    n, F = rp.size - 1, 9
+    for i in range(n):                       # distinct sources per row: no ties
+        row = ci[rp[i]:rp[i + 1]]
+        ci[rp[i]:rp[i + 1]] = np.random.default_rng(i).permutation(n)[:row.size]
+    rng = np.random.default_rng(14)
+    x, do = rng.standard_normal((n, F)), rng.standard_normal((n, F))
+    dst, src = U.edge_index(torch.from_numpy(rp), torch.from_numpy(ci))
+    X = t64(x)
+    out = U.minmax(dst, src, X, op)
+    (out * t64(do, False)).sum().backward()
+    ro, ra = oracle_mod.reduce_fwd(rp, ci, x, op)
+    np.testing.assert_array_equal(out.detach().numpy(), ro)
+    np.testing.assert_allclose(X.grad.numpy(), oracle_mod.reduce_bwd(rp, ci, ra, do), rtol=0,
+                               atol=1e-14)
