@@ -119,9 +119,12 @@ def algorithmic_bytes(kernel: str, n: int, e: int, H: int, D: int, b: int,
         # min/max aggregation (H = 1, D = F): X_j and colidx per edge; out_i and
         # the int32 winners arg_i written per node
         "reduce_fwd_rows": (R + 4, R + 4 * D),
-        # arg_i, rowidx and edge id per edge; dO_i read once (where its winners
-        # are) and dX_j written per node
-        "reduce_bwd_cols": (4 * D + 8, 2 * R),
+        # per node: arg_i and dO_i read, the (feature, dout) pairs written; per
+        # edge: its (start, count) written
+        "reduce_bwd_route": (4, 4 * D + R + D * (4 if b == 2 else 8) + 16),
+        # per edge: rowidx, edge id, (start, count); per node: its pairs read
+        # once (by the edges that won them) and dX_j written
+        "reduce_bwd_gather": (12, D * (4 if b == 2 else 8) + R),
     }.get(kernel)
     if model is None:
         return None

@@ -112,7 +112,7 @@ struct Layout {
 };
 
 // Regions, each 256-byte aligned, in this order.
-Layout ws_layout(const Plan& p, int op, int H, int D)
+Layout ws_layout(const Plan& p, int op, int H, int D, int dt)
 {
     const size_t HD = static_cast<size_t>(H) * D;
     size_t sz[6] = {};
@@ -141,6 +141,8 @@ Layout ws_layout(const Plan& p, int op, int H, int D)
         break;
     case SGAT_OP_REDUCE_BWD:
         sz[0] = static_cast<size_t>(p.col_slots) * HD * 4;          // dX partials
+        sz[1] = static_cast<size_t>(p.nnz) * 4;                     // (start, count) per edge
+        sz[2] = static_cast<size_t>(p.n) * HD * (dt == SGAT_BF16 ? 4 : 8);   // routed pairs
         break;
     default:
         break;
@@ -158,9 +160,10 @@ Layout ws_layout(const Plan& p, int op, int H, int D)
 template <class T>
 T* at(void* ws, size_t off) { return reinterpret_cast<T*>(static_cast<char*>(ws) + off); }
 
-int check_ws(const Plan& p, int op, int H, int D, const void* ws, size_t ws_bytes, Layout& L)
+int check_ws(const Plan& p, int op, int H, int D, int dt, const void* ws, size_t ws_bytes,
+             Layout& L)
 {
-    L = ws_layout(p, op, H, D);
+    L = ws_layout(p, op, H, D, dt);
     if (ws_bytes < L.total) return SGAT_WORKSPACE_TOO_SMALL;
     if (L.total > 0 && (!ws || !aligned(ws, 256))) return SGAT_INVALID_ARGUMENT;
     return SGAT_OK;
@@ -218,7 +221,7 @@ int sgat_workspace_bytes(const sgat_plan* plan, int op, int H, int D, int dtype,
         if (H < 1 || H > 16 || (D != 32 && D != 64 && D != 128)) return SGAT_INVALID_ARGUMENT;
         if (dtype != SGAT_F32 && dtype != SGAT_BF16) return SGAT_INVALID_ARGUMENT;
     }
-    *bytes = ws_layout(plan->p, op, H, D).total;
+    *bytes = ws_layout(plan->p, op, H, D, dtype).total;
     return SGAT_OK;
 }
 
@@ -235,7 +238,7 @@ int gt_fwd(const sgat_plan* plan, int64_t n, int64_t nnz, const int64_t* rowptr,
     if (use_tiles != 0 && use_tiles != 1) return SGAT_INVALID_ARGUMENT;
     if (use_tiles && (!plan->p.block_sparse || dtype != SGAT_BF16)) return SGAT_UNSUPPORTED;
     Layout L;
-    if ((rc = check_ws(plan->p, SGAT_OP_GT_FWD, H, D, ws, ws_bytes, L))) return rc;
+    if ((rc = check_ws(plan->p, SGAT_OP_GT_FWD, H, D, dtype, ws, ws_bytes, L))) return rc;
     if (n == 0) return SGAT_OK;
     if (use_tiles)
         return launch_gt_bs_fwd(plan->p, H, D, Q, K, V, out, lse, static_cast<hipStream_t>(stream));
@@ -258,7 +261,7 @@ int gt_bwd(const sgat_plan* plan, int64_t n, int64_t nnz, const int64_t* rowptr,
     if (use_tiles != 0 && use_tiles != 1) return SGAT_INVALID_ARGUMENT;
     if (use_tiles && (!plan->p.block_sparse || dtype != SGAT_BF16)) return SGAT_UNSUPPORTED;
     Layout L;
-    if ((rc = check_ws(plan->p, SGAT_OP_GT_BWD, H, D, ws, ws_bytes, L))) return rc;
+    if ((rc = check_ws(plan->p, SGAT_OP_GT_BWD, H, D, dtype, ws, ws_bytes, L))) return rc;
     if (n == 0) return SGAT_OK;
     if (use_tiles)
         return launch_gt_bs_bwd(plan->p, H, D, Q, K, V, out, lse, dout, dQ, dK, dV,
@@ -281,7 +284,7 @@ int gat_fwd(const sgat_plan* plan, int64_t n, int64_t nnz, const int64_t* rowptr
     if (n > 0 && (!lse || !aligned(lse, 4) || !a || !aligned(a, 16))) return SGAT_INVALID_ARGUMENT;
     if (!(negative_slope == negative_slope)) return SGAT_INVALID_ARGUMENT;   // NaN
     Layout L;
-    if ((rc = check_ws(plan->p, SGAT_OP_GAT_FWD, H, D, ws, ws_bytes, L))) return rc;
+    if ((rc = check_ws(plan->p, SGAT_OP_GAT_FWD, H, D, dtype, ws, ws_bytes, L))) return rc;
     if (n == 0) return SGAT_OK;
     FwdWs w{at<float>(ws, L.off[0]), at<float>(ws, L.off[1])};
     return launch_gat_fwd(plan->p, H, D, dtype, colidx, x_dst, x_nbr, a, negative_slope, out,
@@ -303,7 +306,7 @@ int gat_bwd(const sgat_plan* plan, int64_t n, int64_t nnz, const int64_t* rowptr
     if (n > 0 && (!lse || !aligned(lse, 4) || !a || !aligned(a, 16))) return SGAT_INVALID_ARGUMENT;
     if (!(negative_slope == negative_slope)) return SGAT_INVALID_ARGUMENT;
     Layout L;
-    if ((rc = check_ws(plan->p, SGAT_OP_GAT_BWD, H, D, ws, ws_bytes, L))) return rc;
+    if ((rc = check_ws(plan->p, SGAT_OP_GAT_BWD, H, D, dtype, ws, ws_bytes, L))) return rc;
     if (n == 0) return launch_da_zero(da, H * D, static_cast<hipStream_t>(stream));
     BwdWs w{at<void>(ws, L.off[0]), at<float>(ws, L.off[1]), at<float>(ws, L.off[2]), nullptr,
             at<float>(ws, L.off[4]), nullptr};
@@ -322,7 +325,7 @@ int reduce_fwd(const sgat_plan* plan, int64_t n, int64_t nnz, const int64_t* row
         if ((rc = check_tensor(t, n))) return rc;
     if (arg && !aligned(arg, 16)) return SGAT_INVALID_ARGUMENT;
     Layout L;
-    if ((rc = check_ws(plan->p, SGAT_OP_REDUCE_FWD, 1, F, ws, ws_bytes, L))) return rc;
+    if ((rc = check_ws(plan->p, SGAT_OP_REDUCE_FWD, 1, F, dtype, ws, ws_bytes, L))) return rc;
     if (n == 0) return SGAT_OK;
     return launch_reduce_fwd(plan->p, F, dtype, op, colidx, X, out, arg, at<float>(ws, L.off[0]),
                              at<int32_t>(ws, L.off[1]), static_cast<hipStream_t>(stream));
@@ -337,9 +340,10 @@ int reduce_bwd(const sgat_plan* plan, int64_t n, int64_t nnz, const int64_t* row
     for (const void* t : {static_cast<const void*>(arg), dout, static_cast<const void*>(dX)})
         if ((rc = check_tensor(t, n))) return rc;
     Layout L;
-    if ((rc = check_ws(plan->p, SGAT_OP_REDUCE_BWD, 1, F, ws, ws_bytes, L))) return rc;
+    if ((rc = check_ws(plan->p, SGAT_OP_REDUCE_BWD, 1, F, dtype, ws, ws_bytes, L))) return rc;
     if (n == 0) return SGAT_OK;
-    return launch_reduce_bwd(plan->p, F, dtype, arg, dout, dX, at<float>(ws, L.off[0]),
+    return launch_reduce_bwd(plan->p, F, dtype, rowptr, arg, dout, dX, at<float>(ws, L.off[0]),
+                             at<uint32_t>(ws, L.off[1]), at<void>(ws, L.off[2]),
                              static_cast<hipStream_t>(stream));
 }
 

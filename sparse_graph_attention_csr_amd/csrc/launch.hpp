@@ -67,8 +67,9 @@ ReduceGeom reduce_geometry(int dt, int F);
 bool reduce_supported(int dt, int F);
 int launch_reduce_fwd(const Plan& p, int F, int dt, int op, const int32_t* colidx, const void* X,
                       void* out, int32_t* arg, float* part_val, int32_t* part_pos, hipStream_t s);
-int launch_reduce_bwd(const Plan& p, int F, int dt, const int32_t* arg, const void* dO, void* dX,
-                      float* part, hipStream_t s);
+int launch_reduce_bwd(const Plan& p, int F, int dt, const int64_t* rowptr, const int32_t* arg,
+                      const void* dO, void* dX, float* part, uint32_t* sc, void* entries,
+                      hipStream_t s);
 
 // da = 0 (the empty sum, for a graph without nodes), by a kernel.
 int launch_da_zero(float* da, int HD, hipStream_t s);

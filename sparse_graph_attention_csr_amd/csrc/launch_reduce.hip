@@ -1,5 +1,6 @@
 // Min/max reduction aggregation launchers: forward rows (+ merge of split
-// rows), backward over the transposed CSR (+ fixed-order sum of split sources).
+// rows); backward: route the contributions by winning edge on the CSR side,
+// gather them over the transposed CSR (+ fixed-order sum of split sources).
 #include "launch.hpp"
 #include "reduce.hpp"
 
@@ -18,11 +19,6 @@ namespace {
 constexpr int unroll_rf(int lpe, int nf)
 {
     const int u = lpe <= 16 ? 2 : SGAT_UNROLL_REDUCE_FWD;
-    return u / nf > 0 ? u / nf : 1;
-}
-constexpr int unroll_rb(int lpe, int nf)
-{
-    const int u = lpe <= 16 ? 2 : SGAT_UNROLL_REDUCE_BWD;
     return u / nf > 0 ? u / nf : 1;
 }
 }  // namespace
@@ -95,30 +91,49 @@ int launch_reduce_fwd(const Plan& p, int F, int dt, int op, const int32_t* colid
                   dim3(kBlock), &m, s);
 }
 
-int launch_reduce_bwd(const Plan& p, int F, int dt, const int32_t* arg, const void* dO, void* dX,
-                      float* part, hipStream_t s)
+int launch_reduce_bwd(const Plan& p, int F, int dt, const int64_t* rowptr, const int32_t* arg,
+                      const void* dO, void* dX, float* part, uint32_t* sc, void* entries,
+                      hipStream_t s)
 {
-    const ReduceGeom g = reduce_geometry(dt, F);
-    ReduceBwdArgs a;
-    a.items = p.dptr<sgat_work_item>(SGAT_ARR_COL_ITEMS);
-    a.n_items = static_cast<int64_t>(p.col_items.size());
-    a.F = F;
-    a.rowidx = p.dptr<int32_t>(SGAT_ARR_ROWIDX);
-    a.col_edge = p.dptr<int32_t>(SGAT_ARR_COL_EDGE);
-    a.arg = arg;
-    a.dO = dO;
-    a.dX = dX;
-    a.part = part;
-    const void* fn = nullptr;
-#define X(DT_, L_, N_) \
-    if (dt == DT_ && g.lpe == L_ && g.nf == N_) fn = reinterpret_cast<const void*>(&reduce_bwd_cols<DT_, L_, N_, unroll_rb(L_, N_)>);
-    SGAT_REDUCE_CONFIGS(X)
+    const int nr = reduce_geometry(dt, F).nf;
+    ReduceRouteArgs r;
+    r.items = p.dptr<sgat_work_item>(SGAT_ARR_ROW_ITEMS);
+    r.n_items = static_cast<int64_t>(p.row_items.size());
+    r.F = F;
+    r.rowptr = rowptr;
+    r.arg = arg;
+    r.dO = dO;
+    r.sc = sc;
+    r.entries = entries;
+    ReduceGatherArgs g;
+    g.items = p.dptr<sgat_work_item>(SGAT_ARR_COL_ITEMS);
+    g.n_items = static_cast<int64_t>(p.col_items.size());
+    g.F = F;
+    g.rowidx = p.dptr<int32_t>(SGAT_ARR_ROWIDX);
+    g.col_edge = p.dptr<int32_t>(SGAT_ARR_COL_EDGE);
+    g.sc = sc;
+    g.entries = entries;
+    g.dX = dX;
+    g.part = part;
+    const void *fr = nullptr, *fg = nullptr;
+#define X(DT_, N_)                                                                        \
+    if (dt == DT_ && nr == N_) {                                                          \
+        fr = reinterpret_cast<const void*>(&reduce_bwd_route<DT_, N_>);                   \
+        fg = reinterpret_cast<const void*>(&reduce_bwd_gather<DT_, N_, SGAT_UNROLL_REDUCE_BWD>); \
+    }
+    X(SGAT_BF16, 1) X(SGAT_BF16, 2) X(SGAT_BF16, 3) X(SGAT_BF16, 4)
+    X(SGAT_F32, 1) X(SGAT_F32, 2) X(SGAT_F32, 3) X(SGAT_F32, 4)
+    X(SGAT_F32, 5) X(SGAT_F32, 6) X(SGAT_F32, 7) X(SGAT_F32, 8)
 #undef X
-    if (!fn) return SGAT_INVALID_ARGUMENT;
+    if (!fr || !fg) return SGAT_INVALID_ARGUMENT;
     int rc;
-    if (a.n_items > 0 &&
-        (rc = launch("reduce_bwd_cols", fn, dim3(static_cast<unsigned>(wave_grid(a.n_items))),
-                     dim3(kBlock), &a, s)))
+    if (r.n_items > 0 &&
+        (rc = launch("reduce_bwd_route", fr, dim3(static_cast<unsigned>(wave_grid(r.n_items))),
+                     dim3(kBlock), &r, s)))
+        return rc;
+    if (g.n_items > 0 &&
+        (rc = launch("reduce_bwd_gather", fg, dim3(static_cast<unsigned>(wave_grid(g.n_items))),
+                     dim3(kBlock), &g, s)))
         return rc;
     return merge_sum("reduce_bwd_merge", p.col_splits, p.dptr<sgat_split>(SGAT_ARR_COL_SPLITS), F,
                      part, 1.f, dX, nullptr, 0.f, nullptr, dt, s);

@@ -216,99 +216,231 @@ __global__ __launch_bounds__(kBlock) void reduce_merge(ReduceMergeArgs a)
     if (a.arg) a.arg[oi] = at;
 }
 
-// Backward over the transposed CSR: for source j and each of its out-edges
-// e = (j -> i), feature f of dX[j] takes dout[i,f] where arg[i,f] == e. The
-// winners are read once per edge; dout only where an edge won. Sums run in
-// transposed-CSR order (lane groups and chunks in fixed order).
-struct ReduceBwdArgs {
-    const sgat_work_item* items;
+// Backward, in two passes. dX[j,f] is the sum of dout[i,f] over the (i, f)
+// whose winner is an edge j -> i. Reading each edge's winners from the
+// transposed side would fetch a whole row of arg per edge and scatter
+// 16-byte reads of dout; instead the contributions are first regrouped by
+// edge on the destination side, where arg_i and dout_i are read once each.
+//
+// Route (one wave per destination row): count the row's F winners per edge
+// in an LDS histogram (over windows of the row's edges, so any degree fits),
+// turn the counts into starts by a wave scan, write every edge's
+// (start, count) inside the row's block of F entries, and place each feature
+// f at its edge's next free slot as the pair (f, dout[i,f]). The order of the
+// pairs inside one edge's range does not matter: they name distinct features.
+//
+// Gather (one wave per transposed-CSR work item): for each out-edge of the
+// source, in transposed-CSR order, add its pairs into an LDS accumulator of F
+// values; one edge's pairs name distinct features, so lanes never collide,
+// and a feature receives the edges' contributions in a fixed order.
+constexpr int kRouteWindow = 1024;        // histogram bins per wave
+
+template <int DT> struct RouteEntry;      // (feature, dout) pair of one winner
+template <> struct RouteEntry<SGAT_BF16> { using T = uint32_t; };   // f | bf16 bits << 16
+template <> struct RouteEntry<SGAT_F32> { using T = uint2; };       // (f, fp32 bits)
+
+struct ReduceRouteArgs {
+    const sgat_work_item* items;   // the CSR work list (a split row's first chunk stands for it)
+    int64_t n_items;
+    int F;
+    const int64_t* rowptr;
+    const int32_t* arg;
+    const void* dO;
+    uint32_t* sc;                  // [nnz] start | count << 16
+    void* entries;                 // [n][F] RouteEntry, grouped by winning edge per row
+};
+
+__device__ __forceinline__ int wave_inclusive_scan(int x)
+{
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+        const int t = __shfl_up(x, o);
+        if (lane >= o) x += t;
+    }
+    return x;
+}
+
+// LDS traffic of one wave stays in issue order; this keeps the compiler from
+// moving accesses across the phase boundaries either.
+__device__ __forceinline__ void wave_lds_fence()
+{
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+}
+
+template <int DT, int NR>
+__global__ __launch_bounds__(kBlock) void reduce_bwd_route(ReduceRouteArgs a)
+{
+    constexpr int VEC = Elem<DT>::VEC;
+    __shared__ int32_t hist_all[kWavesPerBlock][kRouteWindow];
+    const int64_t unit = logical_block() * kWavesPerBlock + wave_id();
+    if (unit >= a.n_items) return;
+    const sgat_work_item it = a.items[unit];
+    if (it.slot >= 0 && !(it.flags & 1)) return;
+    const int64_t r0 = a.rowptr[it.row];
+    const int64_t d = a.rowptr[it.row + 1] - r0;
+    if (d == 0) return;
+    const int lane = threadIdx.x & 63;
+    int32_t* hist = hist_all[wave_id()];
+    const int64_t F = a.F;
+    const int64_t rowF = static_cast<int64_t>(it.row) * F;
+
+    bool fv[NR];
+    int32_t q[NR][VEC];            // winner as an edge index inside the row (nnz < 2^31)
+    float dv[NR][VEC];
+#pragma unroll
+    for (int k = 0; k < NR; ++k) {
+        const int64_t c = (k * kWave + lane) * VEC;
+        fv[k] = c < F;
+        int32_t w[VEC];
+#pragma unroll
+        for (int v = 0; v < VEC; ++v) { w[v] = -1; dv[k][v] = 0.f; }
+        if (fv[k]) {
+            ld_i32<VEC>(a.arg + rowF + c, w);
+            to_f32<DT>(ldg<DT>(a.dO, rowF + c), dv[k]);
+        }
+#pragma unroll
+        for (int v = 0; v < VEC; ++v) q[k][v] = w[v] - static_cast<int32_t>(r0);
+    }
+
+    using E = typename RouteEntry<DT>::T;
+    E* ent = static_cast<E*>(a.entries) + rowF;
+    int total = 0;
+    for (int32_t w0 = 0; w0 < d; w0 += kRouteWindow) {
+        const int nb = static_cast<int>(d - w0 < kRouteWindow ? d - w0 : kRouteWindow);
+        for (int b = lane; b < nb; b += kWave) hist[b] = 0;
+        wave_lds_fence();
+#pragma unroll
+        for (int k = 0; k < NR; ++k)
+#pragma unroll
+            for (int v = 0; v < VEC; ++v) {
+                const int32_t b = q[k][v] - w0;
+                if (fv[k] && b >= 0 && b < nb) atomicAdd(&hist[b], 1);
+            }
+        wave_lds_fence();
+        for (int b0 = 0; b0 < nb; b0 += kWave) {
+            const int b = b0 + lane;
+            const int c = b < nb ? hist[b] : 0;
+            const int incl = wave_inclusive_scan(c);
+            const int st = total + incl - c;
+            if (b < nb) {
+                hist[b] = st;
+                a.sc[r0 + w0 + b] = static_cast<uint32_t>(st) | (static_cast<uint32_t>(c) << 16);
+            }
+            total += __builtin_amdgcn_readlane(incl, 63);
+        }
+        wave_lds_fence();
+#pragma unroll
+        for (int k = 0; k < NR; ++k)
+#pragma unroll
+            for (int v = 0; v < VEC; ++v) {
+                const int32_t b = q[k][v] - w0;
+                if (fv[k] && b >= 0 && b < nb) {
+                    const int slot = atomicAdd(&hist[b], 1);
+                    const uint32_t f = static_cast<uint32_t>((k * kWave + lane) * VEC + v);
+                    if constexpr (DT == SGAT_BF16)
+                        ent[slot] = f | (__float_as_uint(dv[k][v]) & 0xffff0000u);
+                    else
+                        ent[slot] = make_uint2(f, __float_as_uint(dv[k][v]));
+                }
+            }
+        wave_lds_fence();
+    }
+}
+
+struct ReduceGatherArgs {
+    const sgat_work_item* items;   // the transposed-CSR work list
     int64_t n_items;
     int F;
     const int32_t* rowidx;
     const int32_t* col_edge;
-    const int32_t* arg;
-    const void* dO;
+    const uint32_t* sc;
+    const void* entries;
     void* dX;
-    float* part;           // [col_slots][F]
+    float* part;                   // [col_slots][F]
 };
 
-template <int DT, int LPE, int NF, int U>
-__global__ __launch_bounds__(kBlock) void reduce_bwd_cols(ReduceBwdArgs a)
+template <int DT, int NR, int U>
+__global__ __launch_bounds__(kBlock) void reduce_bwd_gather(ReduceGatherArgs a)
 {
     constexpr int VEC = Elem<DT>::VEC;
-    constexpr int EPW = kWave / LPE;
+    constexpr int ACC = NR * kWave * VEC;
+    __shared__ float acc_all[kWavesPerBlock][ACC];
     const int64_t unit = logical_block() * kWavesPerBlock + wave_id();
     if (unit >= a.n_items) return;
     const sgat_work_item it = a.items[unit];
-    const int lane = threadIdx.x & 63, sub = lane / LPE, pos = lane % LPE;
+    const int lane = threadIdx.x & 63;
+    float* acc = acc_all[wave_id()];
     const int64_t F = a.F;
-    bool fv[NF];
-#pragma unroll
-    for (int k = 0; k < NF; ++k) fv[k] = (k * LPE + pos) * VEC < F;
+    for (int b = lane; b < ACC; b += kWave) acc[b] = 0.f;
+    wave_lds_fence();
 
-    float acc[NF][VEC];
-#pragma unroll
-    for (int k = 0; k < NF; ++k)
-#pragma unroll
-        for (int v = 0; v < VEC; ++v) acc[k][v] = 0.f;
-
+    using E = typename RouteEntry<DT>::T;
+    const E* ent = static_cast<const E*>(a.entries);
     const int32_t* ri = a.rowidx + it.begin;
     const int32_t* ce = a.col_edge + it.begin;
     for (int base = 0; base < it.len; base += kWave) {
         const int nb = min(kWave, it.len - base);
         const int li = lane < nb ? ri[base + lane] : 0;
-        const int le = lane < nb ? ce[base + lane] : -1;
-        for (int t = 0; t < nb; t += EPW * U) {
-            int32_t w[U][NF][VEC];
-            int32_t eid[U];
+        const uint32_t ls = lane < nb ? a.sc[lane < nb ? ce[base + lane] : 0] : 0u;
+        for (int t = 0; t < nb; t += U) {
+            float v[U];
+            int f[U];
+            uint32_t cnt[U], st[U];
             int64_t row[U];
 #pragma unroll
             for (int u = 0; u < U; ++u) {
-                const int e = t + u * EPW + sub;
-                // both cross-lane reads run on every lane (a read from a lane
-                // that is switched off returns garbage); the select comes after
-                row[u] = bcast<EPW>(li, e);
-                const int32_t ev = bcast<EPW>(le, e);
-                eid[u] = e < nb ? ev : -2;
-#pragma unroll
-                for (int k = 0; k < NF; ++k) {
-#pragma unroll
-                    for (int v = 0; v < VEC; ++v) w[u][k][v] = -1;
-                    if (e < nb && fv[k]) ld_i32<VEC>(a.arg + row[u] * F + (k * LPE + pos) * VEC, w[u][k]);
+                const int e = t + u;
+                const uint32_t s = __builtin_amdgcn_readlane(ls, e < nb ? e : 0);
+                row[u] = __builtin_amdgcn_readlane(li, e < nb ? e : 0);
+                cnt[u] = e < nb ? s >> 16 : 0u;
+                st[u] = s & 0xffffu;
+                f[u] = -1;
+                v[u] = 0.f;
+                if (static_cast<uint32_t>(lane) < cnt[u]) {
+                    const E x = ent[row[u] * F + st[u] + lane];
+                    if constexpr (DT == SGAT_BF16) {
+                        f[u] = static_cast<int>(x & 0xffffu);
+                        v[u] = __uint_as_float(x & 0xffff0000u);
+                    } else {
+                        f[u] = static_cast<int>(x.x);
+                        v[u] = __uint_as_float(x.y);
+                    }
                 }
             }
 #pragma unroll
             for (int u = 0; u < U; ++u)
+                if (f[u] >= 0 && f[u] < F) acc[f[u]] += v[u];
+            // edges that won more than 64 features of their row
 #pragma unroll
-                for (int k = 0; k < NF; ++k) {
-                    bool any = false;
-#pragma unroll
-                    for (int v = 0; v < VEC; ++v) any |= w[u][k][v] == eid[u];
-                    if (any) {
-                        float d[VEC];
-                        to_f32<DT>(ldg<DT>(a.dO, row[u] * F + (k * LPE + pos) * VEC), d);
-#pragma unroll
-                        for (int v = 0; v < VEC; ++v)
-                            if (w[u][k][v] == eid[u]) acc[k][v] += d[v];
+            for (int u = 0; u < U; ++u)
+                for (uint32_t c0 = kWave; c0 < cnt[u]; c0 += kWave)
+                    if (c0 + lane < cnt[u]) {
+                        const E x = ent[row[u] * F + st[u] + c0 + lane];
+                        int ff;
+                        float vv;
+                        if constexpr (DT == SGAT_BF16) {
+                            ff = static_cast<int>(x & 0xffffu);
+                            vv = __uint_as_float(x & 0xffff0000u);
+                        } else {
+                            ff = static_cast<int>(x.x);
+                            vv = __uint_as_float(x.y);
+                        }
+                        if (ff < F) acc[ff] += vv;
                     }
-                }
         }
     }
-    if constexpr (EPW > 1) {
+    wave_lds_fence();
 #pragma unroll
-        for (int off = LPE; off < kWave; off <<= 1)
+    for (int k = 0; k < NR; ++k) {
+        const int64_t c = (k * kWave + lane) * VEC;
+        if (c >= F) continue;
+        float x[VEC];
 #pragma unroll
-            for (int k = 0; k < NF; ++k)
-#pragma unroll
-                for (int v = 0; v < VEC; ++v) acc[k][v] += __shfl_xor(acc[k][v], off);
-    }
-    if (sub != 0) return;
-#pragma unroll
-    for (int k = 0; k < NF; ++k) {
-        if (!fv[k]) continue;
-        const int64_t col = (k * LPE + pos) * VEC;
-        if (it.slot < 0) stg<DT>(a.dX, static_cast<int64_t>(it.row) * F + col, acc[k]);
-        else st_f32<VEC>(a.part + static_cast<int64_t>(it.slot) * F + col, acc[k]);
+        for (int q = 0; q < VEC; ++q) x[q] = acc[c + q];
+        if (it.slot < 0) stg<DT>(a.dX, static_cast<int64_t>(it.row) * F + c, x);
+        else st_f32<VEC>(a.part + static_cast<int64_t>(it.slot) * F + c, x);
     }
 }
 

@@ -157,8 +157,12 @@ def test_reduce_workspace_bytes(plan):
     F = 512
     fwd = plan.workspace_bytes(B.OP_REDUCE_FWD, 1, F, B.BF16)
     assert fwd == 2 * (-(-s["row_slots"] * F * 4 // 256) * 256)
-    bwd = plan.workspace_bytes(B.OP_REDUCE_BWD, 1, F, B.F32)
-    assert bwd == -(-s["col_slots"] * F * 4 // 256) * 256
+    def up(x):
+        return -(-x // 256) * 256
+
+    for dt, eb in ((B.F32, 8), (B.BF16, 4)):
+        bwd = plan.workspace_bytes(B.OP_REDUCE_BWD, 1, F, dt)
+        assert bwd == up(s["col_slots"] * F * 4) + up(s["nnz"] * 4) + up(s["n"] * F * eb)
     with pytest.raises(B.SgatError):
         plan.workspace_bytes(B.OP_REDUCE_FWD, 2, F, B.BF16)      # H must be 1
     with pytest.raises(B.SgatError):
