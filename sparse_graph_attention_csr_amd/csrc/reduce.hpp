@@ -349,6 +349,20 @@ __global__ __launch_bounds__(kBlock) void reduce_bwd_route(ReduceRouteArgs a)
     }
 }
 
+template <int DT>
+__device__ __forceinline__ int route_feature(typename RouteEntry<DT>::T x)
+{
+    if constexpr (DT == SGAT_BF16) return static_cast<int>(x & 0xffffu);
+    else return static_cast<int>(x.x);
+}
+
+template <int DT>
+__device__ __forceinline__ float route_value(typename RouteEntry<DT>::T x)
+{
+    if constexpr (DT == SGAT_BF16) return __uint_as_float(x & 0xffff0000u);
+    else return __uint_as_float(x.y);
+}
+
 struct ReduceGatherArgs {
     const sgat_work_item* items;   // the transposed-CSR work list
     int64_t n_items;
@@ -366,69 +380,64 @@ __global__ __launch_bounds__(kBlock) void reduce_bwd_gather(ReduceGatherArgs a)
 {
     constexpr int VEC = Elem<DT>::VEC;
     constexpr int ACC = NR * kWave * VEC;
-    __shared__ float acc_all[kWavesPerBlock][ACC];
+    // F accumulators, then one spare slot per lane that idle lanes update
+    __shared__ float acc_all[kWavesPerBlock][ACC + kWave];
     const int64_t unit = logical_block() * kWavesPerBlock + wave_id();
     if (unit >= a.n_items) return;
     const sgat_work_item it = a.items[unit];
     const int lane = threadIdx.x & 63;
     float* acc = acc_all[wave_id()];
     const int64_t F = a.F;
-    for (int b = lane; b < ACC; b += kWave) acc[b] = 0.f;
+    for (int b = lane; b < ACC + kWave; b += kWave) acc[b] = 0.f;
+    const int spare = ACC + lane;
     wave_lds_fence();
 
     using E = typename RouteEntry<DT>::T;
     const E* ent = static_cast<const E*>(a.entries);
     const int32_t* ri = a.rowidx + it.begin;
     const int32_t* ce = a.col_edge + it.begin;
+    // Every load below is unconditional, at an index clamped into the row's
+    // block of F pairs; only the LDS update is masked. (A load under a
+    // lane-dependent branch is waited for inside that branch, which would
+    // serialise the edges.)
     for (int base = 0; base < it.len; base += kWave) {
         const int nb = min(kWave, it.len - base);
-        const int li = lane < nb ? ri[base + lane] : 0;
-        const uint32_t ls = lane < nb ? a.sc[lane < nb ? ce[base + lane] : 0] : 0u;
+        const int lc = min(lane, nb - 1);
+        const int li = ri[base + lc];
+        const uint32_t ls = a.sc[ce[base + lc]];
         for (int t = 0; t < nb; t += U) {
-            float v[U];
-            int f[U];
+            E x[U];
             uint32_t cnt[U], st[U];
             int64_t row[U];
 #pragma unroll
             for (int u = 0; u < U; ++u) {
-                const int e = t + u;
-                const uint32_t s = __builtin_amdgcn_readlane(ls, e < nb ? e : 0);
-                row[u] = __builtin_amdgcn_readlane(li, e < nb ? e : 0);
-                cnt[u] = e < nb ? s >> 16 : 0u;
-                st[u] = s & 0xffffu;
-                f[u] = -1;
-                v[u] = 0.f;
-                if (static_cast<uint32_t>(lane) < cnt[u]) {
-                    const E x = ent[row[u] * F + st[u] + lane];
-                    if constexpr (DT == SGAT_BF16) {
-                        f[u] = static_cast<int>(x & 0xffffu);
-                        v[u] = __uint_as_float(x & 0xffff0000u);
-                    } else {
-                        f[u] = static_cast<int>(x.x);
-                        v[u] = __uint_as_float(x.y);
-                    }
-                }
+                const int e = t + u < nb ? t + u : nb - 1;
+                const uint32_t sv = __builtin_amdgcn_readlane(ls, e);
+                row[u] = __builtin_amdgcn_readlane(li, e);
+                cnt[u] = t + u < nb ? sv >> 16 : 0u;
+                st[u] = sv & 0xffffu;
+                const int64_t k = min(static_cast<int64_t>(st[u]) + lane, F - 1);
+                x[u] = ent[row[u] * F + k];
             }
+            // pairs inside [start, start + count) were written by this call's
+            // route pass, with features below F. Lanes past the count update
+            // their spare slot with value * 0: the product needs the loaded
+            // value on every lane, so the compiler cannot move a load under a
+            // lane-dependent branch (a select of 0 would let it).
 #pragma unroll
-            for (int u = 0; u < U; ++u)
-                if (f[u] >= 0 && f[u] < F) acc[f[u]] += v[u];
+            for (int u = 0; u < U; ++u) {
+                const bool live = static_cast<uint32_t>(lane) < cnt[u];
+                acc[live ? route_feature<DT>(x[u]) : spare] += route_value<DT>(x[u]) * (live ? 1.f : 0.f);
+            }
             // edges that won more than 64 features of their row
 #pragma unroll
             for (int u = 0; u < U; ++u)
-                for (uint32_t c0 = kWave; c0 < cnt[u]; c0 += kWave)
-                    if (c0 + lane < cnt[u]) {
-                        const E x = ent[row[u] * F + st[u] + c0 + lane];
-                        int ff;
-                        float vv;
-                        if constexpr (DT == SGAT_BF16) {
-                            ff = static_cast<int>(x & 0xffffu);
-                            vv = __uint_as_float(x & 0xffff0000u);
-                        } else {
-                            ff = static_cast<int>(x.x);
-                            vv = __uint_as_float(x.y);
-                        }
-                        if (ff < F) acc[ff] += vv;
-                    }
+                for (uint32_t c0 = kWave; c0 < cnt[u]; c0 += kWave) {
+                    const int64_t k = min(static_cast<int64_t>(st[u] + c0) + lane, F - 1);
+                    const E y = ent[row[u] * F + k];
+                    const bool live = c0 + lane < cnt[u];
+                    acc[live ? route_feature<DT>(y) : spare] += route_value<DT>(y) * (live ? 1.f : 0.f);
+                }
         }
     }
     wave_lds_fence();
