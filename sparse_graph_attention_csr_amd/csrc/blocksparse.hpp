@@ -63,7 +63,11 @@ struct Shape {
     static constexpr int KS = D / 32;     // k-steps of a 16x16xD score product
     static constexpr int NB = D / 16;     // 16-channel output blocks
     static constexpr int SPL = D / 32;    // 16-byte segments of a 16-row tile per lane
-    static constexpr int LDW = D + 16;    // LDS row stride (elements): 4 rows hit distinct banks
+    // LDS row stride (elements). D + 8 makes both access patterns conflict-free:
+    // 16-byte row writes by lanes i = 0..15 start 4 banks apart (mod 64), and
+    // the transposed reads of rows 4g + kk by the four lane groups g fall 16
+    // banks apart.
+    static constexpr int LDW = D + 8;
 };
 
 // Start offsets of rows 1..15 of a 16-row (or 16-source) block in a pointer

@@ -194,12 +194,16 @@ __global__ __launch_bounds__(kBlock) void gat_fwd_rows(GatFwdArgs a)
     const G g(hg, a.H);
     const int64_t HD = static_cast<int64_t>(a.H) * D;
 
-    float xs[VEC] = {}, at[VEC] = {};
+    // a_d LeakyReLU(z_d) = z_d g_d with g_d = a_d for z_d > 0, a_d * slope otherwise
+    float xs[VEC] = {}, at[VEC] = {}, as[VEC];
     if (g.hvalid) {
         to_f32<DT>(ldg<DT>(a.Xs, static_cast<int64_t>(it.row) * HD + g.col), xs);
         ld_f32<VEC>(a.att + g.col, at);
+    }
 #pragma unroll
-        for (int k = 0; k < VEC; ++k) at[k] *= kLog2e;
+    for (int k = 0; k < VEC; ++k) {
+        at[k] *= kLog2e;
+        as[k] = at[k] * a.slope;
     }
     Online<VEC> st;
     const int32_t* ci = a.colidx + it.begin;
@@ -227,7 +231,7 @@ __global__ __launch_bounds__(kBlock) void gat_fwd_rows(GatFwdArgs a)
 #pragma unroll
                 for (int k = 0; k < VEC; ++k) {
                     const float z = xs[k] + x[k];
-                    part = fmaf(at[k], z > 0.f ? z : a.slope * z, part);
+                    part = fmaf(z, z > 0.f ? at[k] : as[k], part);
                 }
                 const float hs = head_sum<G::SPH>(part);
                 s[u] = ok[u] ? hs : kNegInf;
@@ -538,8 +542,12 @@ __global__ __launch_bounds__(kBlock) void gat_bwd_rows(GatBwdRowArgs a)
     const int64_t HD = static_cast<int64_t>(a.H) * D;
     const int wid = wave_id();
 
-    float at[VEC] = {};
+    // g_d = a_d LeakyReLU'(z_d): a_d for z_d > 0, a_d * slope otherwise; then
+    // a_d LeakyReLU(z_d) = z_d g_d and the dXs term is dE g_d
+    float at[VEC] = {}, as[VEC];
     if (g.hvalid) ld_f32<VEC>(a.att + g.col, at);
+#pragma unroll
+    for (int k = 0; k < VEC; ++k) as[k] = at[k] * a.slope;
     float da[VEC] = {};
 
     const int64_t stride = static_cast<int64_t>(gridDim.x) * kWavesPerBlock;
@@ -578,13 +586,14 @@ __global__ __launch_bounds__(kBlock) void gat_bwd_rows(GatBwdRowArgs a)
                 }
 #pragma unroll
                 for (int u = 0; u < U; ++u) {
-                    float x[VEC], z[VEC];
+                    float x[VEC], z[VEC], gz[VEC];
                     to_f32<DT>(xf[u], x);
                     float part = 0.f;
 #pragma unroll
                     for (int k = 0; k < VEC; ++k) {
                         z[k] = xs[k] + x[k];
-                        part = fmaf(at[k], z[k] > 0.f ? z[k] : a.slope * z[k], part);
+                        gz[k] = z[k] > 0.f ? at[k] : as[k];
+                        part = fmaf(z[k], gz[k], part);
                     }
                     const float e2 = head_sum<G::SPH>(part) * kLog2e;
                     const float dp = head_sum<G::SPH>(dot<DT>(dof, xf[u]));
@@ -592,9 +601,8 @@ __global__ __launch_bounds__(kBlock) void gat_bwd_rows(GatBwdRowArgs a)
                     const float dE = p * (dp - delta);
 #pragma unroll
                     for (int k = 0; k < VEC; ++k) {
-                        const bool pos = z[k] > 0.f;
-                        dxs[k] = fmaf(dE * at[k], pos ? 1.f : a.slope, dxs[k]);
-                        da[k] = fmaf(dE, pos ? z[k] : a.slope * z[k], da[k]);
+                        dxs[k] = fmaf(dE, gz[k], dxs[k]);
+                        da[k] = fmaf(dE, z[k] > 0.f ? z[k] : a.slope * z[k], da[k]);
                     }
                 }
             }
@@ -743,12 +751,15 @@ __global__ __launch_bounds__(kBlock) void gat_bwd_cols(GatBwdColArgs a)
     const G g(hg, a.H);
     const int64_t HD = static_cast<int64_t>(a.H) * D;
 
+    // g_d = a_d LeakyReLU'(z_d); a_d LeakyReLU(z_d) = z_d g_d
     Frag xtf = frag_zero();
-    float xt[VEC] = {}, at[VEC] = {};
+    float xt[VEC] = {}, at[VEC] = {}, as[VEC];
     if (g.hvalid) {
         xtf = ldg<DT>(a.Xt, static_cast<int64_t>(it.row) * HD + g.col);
         ld_f32<VEC>(a.att + g.col, at);
     }
+#pragma unroll
+    for (int k = 0; k < VEC; ++k) as[k] = at[k] * a.slope;
     to_f32<DT>(xtf, xt);
     float dxt[VEC] = {};
     const int32_t* ri = a.rowidx + it.begin;
@@ -775,13 +786,14 @@ __global__ __launch_bounds__(kBlock) void gat_bwd_cols(GatBwdColArgs a)
             }
 #pragma unroll
             for (int u = 0; u < U; ++u) {
-                float xs[VEC], z[VEC];
+                float xs[VEC], gz[VEC];
                 to_f32<DT>(sf[u], xs);
                 float part = 0.f;
 #pragma unroll
                 for (int k = 0; k < VEC; ++k) {
-                    z[k] = xs[k] + xt[k];
-                    part = fmaf(at[k], z[k] > 0.f ? z[k] : a.slope * z[k], part);
+                    const float z = xs[k] + xt[k];
+                    gz[k] = z > 0.f ? at[k] : as[k];
+                    part = fmaf(z, gz[k], part);
                 }
                 const float e2 = head_sum<G::SPH>(part) * kLog2e;
                 const float dp = head_sum<G::SPH>(dot<DT>(df[u], xtf));
@@ -790,10 +802,7 @@ __global__ __launch_bounds__(kBlock) void gat_bwd_cols(GatBwdColArgs a)
                 float dx[VEC];
                 to_f32<DT>(df[u], dx);
 #pragma unroll
-                for (int k = 0; k < VEC; ++k) {
-                    const float gz = z[k] > 0.f ? 1.f : a.slope;
-                    dxt[k] = fmaf(p, dx[k], fmaf(dE * at[k], gz, dxt[k]));
-                }
+                for (int k = 0; k < VEC; ++k) dxt[k] = fmaf(p, dx[k], fmaf(dE, gz[k], dxt[k]));
             }
         }
     }

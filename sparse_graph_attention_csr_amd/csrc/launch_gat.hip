@@ -25,7 +25,7 @@ namespace {
 // registers.
 constexpr int unroll_fwd(int epw) { return epw >= 4 ? (SGAT_UNROLL_FWD + 3) / 4 : SGAT_UNROLL_FWD; }
 constexpr int unroll_bwd(int epw) { return epw >= 4 ? (SGAT_UNROLL_BWD + 1) / 2 : SGAT_UNROLL_BWD; }
-constexpr int kGatBwdMaxBlocks = 2048;
+constexpr int kGatBwdMaxBlocks = 4096;
 }
 
 // Fixed-order sum of the per-workgroup da partials: one workgroup per element
