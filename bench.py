@@ -196,6 +196,28 @@ def cpu_baseline(w, seconds: float):
                       f"{spec.passes}, fp64, {t:.1f} s"}
 
 
+def load_workload(name: str, cache_dir: str) -> dict:
+    """The seeded workload, generated or (with a cache directory) loaded from
+    the .npz an earlier run saved there."""
+    import numpy as np
+
+    from sparse_graph_attention_csr_amd import inputs as I
+    if not cache_dir:
+        return I.make_workload(name)
+    path = os.path.join(cache_dir, name + ".npz")
+    if os.path.exists(path):
+        with np.load(path, allow_pickle=False) as z:
+            w = {k: z[k] for k in z.files}
+    else:
+        w = I.make_workload(name)
+        os.makedirs(cache_dir, exist_ok=True)
+        tmp = path + ".tmp.npz"
+        np.savez(tmp, **{k: v for k, v in w.items() if isinstance(v, np.ndarray)})
+        os.replace(tmp, path)
+    w["spec"] = I.WORKLOADS[name]
+    return w
+
+
 def compare_unfused(spec, g, fused_step, fused_owned, inputs, fused_out, bwd, fused_ms,
                     steps, warmup):
     """Latency and peak device memory of one step of the unfused PyTorch
@@ -285,6 +307,9 @@ def main():
     ap.add_argument("--compare-unfused", action="store_true",
                     help="also time the unfused PyTorch formulation (bench_unfused.py) and "
                          "report latency and peak-memory ratios")
+    ap.add_argument("--cache-dir", default="",
+                    help="keep the generated workload arrays here (.npz) and reuse them on the "
+                         "next run (inputs only; the timed work is unchanged)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB three times "
                          "(calibrates the HBM byte counters) and exit")
@@ -313,7 +338,7 @@ def main():
                           "launches": 3}), flush=True)
         return
     spec = I.WORKLOADS[args.workload]
-    w = I.make_workload(args.workload)
+    w = load_workload(args.workload, args.cache_dir)
     if args.reorder != "none":
         w = I.relabel(w, I.node_order(w["rowptr"], w["colidx"], args.reorder))
     rp, ci = w["rowptr"], w["colidx"]
