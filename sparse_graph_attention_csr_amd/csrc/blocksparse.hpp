@@ -18,9 +18,11 @@
 // are packed 16 at a time into gathered "pseudo-tiles" whose column c is one
 // residual edge, so they go through the same softmax.
 //
-// Every kernel walks its tiles software-pipelined: the loads of tile k+1 are
-// issued before tile k is computed, so each wave keeps one tile of gathers in
-// flight while its matrix and softmax work runs.
+// Every kernel walks its tiles software-pipelined with one set of tile
+// registers: a tile's first phase consumes them (the score products, and the
+// operand that is transposed goes to LDS), the loads of the next tile refill
+// them at once, and they arrive while the second phase (softmax, the
+// LDS-fed products) runs. Tile descriptions are fetched two tiles ahead.
 #pragma once
 
 #include "gather.hpp"
@@ -28,6 +30,7 @@
 namespace sgat {
 
 constexpr int kTileDim = 16;
+constexpr float kRescaleLog2 = 8.f;   // tile forward: weights stay below 2^8 (see fwd_phase_b)
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
@@ -63,12 +66,52 @@ struct Shape {
     static constexpr int KS = D / 32;     // k-steps of a 16x16xD score product
     static constexpr int NB = D / 16;     // 16-channel output blocks
     static constexpr int SPL = D / 32;    // 16-byte segments of a 16-row tile per lane
-    // LDS row stride (elements). D + 8 makes both access patterns conflict-free:
-    // 16-byte row writes by lanes i = 0..15 start 4 banks apart (mod 64), and
-    // the transposed reads of rows 4g + kk by the four lane groups g fall 16
-    // banks apart.
-    static constexpr int LDW = D + 8;
+    // LDS row stride (elements) of tiles read back with ds_read_b64_tr_b16.
+    // Measured on gfx950 (SQ_LDS_BANK_CONFLICT per LDS instruction, community
+    // workload): D + 8, D + 24 and D + 40 give the fewest conflicts, D + 16
+    // twice as many, D + 32 seven times as many; kernel times are the same
+    // within 1 % for all but D + 32, so LDS is not what bounds these kernels.
+    static constexpr int LDV = D + 8;
 };
+
+// Transposed 4 x 16-bit LDS read (gfx950 ds_read_b64_tr_b16). Within each
+// group of 16 lanes, lane j receives element j % 4 of the 64-bit word that
+// lane 4k + j / 4 addressed, in slot k.
+__device__ __forceinline__ s16x4_t lds_read_tr16(const uint16_t* p)
+{
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) s16x4_t*)(p));
+}
+
+// V tile lanes: lane l loads and stores row vrow(l) = l % 8 + 8 * (l / 32),
+// 16-byte chunk vchunk(l) = (l / 8) % 4 of each 32-channel slab (the V tile
+// goes only through LDS, so any assignment of its chunks to lanes works; this
+// one has every 16 lanes store 8 rows x 2 chunks).
+__device__ __forceinline__ int vrow(int l) { return (l & 7) + 8 * (l >> 5); }
+__device__ __forceinline__ int vchunk(int l) { return (l >> 3) & 3; }
+
+// Tiles whose lanes are fixed by the MFMA operand layout (lane (i, g) holds
+// row i, 16-byte chunk 4s + g of every 32-channel slab s) are stored at row
+// stride LDV with the chunks of rows 8..15 swapped in pairs (chunk ^ 1), so
+// that rows i and i + 8, stored by the same instruction, start on different
+// banks.
+template <int D>
+__device__ __forceinline__ void store_operand_tile(uint16_t* t, const Frag (&f)[Shape<D>::KS],
+                                                   int i, int g)
+{
+    uint16_t* row = t + i * Shape<D>::LDV + 8 * (g ^ ((i >> 3) & 1));
+#pragma unroll
+    for (int s = 0; s < Shape<D>::KS; ++s) *reinterpret_cast<Frag*>(row + 32 * s) = f[s];
+}
+
+// Base address of lane (i, g)'s transposed reads of such a tile: block s
+// (channels 16s..16s+15, rows 4g..4g+3 into the MFMA A operand) is at + 16 s.
+// Lane i of the group addresses row 4g + i/4, channels 16s + 4(i%4).
+template <int D>
+__device__ __forceinline__ const uint16_t* operand_tr_base(const uint16_t* t, int i, int g)
+{
+    return t + (4 * g + (i >> 2)) * Shape<D>::LDV + 8 * (((i >> 1) & 1) ^ (g >> 1)) + 4 * (i & 1);
+}
 
 // Start offsets of rows 1..15 of a 16-row (or 16-source) block in a pointer
 // array, loaded once per block (rows past the end start at ptr[hi]).
@@ -143,24 +186,28 @@ template <int D>
 struct FwdTile {
     Frag kf[Shape<D>::KS];
     uint4 vr[Shape<D>::SPL];
-    __device__ __forceinline__ void load(const void* K, const void* V, int64_t base, int g)
+    // kbase: row l%16's node row (K, MFMA operand layout); vbase: row
+    // vrow(l)'s node row (V, staged through LDS)
+    __device__ __forceinline__ void load(const void* K, const void* V, int64_t kbase,
+                                         int64_t vbase, int g, int l)
     {
 #pragma unroll
-        for (int s = 0; s < Shape<D>::KS; ++s) kf[s] = ldg<SGAT_BF16>(K, base + 32 * s + 8 * g);
+        for (int s = 0; s < Shape<D>::KS; ++s) kf[s] = ldg<SGAT_BF16>(K, kbase + 32 * s + 8 * g);
 #pragma unroll
         for (int q = 0; q < Shape<D>::SPL; ++q)
-            vr[q] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(V) + base +
-                                                    8 * (g + 4 * q));
+            vr[q] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(V) + vbase +
+                                                    32 * q + 8 * vchunk(l));
     }
 };
 
-// One forward tile for one head: masked online-softmax update of (m, lsum)
-// and O^T += V^T P^T.
+// One forward tile for one head, in two phases. Phase A consumes the tile's
+// registers (S^T = K Q^T, V into LDS), so the next tile's loads can refill
+// them before phase B: the masked online-softmax update of (m, lsum) and
+// O^T += V^T P^T from LDS.
 template <int D>
-__device__ __forceinline__ void fwd_compute(const FwdTile<D>& tl, uint32_t valid,
-                                            const bf16x8_t (&qf)[Shape<D>::KS], float& m,
-                                            float& lsum, f32x4_t (&acc)[Shape<D>::NB],
-                                            uint16_t* vs, float scale2, int i, int g)
+__device__ __forceinline__ f32x4_t fwd_phase_a(const FwdTile<D>& tl,
+                                               const bf16x8_t (&qf)[Shape<D>::KS], uint16_t* vs,
+                                               int l)
 {
     using S = Shape<D>;
     f32x4_t st = {0.f, 0.f, 0.f, 0.f};
@@ -170,8 +217,16 @@ __device__ __forceinline__ void fwd_compute(const FwdTile<D>& tl, uint32_t valid
                                                      st, 0, 0, 0);
 #pragma unroll
     for (int q = 0; q < S::SPL; ++q)
-        *reinterpret_cast<uint4*>(vs + i * S::LDW + 8 * (g + 4 * q)) = tl.vr[q];
+        *reinterpret_cast<uint4*>(vs + vrow(l) * S::LDV + 32 * q + 8 * vchunk(l)) = tl.vr[q];
+    return st;
+}
 
+template <int D>
+__device__ __forceinline__ void fwd_phase_b(const f32x4_t& st, uint32_t valid, float& m,
+                                            float& lsum, f32x4_t (&acc)[Shape<D>::NB],
+                                            const uint16_t* vs, float scale2, int i, int g)
+{
+    using S = Shape<D>;
     float sv[4];
     float rmax = kNegInf;
 #pragma unroll
@@ -181,27 +236,37 @@ __device__ __forceinline__ void fwd_compute(const FwdTile<D>& tl, uint32_t valid
     }
     rmax = fmaxf(rmax, __shfl_xor(rmax, 16));
     rmax = fmaxf(rmax, __shfl_xor(rmax, 32));
-    const float mn = fmaxf(m, rmax);
-    const float corr = mn == kNegInf ? 1.f : fast_exp2(m - mn);
+    // Lazy rescaling: m is a reference maximum, moved (and O, lsum rescaled)
+    // only when a row's score passes it by more than 2^kRescaleLog2, so the
+    // weights exp2(s - m) stay below 2^kRescaleLog2 and the common tile leaves
+    // the accumulators untouched in the matrix registers. out = O / lsum and
+    // lse = m + log2(lsum) hold for any reference m.
+    const bool raise = rmax > m + kRescaleLog2;   // never for a row that has no score yet
+    if (__any(raise)) {
+        const float corr = raise ? fast_exp2(m - rmax) : 1.f;   // m = -inf gives 0
+        if (raise) m = rmax;
+        lsum *= corr;
+#pragma unroll
+        for (int s = 0; s < S::NB; ++s) acc[s] *= corr;
+    }
     float p[4], ps = 0.f;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-        p[k] = ((valid >> k) & 1u) ? fast_exp2(sv[k] - mn) : 0.f;
+        p[k] = ((valid >> k) & 1u) ? fast_exp2(sv[k] - m) : 0.f;
         ps += p[k];
     }
     ps += __shfl_xor(ps, 16);
     ps += __shfl_xor(ps, 32);
-    lsum = lsum * corr + ps;
-    m = mn;
+    lsum += ps;
     const s16x4_t pb = {bf16_bits(p[0]), bf16_bits(p[1]), bf16_bits(p[2]), bf16_bits(p[3])};
     __builtin_amdgcn_wave_barrier();
+    // A operand of block s: V[4g + kk][16s + i] for kk = 0..3, one transposed
+    // read (lane 4k + j/4 of the group addresses row 4g + k, channels 16s + 4(j%4))
+    const uint16_t* vt = vs + (4 * g + (i >> 2)) * S::LDV + 4 * (i & 3);
 #pragma unroll
     for (int s = 0; s < S::NB; ++s) {
-        s16x4_t va;
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk)
-            va[kk] = static_cast<short>(vs[(4 * g + kk) * S::LDW + 16 * s + i]);
-        acc[s] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pb, acc[s] * corr, 0, 0, 0);
+        const s16x4_t va = lds_read_tr16(vt + 16 * s);
+        acc[s] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pb, acc[s], 0, 0, 0);
     }
     __builtin_amdgcn_wave_barrier();
 }
@@ -214,11 +279,14 @@ __device__ __forceinline__ void store_tile_rows(void* dst, int64_t off, const f3
     *reinterpret_cast<uint2*>(static_cast<uint16_t*>(dst) + off) = w;
 }
 
+// At least 3 waves per SIMD: at D = 128 the compiler would otherwise keep
+// the accumulators twice (VGPR copies of MFMA results in AGPRs) and stop at 2;
+// with the target it keeps them in VGPRs only, without spilling.
 template <int D>
-__global__ __launch_bounds__(kBlock) void gt_bs_fwd(BsFwdArgs a)
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) void gt_bs_fwd(BsFwdArgs a)
 {
     using S = Shape<D>;
-    __shared__ __attribute__((aligned(16))) uint16_t vs_all[kWavesPerBlock][16 * S::LDW];
+    __shared__ __attribute__((aligned(16))) uint16_t vs_all[kWavesPerBlock][16 * S::LDV];
     const int64_t br = logical_block();
     if (br >= a.n_tile_rows) return;          // the whole workgroup leaves; no barrier follows
     const int w = wave_id();
@@ -254,8 +322,10 @@ __global__ __launch_bounds__(kBlock) void gt_bs_fwd(BsFwdArgs a)
 #pragma unroll
         for (int s = 0; s < S::NB; ++s) acc[s] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-        // pipeline: descriptions two tiles ahead, data one tile ahead
-        FwdTile<D> next;
+        // pipeline: descriptions two tiles ahead; the data of tile k+1 is
+        // loaded into the tile registers as soon as phase A of tile k has
+        // consumed them, and arrives during phase B
+        FwdTile<D> tile;
         RowRef rnext{0, 0};
         int32_t col2 = 0;
         uint32_t word2 = 0;
@@ -264,18 +334,19 @@ __global__ __launch_bounds__(kBlock) void gt_bs_fwd(BsFwdArgs a)
             uint32_t w0;
             tiles.fetch(0, i, c0, w0);
             rnext = tiles.decode(0, i, g, c0, w0);
-            next.load(a.K, a.V, rnext.src * HD + hoff, g);
+            tile.load(a.K, a.V, rnext.src * HD + hoff, __shfl(rnext.src, vrow(l)) * HD + hoff, g, l);
         }
         if (nt > 1) tiles.fetch(1, i, col2, word2);
         for (int64_t k = 0; k < nt; ++k) {
-            const FwdTile<D> cur = next;
             const uint32_t valid = rnext.valid;
+            const f32x4_t st = fwd_phase_a<D>(tile, qf, vs, l);
             if (k + 1 < nt) {
                 rnext = tiles.decode(k + 1, i, g, col2, word2);
                 if (k + 2 < nt) tiles.fetch(k + 2, i, col2, word2);
-                next.load(a.K, a.V, rnext.src * HD + hoff, g);
+                tile.load(a.K, a.V, rnext.src * HD + hoff, __shfl(rnext.src, vrow(l)) * HD + hoff,
+                          g, l);
             }
-            fwd_compute<D>(cur, valid, qf, m, lsum, acc, vs, a.scale2, i, g);
+            fwd_phase_b<D>(st, valid, m, lsum, acc, vs, a.scale2, i, g);
         }
 
         if (row_ok) {
@@ -329,15 +400,17 @@ struct RowBwdTile {
 
 // Tile-row step: rows i = l%16, columns 4g..4g+3 in this lane;
 // dS = P (dP - Delta_i) and dQ^T += K^T dS^T (K transposed through LDS).
+// Phase A consumes the tile registers (S, dP; K into LDS); phase B forms dS
+// and accumulates from LDS, while the next tile's loads refill the registers.
 template <int D>
-__device__ __forceinline__ void row_bwd_compute(const RowBwdTile<D>& tl, uint32_t valid,
+__device__ __forceinline__ void row_bwd_phase_a(const RowBwdTile<D>& tl,
                                                 const bf16x8_t (&qf)[Shape<D>::KS],
-                                                const bf16x8_t (&df)[Shape<D>::KS], float lse2,
-                                                float delta, f32x4_t (&acc)[Shape<D>::NB],
-                                                uint16_t* ks, float scale2, int i, int g)
+                                                const bf16x8_t (&df)[Shape<D>::KS], f32x4_t& st,
+                                                f32x4_t& dp, uint16_t* ks, int i, int g)
 {
     using S = Shape<D>;
-    f32x4_t st = {0.f, 0.f, 0.f, 0.f}, dp = {0.f, 0.f, 0.f, 0.f};
+    st = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    dp = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < S::KS; ++s) {
         st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, tl.kf[s]), qf[s],
@@ -345,9 +418,16 @@ __device__ __forceinline__ void row_bwd_compute(const RowBwdTile<D>& tl, uint32_
         dp = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, tl.vf[s]), df[s],
                                                      dp, 0, 0, 0);
     }
-#pragma unroll
-    for (int s = 0; s < S::KS; ++s)
-        *reinterpret_cast<Frag*>(ks + i * S::LDW + 32 * s + 8 * g) = tl.kf[s];
+    store_operand_tile<D>(ks, tl.kf, i, g);
+}
+
+template <int D>
+__device__ __forceinline__ void row_bwd_phase_b(const f32x4_t& st, const f32x4_t& dp,
+                                                uint32_t valid, float lse2, float delta,
+                                                f32x4_t (&acc)[Shape<D>::NB], const uint16_t* ks,
+                                                float scale2, int i, int g)
+{
+    using S = Shape<D>;
     short dsb[4];
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
@@ -356,22 +436,20 @@ __device__ __forceinline__ void row_bwd_compute(const RowBwdTile<D>& tl, uint32_
     }
     const s16x4_t b = {dsb[0], dsb[1], dsb[2], dsb[3]};
     __builtin_amdgcn_wave_barrier();
+    const uint16_t* kt = operand_tr_base<D>(ks, i, g);
 #pragma unroll
     for (int s = 0; s < S::NB; ++s) {
-        s16x4_t ka;
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk)
-            ka[kk] = static_cast<short>(ks[(4 * g + kk) * S::LDW + 16 * s + i]);
+        const s16x4_t ka = lds_read_tr16(kt + 16 * s);   // K[4g + kk][16s + i], kk = 0..3
         acc[s] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ka, b, acc[s], 0, 0, 0);
     }
     __builtin_amdgcn_wave_barrier();
 }
 
 template <int D>
-__global__ __launch_bounds__(kBlock) void gt_bs_bwd_rows(BsBwdArgs a)
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) void gt_bs_bwd_rows(BsBwdArgs a)
 {
     using S = Shape<D>;
-    __shared__ __attribute__((aligned(16))) uint16_t ks_all[kWavesPerBlock][16 * S::LDW];
+    __shared__ __attribute__((aligned(16))) uint16_t ks_all[kWavesPerBlock][16 * S::LDV];
     const int64_t br = logical_block();
     if (br >= a.n_blocks) return;
     const int w = wave_id();
@@ -418,8 +496,9 @@ __global__ __launch_bounds__(kBlock) void gt_bs_bwd_rows(BsBwdArgs a)
 #pragma unroll
         for (int s = 0; s < S::NB; ++s) acc[s] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-        // pipeline: descriptions two tiles ahead, data one tile ahead
-        RowBwdTile<D> next;
+        // pipeline: descriptions two tiles ahead; tile k+1's data refills the
+        // tile registers once phase A of tile k has consumed them
+        RowBwdTile<D> tile;
         RowRef rnext{0, 0};
         int32_t col2 = 0;
         uint32_t word2 = 0;
@@ -428,18 +507,19 @@ __global__ __launch_bounds__(kBlock) void gt_bs_bwd_rows(BsBwdArgs a)
             uint32_t w0;
             tiles.fetch(0, i, c0, w0);
             rnext = tiles.decode(0, i, g, c0, w0);
-            next.load(a.K, a.V, rnext.src * HD + hoff, g);
+            tile.load(a.K, a.V, rnext.src * HD + hoff, g);
         }
         if (nt > 1) tiles.fetch(1, i, col2, word2);
         for (int64_t k = 0; k < nt; ++k) {
-            const RowBwdTile<D> cur = next;
             const uint32_t valid = rnext.valid;
+            f32x4_t st, dp;
+            row_bwd_phase_a<D>(tile, qf, df, st, dp, ks, i, g);
             if (k + 1 < nt) {
                 rnext = tiles.decode(k + 1, i, g, col2, word2);
                 if (k + 2 < nt) tiles.fetch(k + 2, i, col2, word2);
-                next.load(a.K, a.V, rnext.src * HD + hoff, g);
+                tile.load(a.K, a.V, rnext.src * HD + hoff, g);
             }
-            row_bwd_compute<D>(cur, valid, qf, df, lse2, dsum, acc, ks, a.scale2, i, g);
+            row_bwd_phase_b<D>(st, dp, valid, lse2, dsum, acc, ks, a.scale2, i, g);
         }
         if (row_ok) {
 #pragma unroll
@@ -529,16 +609,19 @@ struct ColBwdTile {
 // Tile-column step: S = Q K^T and dP = dO V^T in the lane layout of rows
 // 4g..4g+3, column l%16; dK^T += Q^T dS, dV^T += dO^T P (Q and dO transposed
 // through LDS).
+// Phase A consumes the tile registers (S, dP; Q and dO into LDS); phase B
+// forms P and dS and accumulates from LDS while the next tile's loads refill
+// the registers (the row statistics and edge bits are kept aside).
 template <int D>
-__device__ __forceinline__ void col_bwd_compute(const ColBwdTile<D>& tl,
+__device__ __forceinline__ void col_bwd_phase_a(const ColBwdTile<D>& tl,
                                                 const bf16x8_t (&kf)[Shape<D>::KS],
-                                                const bf16x8_t (&vf)[Shape<D>::KS],
-                                                f32x4_t (&dk)[Shape<D>::NB],
-                                                f32x4_t (&dv)[Shape<D>::NB], uint16_t* qs,
-                                                uint16_t* os, float scale2, int c, int g)
+                                                const bf16x8_t (&vf)[Shape<D>::KS], f32x4_t& sc,
+                                                f32x4_t& dp, uint16_t* qs, uint16_t* os, int c,
+                                                int g)
 {
     using S = Shape<D>;
-    f32x4_t sc = {0.f, 0.f, 0.f, 0.f}, dp = {0.f, 0.f, 0.f, 0.f};
+    sc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    dp = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < S::KS; ++s) {
         sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, tl.qa[s]), kf[s],
@@ -546,31 +629,37 @@ __device__ __forceinline__ void col_bwd_compute(const ColBwdTile<D>& tl,
         dp = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, tl.oa[s]), vf[s],
                                                      dp, 0, 0, 0);
     }
-#pragma unroll
-    for (int s = 0; s < S::KS; ++s) {
-        *reinterpret_cast<Frag*>(qs + c * S::LDW + 32 * s + 8 * g) = tl.qa[s];
-        *reinterpret_cast<Frag*>(os + c * S::LDW + 32 * s + 8 * g) = tl.oa[s];
-    }
+    store_operand_tile<D>(qs, tl.qa, c, g);
+    store_operand_tile<D>(os, tl.oa, c, g);
+}
+
+template <int D>
+__device__ __forceinline__ void col_bwd_phase_b(const f32x4_t& sc, const f32x4_t& dp,
+                                                const RowStat (&rs)[4], uint32_t valid,
+                                                f32x4_t (&dk)[Shape<D>::NB],
+                                                f32x4_t (&dv)[Shape<D>::NB], const uint16_t* qs,
+                                                const uint16_t* os, float scale2, int c, int g)
+{
+    using S = Shape<D>;
     short pb[4], db[4];
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-        const float p = ((tl.valid >> k) & 1u) ? fast_exp2(sc[k] * scale2 - tl.st[k].lse2) : 0.f;
+        const float p = ((valid >> k) & 1u) ? fast_exp2(sc[k] * scale2 - rs[k].lse2) : 0.f;
         pb[k] = bf16_bits(p);
-        db[k] = bf16_bits(p * (dp[k] - tl.st[k].delta));
+        db[k] = bf16_bits(p * (dp[k] - rs[k].delta));
     }
     const s16x4_t P = {pb[0], pb[1], pb[2], pb[3]};
     const s16x4_t Sd = {db[0], db[1], db[2], db[3]};
     __builtin_amdgcn_wave_barrier();
+    const uint16_t* qt = operand_tr_base<D>(qs, c, g);
+    const uint16_t* ot = operand_tr_base<D>(os, c, g);
 #pragma unroll
     for (int s = 0; s < S::NB; ++s) {
-        s16x4_t qt, ot;
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-            qt[kk] = static_cast<short>(qs[(4 * g + kk) * S::LDW + 16 * s + c]);
-            ot[kk] = static_cast<short>(os[(4 * g + kk) * S::LDW + 16 * s + c]);
-        }
-        dk[s] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(qt, Sd, dk[s], 0, 0, 0);
-        dv[s] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ot, P, dv[s], 0, 0, 0);
+        // Q[4g + kk][16s + c] and dO[4g + kk][16s + c], kk = 0..3
+        dk[s] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(lds_read_tr16(qt + 16 * s), Sd, dk[s],
+                                                          0, 0, 0);
+        dv[s] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(lds_read_tr16(ot + 16 * s), P, dv[s],
+                                                          0, 0, 0);
     }
     __builtin_amdgcn_wave_barrier();
 }
@@ -579,8 +668,8 @@ template <int D>
 __global__ __launch_bounds__(kBlock) void gt_bs_bwd_cols(BsBwdArgs a)
 {
     using S = Shape<D>;
-    __shared__ __attribute__((aligned(16))) uint16_t qs_all[kWavesPerBlock][16 * S::LDW];
-    __shared__ __attribute__((aligned(16))) uint16_t os_all[kWavesPerBlock][16 * S::LDW];
+    __shared__ __attribute__((aligned(16))) uint16_t qs_all[kWavesPerBlock][16 * S::LDV];
+    __shared__ __attribute__((aligned(16))) uint16_t os_all[kWavesPerBlock][16 * S::LDV];
     const int64_t bc = logical_block();
     if (bc >= a.n_blocks) return;
     const int w = wave_id();
@@ -626,23 +715,27 @@ __global__ __launch_bounds__(kBlock) void gt_bs_bwd_cols(BsBwdArgs a)
             dk[s] = f32x4_t{0.f, 0.f, 0.f, 0.f};
             dv[s] = f32x4_t{0.f, 0.f, 0.f, 0.f};
         }
-        // pipeline: descriptions two tiles ahead, data one tile ahead
-        ColBwdTile<D> next;
+        // pipeline: descriptions two tiles ahead; tile k+1's data refills the
+        // tile registers once phase A of tile k has consumed them
+        ColBwdTile<D> tile;
         int32_t t2 = 0, d2 = 0;
         if (nt > 0) {
             int32_t t0, d0;
             T.fetch(0, c, t0, d0);
-            next.load(T, 0, t0, d0, a.Q, a.dO, HD, hoff, c, g);
+            tile.load(T, 0, t0, d0, a.Q, a.dO, HD, hoff, c, g);
         }
         if (nt > 1) T.fetch(1, c, t2, d2);
         for (int64_t k = 0; k < nt; ++k) {
-            const ColBwdTile<D> cur = next;
+            const uint32_t valid = tile.valid;
+            const RowStat rs[4] = {tile.st[0], tile.st[1], tile.st[2], tile.st[3]};
+            f32x4_t sc, dp;
+            col_bwd_phase_a<D>(tile, kf, vf, sc, dp, qs, os, c, g);
             if (k + 1 < nt) {
                 const int32_t t1 = t2, d1 = d2;
                 if (k + 2 < nt) T.fetch(k + 2, c, t2, d2);
-                next.load(T, k + 1, t1, d1, a.Q, a.dO, HD, hoff, c, g);
+                tile.load(T, k + 1, t1, d1, a.Q, a.dO, HD, hoff, c, g);
             }
-            col_bwd_compute<D>(cur, kf, vf, dk, dv, qs, os, a.scale2, c, g);
+            col_bwd_phase_b<D>(sc, dp, rs, valid, dk, dv, qs, os, a.scale2, c, g);
         }
         if (j_ok) {
 #pragma unroll
