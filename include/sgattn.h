@@ -16,7 +16,9 @@
  * weight is written to device memory; the backward recomputes the weights
  * from one log-sum-exp value per (node, head) (Yandex Research blog "On
  * efficient scaling of GNNs via IO-aware layer implementations", paragraph on
- * attention-based architectures).
+ * attention-based architectures). It also computes the reduction-based
+ * aggregation family of the IO-aware layers paper (Abstract): min or max
+ * pooling of the neighbour rows, reduce_fwd / reduce_bwd below.
  *
  * Conventions for every entry point:
  *   - Graph: CSR by destination. Row i holds edges e in [rowptr[i],
@@ -26,7 +28,11 @@
  *   - Features: [n, H, D] row-major (node, head, channel), element type fp32
  *     or bf16, base address 16-byte aligned. H in 1..16, D in {32, 64, 128}.
  *     Accumulation is fp32; outputs and gradients are written in the input
- *     type, rounded to nearest even. lse is fp32 [n, H], natural log.
+ *     type, rounded to nearest even. lse is fp32 [n, H], natural log. (The
+ *     aggregation takes [n, F] rows instead; see reduce_fwd.)
+ *   - Graph capture: the compute calls allocate nothing, synchronise nothing
+ *     and issue no memset, so a sequence of them can be captured into a HIP
+ *     graph and replayed (same buffers, same plan).
  *   - Memory: every tensor, plan buffer and workspace pointer is a device
  *     pointer owned by the caller. The library never allocates or frees device
  *     memory. Host arrays given to sgat_plan_create are copied.
