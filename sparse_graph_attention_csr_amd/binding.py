@@ -165,6 +165,41 @@ def _shape(t):
     return t.shape
 
 
+def _expect(name, t, shape, dtype, device):
+    """The C ABI receives bare pointers and cannot check sizes, so every tensor
+    argument is checked here: shape, dtype, device and contiguity."""
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _check_call(plan, rowptr, colidx, ws, lead, name="q"):
+    """Common checks: the lead tensor is on a GPU and has the plan's n rows;
+    the graph arrays are the plan's device CSR; the workspace is on the GPU."""
+    import torch
+    dev = lead.device
+    if lead.shape[0] != plan.n:
+        raise ValueError(f"{name} has {lead.shape[0]} rows, the plan {plan.n}")
+    if dev.type != "cuda":
+        raise ValueError(f"{name} is on {dev}: the library runs on the GPU")
+    _expect("rowptr", rowptr, (plan.n + 1,), torch.int64, dev)
+    _expect("colidx", colidx, (plan.nnz,), torch.int32, dev)
+    if ws is not None and (ws.device != dev or not ws.is_contiguous()):
+        raise ValueError("the workspace must be a contiguous tensor on the same GPU")
+    return dev
+
+
+def _ws_bytes(ws):
+    return 0 if ws is None else ws.numel() * ws.element_size()
+
+
 # ---------------------------------------------------------------------------
 # plan
 # ---------------------------------------------------------------------------
@@ -242,40 +277,65 @@ class Plan:
 # ---------------------------------------------------------------------------
 
 def gt_fwd(plan: Plan, rowptr, colidx, q, k, v, out, lse, ws, use_tiles=False, stream=None):
+    import torch
     n, H, D = _shape(q)
+    dev = _check_call(plan, rowptr, colidx, ws, q)
+    for nm, t in (("q", q), ("k", k), ("v", v), ("out", out)):
+        _expect(nm, t, q.shape, q.dtype, dev)
+    _expect("lse", lse, (n, H), torch.float32, dev)
     _check("gt_fwd", lib().gt_fwd(
         plan.handle, plan.n, plan.nnz, _ptr(rowptr), _ptr(colidx), H, D, _dtype_code(q),
         _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),
-        _ptr(ws), 0 if ws is None else ws.numel(), int(bool(use_tiles)), _stream(stream)))
+        _ptr(ws), _ws_bytes(ws), int(bool(use_tiles)), _stream(stream)))
 
 
 def gt_bwd(plan: Plan, rowptr, colidx, q, k, v, out, lse, dout, dq, dk, dv, ws,
            use_tiles=False, stream=None):
+    import torch
     n, H, D = _shape(q)
+    dev = _check_call(plan, rowptr, colidx, ws, q)
+    for nm, t in (("q", q), ("k", k), ("v", v), ("out", out), ("dout", dout), ("dq", dq),
+                  ("dk", dk), ("dv", dv)):
+        _expect(nm, t, q.shape, q.dtype, dev)
+    _expect("lse", lse, (n, H), torch.float32, dev)
     _check("gt_bwd", lib().gt_bwd(
         plan.handle, plan.n, plan.nnz, _ptr(rowptr), _ptr(colidx), H, D, _dtype_code(q),
         _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(dout),
-        _ptr(dq), _ptr(dk), _ptr(dv), _ptr(ws), 0 if ws is None else ws.numel(),
+        _ptr(dq), _ptr(dk), _ptr(dv), _ptr(ws), _ws_bytes(ws),
         int(bool(use_tiles)), _stream(stream)))
 
 
 def gat_fwd(plan: Plan, rowptr, colidx, x_dst, x_nbr, a, negative_slope, out, lse, ws,
             stream=None):
+    import torch
     n, H, D = _shape(x_dst)
+    dev = _check_call(plan, rowptr, colidx, ws, x_dst, "x_dst")
+    for nm, t in (("x_nbr", x_nbr), ("out", out)):
+        _expect(nm, t, x_dst.shape, x_dst.dtype, dev)
+    _expect("a", a, (H, D), torch.float32, dev)
+    _expect("lse", lse, (n, H), torch.float32, dev)
     _check("gat_fwd", lib().gat_fwd(
         plan.handle, plan.n, plan.nnz, _ptr(rowptr), _ptr(colidx), H, D, _dtype_code(x_dst),
         _ptr(x_dst), _ptr(x_nbr), _ptr(a), float(negative_slope), _ptr(out), _ptr(lse),
-        _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream)))
+        _ptr(ws), _ws_bytes(ws), _stream(stream)))
 
 
 def gat_bwd(plan: Plan, rowptr, colidx, x_dst, x_nbr, a, negative_slope, out, lse, dout,
             dx_dst, dx_nbr, da, ws, stream=None):
+    import torch
     n, H, D = _shape(x_dst)
+    dev = _check_call(plan, rowptr, colidx, ws, x_dst, "x_dst")
+    for nm, t in (("x_nbr", x_nbr), ("out", out), ("dout", dout), ("dx_dst", dx_dst),
+                  ("dx_nbr", dx_nbr)):
+        _expect(nm, t, x_dst.shape, x_dst.dtype, dev)
+    _expect("a", a, (H, D), torch.float32, dev)
+    _expect("da", da, (H, D), torch.float32, dev)
+    _expect("lse", lse, (n, H), torch.float32, dev)
     _check("gat_bwd", lib().gat_bwd(
         plan.handle, plan.n, plan.nnz, _ptr(rowptr), _ptr(colidx), H, D, _dtype_code(x_dst),
         _ptr(x_dst), _ptr(x_nbr), _ptr(a), float(negative_slope), _ptr(out), _ptr(lse),
         _ptr(dout), _ptr(dx_dst), _ptr(dx_nbr), _ptr(da), _ptr(ws),
-        0 if ws is None else ws.numel(), _stream(stream)))
+        _ws_bytes(ws), _stream(stream)))
 
 
 def _shape2(t):
@@ -286,20 +346,27 @@ def _shape2(t):
 
 def reduce_fwd(plan: Plan, rowptr, colidx, x, op, out, arg, ws, stream=None):
     """op: REDUCE_MIN / REDUCE_MAX (or "min" / "max"); arg may be None."""
+    import torch
     n, F = _shape2(x)
+    dev = _check_call(plan, rowptr, colidx, ws, x, "x")
+    _expect("out", out, x.shape, x.dtype, dev)
+    if arg is not None:
+        _expect("arg", arg, (n, F), torch.int32, dev)
     op = REDUCE_OPS.get(op, op)
     _check("reduce_fwd", lib().reduce_fwd(
         plan.handle, plan.n, plan.nnz, _ptr(rowptr), _ptr(colidx), F, _dtype_code(x), int(op),
-        _ptr(x), _ptr(out), _ptr(arg), _ptr(ws), 0 if ws is None else ws.numel(),
-        _stream(stream)))
+        _ptr(x), _ptr(out), _ptr(arg), _ptr(ws), _ws_bytes(ws), _stream(stream)))
 
 
 def reduce_bwd(plan: Plan, rowptr, colidx, arg, dout, dx, ws, stream=None):
+    import torch
     n, F = _shape2(dout)
+    dev = _check_call(plan, rowptr, colidx, ws, dout, "dout")
+    _expect("arg", arg, (n, F), torch.int32, dev)
+    _expect("dx", dx, dout.shape, dout.dtype, dev)
     _check("reduce_bwd", lib().reduce_bwd(
         plan.handle, plan.n, plan.nnz, _ptr(rowptr), _ptr(colidx), F, _dtype_code(dout),
-        _ptr(arg), _ptr(dout), _ptr(dx), _ptr(ws), 0 if ws is None else ws.numel(),
-        _stream(stream)))
+        _ptr(arg), _ptr(dout), _ptr(dx), _ptr(ws), _ws_bytes(ws), _stream(stream)))
 
 
 # ---------------------------------------------------------------------------

@@ -177,3 +177,20 @@ def test_plan_rejects_nnz_beyond_int32():
     assert B.lib().sgat_plan_create(1, 1 << 31, rp.ctypes.data, ci.ctypes.data, None,
                                     ctypes.byref(out)) == 1
     assert not out.value
+
+
+def test_binding_refuses_host_tensors_before_any_call(plan):
+    """The binding checks tensor arguments itself (the ABI sees bare pointers):
+    host tensors never reach the library."""
+    import torch
+    n, H, D = plan.n, 2, 32
+    q = torch.zeros(n, H, D)
+    lse = torch.zeros(n, H)
+    rp = torch.zeros(n + 1, dtype=torch.int64)
+    ci = torch.zeros(plan.nnz, dtype=torch.int32)
+    with pytest.raises(ValueError, match="GPU"):
+        B.gt_fwd(plan, rp, ci, q, q, q, q.clone(), lse, None)
+    with pytest.raises(ValueError, match="GPU"):
+        B.reduce_fwd(plan, rp, ci, torch.zeros(n, 64), "min", torch.zeros(n, 64), None, None)
+    with pytest.raises(ValueError, match="rows"):
+        B.gt_fwd(plan, rp, ci, torch.zeros(n + 1, H, D), q, q, q, lse, None)

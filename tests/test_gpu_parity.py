@@ -190,3 +190,32 @@ def test_locality_order_gives_identical_results():
         res.append([host(x) for x in (out, lse, *r.gt_bwd(q, k, v, out, lse, do))])
     for x, y in zip(*res):
         assert np.array_equal(x, y)
+
+
+def test_binding_rejects_mismatched_tensors():
+    """Shapes, dtypes, contiguity and workspace size are checked before any
+    launch, so a wrong argument raises instead of reading out of bounds."""
+    note("binding argument checks")
+    import torch
+    from sparse_graph_attention_csr_amd import binding as B
+    rp, ci = graph(23)
+    n, H, D = rp.size - 1, 2, 64
+    g = B.DeviceGraph(rp, ci)
+    q = torch.randn(n, H, D, device="cuda")
+    out = torch.empty_like(q)
+    lse = torch.empty(n, H, device="cuda")
+    ws = g.workspace(B.OP_GT_FWD, H, D, B.F32)
+    with pytest.raises(ValueError, match="k has shape"):
+        B.gt_fwd(g.plan, g.rowptr, g.colidx, q, q[:, :, :32].contiguous(), q, out, lse, ws)
+    with pytest.raises(TypeError, match="lse"):
+        B.gt_fwd(g.plan, g.rowptr, g.colidx, q, q, q, out, lse.double(), ws)
+    with pytest.raises(TypeError, match="colidx"):
+        B.gt_fwd(g.plan, g.rowptr, g.colidx.long(), q, q, q, out, lse, ws)
+    with pytest.raises(ValueError, match="contiguous"):
+        B.gt_fwd(g.plan, g.rowptr, g.colidx, q, q, q, out.transpose(1, 2).contiguous()
+                 .transpose(1, 2), lse, ws)
+    if ws.numel() > 256:
+        with pytest.raises(B.SgatError):
+            B.gt_fwd(g.plan, g.rowptr, g.colidx, q, q, q, out, lse, ws[:ws.numel() - 256])
+    B.gt_fwd(g.plan, g.rowptr, g.colidx, q, q, q, out, lse, ws)     # the correct call runs
+    torch.cuda.synchronize()
