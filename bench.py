@@ -190,7 +190,7 @@ def cpu_baseline(w, seconds: float):
         r = int(min(n, np.searchsorted(rp, target)))
         e, t = run(r)
     rate = e * spec.heads / t / 1e9
-    return {"value": rate, "unit": "GEdge*head/s", "cores": oracle.num_threads(),
+    return {"value": rate, "unit": "GEdge\u00b7head/s", "cores": oracle.num_threads(),
             "kind": "oracle",
             "sample": f"destination rows 0..{r - 1} of {n} ({e} of {int(rp[-1])} edges), "
                       f"{spec.passes}, fp64, {t:.1f} s"}
@@ -463,9 +463,9 @@ def main():
                 "algorithmic_bytes": dk["algorithmic_bytes"]}
 
     line = {
-        "metric": "fused graph-attn fwd+bwd GEdge*head/s; achieved HBM GB/s vs MI355X peak",
+        "metric": "fused graph-attn fwd+bwd GEdge\u00b7head/s; achieved HBM GB/s vs MI355X peak",
         "value": round(value, 4),
-        "unit": "GEdge*head/s",
+        "unit": "GEdge\u00b7head/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
