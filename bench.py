@@ -82,6 +82,22 @@ def mfma_flops(kernel: str, H: int, D: int, tw: dict) -> float | None:
     return float((tw["tiles"] + tw["pseudo_tiles"]) * H * per * (2 * 16 * 16 * D))
 
 
+def gat_record_bytes(H: int, D: int, b: int) -> int:
+    """Bytes per edge of the records the GATv2 CSR backward pass leaves for the
+    transposed pass: per head group of hg heads (the lanes of one edge group)
+    a float2 (p, dE) per head and one byte of sign bits per lane, in whole
+    dword pairs."""
+    vec = 16 // b
+    sph = D // vec
+    want = min(H, 64 // sph)
+    hg = 1
+    while hg < want:
+        hg *= 2
+    n_hg = -(-H // hg)
+    lanes = hg * sph
+    return n_hg * 4 * (2 * hg + ((lanes // 4 + 1) & ~1))
+
+
 def algorithmic_bytes(kernel: str, n: int, e: int, H: int, D: int, b: int,
                       tw: dict | None = None) -> int | None:
     """Bytes a kernel must move: neighbour-row gathers per edge plus the
@@ -112,10 +128,11 @@ def algorithmic_bytes(kernel: str, n: int, e: int, H: int, D: int, b: int,
         "gt_bwd_rows": (R + 4 + 4 * H, R + 8),
         # Xt_j and colidx per edge; Xs_i read, out_i, lse_i written
         "gat_fwd_rows": (R + 4, 2 * R + 4 * H + 8),
-        # Xt_j, colidx per edge; Xs_i, dO_i, O_i, lse_i read, dXs_i, (lse, Delta) written
-        "gat_bwd_rows": (R + 4, 4 * R + 12 * H + 8),
-        # Xs_i, dO_i, (lse_i, Delta_i), rowidx per edge; Xt_j read, dXt_j written
-        "gat_bwd_cols": (2 * R + 8 * H + 4, 2 * R + 8),
+        # Xt_j, colidx read and the edge record written per edge; Xs_i, dO_i,
+        # O_i, lse_i read, dXs_i written
+        "gat_bwd_rows": (R + 4 + gat_record_bytes(H, D, b), 4 * R + 4 * H + 8),
+        # dO_i, rowidx, edge id and the edge record per edge; dXt_j written
+        "gat_bwd_cols": (R + 8 + gat_record_bytes(H, D, b), R + 8),
         # min/max aggregation (H = 1, D = F): X_j and colidx per edge; out_i and
         # the int32 winners arg_i written per node
         "reduce_fwd_rows": (R + 4, R + 4 * D),

@@ -130,7 +130,7 @@ Layout ws_layout(const Plan& p, int op, int H, int D, int dt)
         sz[4] = static_cast<size_t>(p.nnz) * H * 4;                 // dS per edge
         break;
     case SGAT_OP_GAT_BWD:
-        sz[0] = static_cast<size_t>(p.n) * H * 8;                   // stats
+        sz[0] = static_cast<size_t>(p.nnz) * gat_edge_record_dwords(dt, D, H) * 4; // edge records
         sz[1] = static_cast<size_t>(p.row_slots) * HD * 4;          // dXs partials
         sz[2] = static_cast<size_t>(p.col_slots) * HD * 4;          // dXt partials
         sz[4] = static_cast<size_t>(gat_bwd_row_blocks(p)) * HD * 4; // da partials
@@ -308,8 +308,8 @@ int gat_bwd(const sgat_plan* plan, int64_t n, int64_t nnz, const int64_t* rowptr
     Layout L;
     if ((rc = check_ws(plan->p, SGAT_OP_GAT_BWD, H, D, dtype, ws, ws_bytes, L))) return rc;
     if (n == 0) return launch_da_zero(da, H * D, static_cast<hipStream_t>(stream));
-    BwdWs w{at<void>(ws, L.off[0]), at<float>(ws, L.off[1]), at<float>(ws, L.off[2]), nullptr,
-            at<float>(ws, L.off[4]), nullptr};
+    BwdWs w{nullptr, at<float>(ws, L.off[1]), at<float>(ws, L.off[2]), nullptr,
+            at<float>(ws, L.off[4]), nullptr, at<void>(ws, L.off[0])};
     return launch_gat_bwd(plan->p, H, D, dtype, colidx, x_dst, x_nbr, a, negative_slope, out, lse,
                           dout, dx_dst, dx_nbr, da, w, static_cast<hipStream_t>(stream));
 }

@@ -146,6 +146,14 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 // Wave index inside the block as a uniform (scalar) value.
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 
+// LDS traffic of one wave stays in issue order; this keeps the compiler from
+// moving accesses across the phase boundaries either.
+__device__ __forceinline__ void wave_lds_fence()
+{
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+}
+
 // Logical block index. Hardware hands consecutive workgroups to the XCDs in
 // turn; remap so that each XCD receives runs of kXcdWindow consecutive logical
 // blocks (neighbouring rows share K/V rows in its L2). The grid is a multiple

@@ -516,6 +516,18 @@ __global__ __launch_bounds__(kBlock) void gt_bwd_rows(GtBwdRowArgs a)
 
 // GATv2 CSR pass: dXs and the da partials. Grid-stride over items with a
 // fixed grid so the da partials are one per workgroup; blockIdx.y = head group.
+// It also leaves one record per (head group, edge) with what the transposed
+// pass needs of the edge, so that pass gathers neither Xs_i nor row
+// statistics: for head h of the group the weight p and dE (float2 at dword
+// 2h), then from byte 8*hg on one byte per lane of the edge group (lane
+// position q covers channels q*VEC .. q*VEC+VEC-1 of the group's hg*D), bit k
+// set where z > 0 on channel q*VEC + k. Records of head group g start at
+// g * nnz records; each is an even number of dwords.
+__host__ __device__ constexpr int gat_rec_dwords(int hg, int lanes)
+{
+    return 2 * hg + ((lanes / 4 + 1) & ~1);
+}
+
 struct GatBwdRowArgs {
     const sgat_work_item* items;
     int64_t n_items;
@@ -525,7 +537,8 @@ struct GatBwdRowArgs {
     const float* att;
     float slope;
     const float* lse;
-    RowStat* stats;
+    uint32_t* edge_rec;   // [n_hg][nnz][gat_rec_dwords]
+    int64_t nnz;
     void* dXs;
     float* part;
     float* da_part;   // [gridDim.x][H*D]
@@ -536,11 +549,18 @@ __global__ __launch_bounds__(kBlock) void gat_bwd_rows(GatBwdRowArgs a)
 {
     using G = Geo<DT, D, EPW>;
     constexpr int VEC = G::VEC;
+    constexpr int RS = gat_rec_dwords(G::HG, G::LPE);
     __shared__ float red[kWavesPerBlock][G::LPE * VEC];
+    // records of one 64-edge block, written out contiguously once per block
+    // (per-edge global stores inside the loop would make each wait for the
+    // next loads also wait for them)
+    __shared__ __align__(16) uint32_t recbuf[kWavesPerBlock][kWave * RS];
     const int hg = blockIdx.y;
     const G g(hg, a.H);
     const int64_t HD = static_cast<int64_t>(a.H) * D;
     const int wid = wave_id();
+    const int hl = g.pos / G::SPH;   // head within the group
+    uint32_t* const lrec = recbuf[wid];
 
     // g_d = a_d LeakyReLU'(z_d): a_d for z_d > 0, a_d * slope otherwise; then
     // a_d LeakyReLU(z_d) = z_d g_d and the dXs term is dE g_d
@@ -565,11 +585,10 @@ __global__ __launch_bounds__(kBlock) void gat_bwd_rows(GatBwdRowArgs a)
             lse2 = a.lse[static_cast<int64_t>(it.row) * a.H + g.head] * kLog2e;
         }
         const float delta = head_sum<G::SPH>(dot<DT>(dof, of));
-        if ((it.flags & 1) && g.sub == 0 && g.hvalid && g.leader)
-            a.stats[static_cast<int64_t>(it.row) * a.H + g.head] = RowStat{lse2, delta};
 
         float dxs[VEC] = {};
         const int32_t* ci = a.colidx + it.begin;
+        uint32_t* rec = a.edge_rec + (static_cast<int64_t>(hg) * a.nnz + it.begin) * RS;
         for (int base = 0; base < it.len; base += kWave) {
             const int nb = min(kWave, it.len - base);
             const int cj = g.lane < nb ? ci[base + g.lane] : 0;
@@ -599,13 +618,29 @@ __global__ __launch_bounds__(kBlock) void gat_bwd_rows(GatBwdRowArgs a)
                     const float dp = head_sum<G::SPH>(dot<DT>(dof, xf[u]));
                     const float p = ok[u] ? fast_exp2(e2 - lse2) : 0.f;
                     const float dE = p * (dp - delta);
+                    uint32_t zbits = 0;
 #pragma unroll
                     for (int k = 0; k < VEC; ++k) {
                         dxs[k] = fmaf(dE, gz[k], dxs[k]);
                         da[k] = fmaf(dE, z[k] > 0.f ? z[k] : a.slope * z[k], da[k]);
+                        zbits |= (z[k] > 0.f ? 1u : 0u) << k;
+                    }
+                    // t + u*EPW + sub < 64: EPW*U divides the block of 64 edges
+                    uint32_t* lr = lrec + (t + u * EPW + g.sub) * RS;
+                    reinterpret_cast<uint8_t*>(lr + 2 * G::HG)[g.pos] = static_cast<uint8_t>(zbits);
+                    if (g.leader) {
+                        lr[2 * hl] = __float_as_uint(p);
+                        lr[2 * hl + 1] = __float_as_uint(dE);
                     }
                 }
             }
+            wave_lds_fence();
+            {
+                uint2* dst = reinterpret_cast<uint2*>(rec + static_cast<int64_t>(base) * RS);
+                const uint2* src = reinterpret_cast<const uint2*>(lrec);
+                for (int w = g.lane; w < nb * (RS / 2); w += kWave) dst[w] = src[w];
+            }
+            wave_lds_fence();
         }
         if constexpr (EPW > 1) sum_groups<VEC, G::LPE>(dxs);
         if (g.sub == 0 && g.hvalid) grad_store<DT, VEC>(dxs, 1.f, it, HD, g.col, a.dXs, a.part);
@@ -730,14 +765,18 @@ struct GatBwdColArgs {
     int64_t n_units;
     int n_hg, H;
     const int32_t* rowidx;
-    const void *Xs, *Xt, *dO;
+    const int32_t* col_edge;    // CSR edge id of each transposed entry
+    const void* dO;
     const float* att;
     float slope;
-    const RowStat* stats;
+    const uint32_t* edge_rec;   // written by the CSR pass
+    int64_t nnz;
     void* dXt;
     float* part;
 };
 
+// dXt_j = sum over i of p_ij dO_i + dE_ij g_ij, g = a LeakyReLU'(z_ij): the
+// per-edge p, dE and signs of z come from the CSR pass; only dO_i is gathered.
 template <int DT, int D, int EPW, int U>
 __global__ __launch_bounds__(kBlock) void gat_bwd_cols(GatBwdColArgs a)
 {
@@ -750,59 +789,50 @@ __global__ __launch_bounds__(kBlock) void gat_bwd_cols(GatBwdColArgs a)
     const sgat_work_item it = a.items[ii];
     const G g(hg, a.H);
     const int64_t HD = static_cast<int64_t>(a.H) * D;
+    constexpr int RS = gat_rec_dwords(G::HG, G::LPE);
+    const uint32_t* const rbase = a.edge_rec + static_cast<int64_t>(hg) * a.nnz * RS;
+    const int hl = g.pos / G::SPH;
+    const int zl = 2 * G::HG + g.pos / 4, zsh = 8 * (g.pos % 4);   // the lane's sign byte
 
-    // g_d = a_d LeakyReLU'(z_d); a_d LeakyReLU(z_d) = z_d g_d
-    Frag xtf = frag_zero();
-    float xt[VEC] = {}, at[VEC] = {}, as[VEC];
-    if (g.hvalid) {
-        xtf = ldg<DT>(a.Xt, static_cast<int64_t>(it.row) * HD + g.col);
-        ld_f32<VEC>(a.att + g.col, at);
-    }
+    float at[VEC] = {}, as[VEC];
+    if (g.hvalid) ld_f32<VEC>(a.att + g.col, at);
 #pragma unroll
     for (int k = 0; k < VEC; ++k) as[k] = at[k] * a.slope;
-    to_f32<DT>(xtf, xt);
     float dxt[VEC] = {};
     const int32_t* ri = a.rowidx + it.begin;
+    const int32_t* re = a.col_edge + it.begin;
     for (int base = 0; base < it.len; base += kWave) {
         const int nb = min(kWave, it.len - base);
         const int ci = g.lane < nb ? ri[base + g.lane] : 0;
+        const int ce = g.lane < nb ? re[base + g.lane] : 0;
         for (int t = 0; t < nb; t += EPW * U) {
-            Frag sf[U], df[U];
-            RowStat rs[U];
-            bool ok[U];
+            Frag df[U];
+            float2 pd[U];
+            uint32_t zb[U];
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const int e = t + u * EPW + g.sub;
-                ok[u] = e < nb;
                 const int64_t i = bcast<EPW>(ci, e);
-                sf[u] = frag_zero();
+                const int64_t eid = bcast<EPW>(ce, e);
                 df[u] = frag_zero();
-                rs[u] = RowStat{0.f, 0.f};
-                if (ok[u] && g.hvalid) {
-                    sf[u] = ldg<DT>(a.Xs, i * HD + g.col);
+                pd[u] = make_float2(0.f, 0.f);
+                zb[u] = 0;
+                if (e < nb && g.hvalid) {
+                    const uint32_t* r = rbase + eid * RS;
                     df[u] = ldg<DT>(a.dO, i * HD + g.col);
-                    rs[u] = a.stats[i * a.H + g.head];
+                    pd[u] = *reinterpret_cast<const float2*>(r + 2 * hl);
+                    zb[u] = r[zl] >> zsh;
                 }
             }
 #pragma unroll
             for (int u = 0; u < U; ++u) {
-                float xs[VEC], gz[VEC];
-                to_f32<DT>(sf[u], xs);
-                float part = 0.f;
-#pragma unroll
-                for (int k = 0; k < VEC; ++k) {
-                    const float z = xs[k] + xt[k];
-                    gz[k] = z > 0.f ? at[k] : as[k];
-                    part = fmaf(z, gz[k], part);
-                }
-                const float e2 = head_sum<G::SPH>(part) * kLog2e;
-                const float dp = head_sum<G::SPH>(dot<DT>(df[u], xtf));
-                const float p = ok[u] ? fast_exp2(e2 - rs[u].lse2) : 0.f;
-                const float dE = p * (dp - rs[u].delta);
                 float dx[VEC];
                 to_f32<DT>(df[u], dx);
 #pragma unroll
-                for (int k = 0; k < VEC; ++k) dxt[k] = fmaf(p, dx[k], fmaf(dE, gz[k], dxt[k]));
+                for (int k = 0; k < VEC; ++k) {
+                    const float gz = (zb[u] >> k) & 1u ? at[k] : as[k];
+                    dxt[k] = fmaf(pd[u].x, dx[k], fmaf(pd[u].y, gz, dxt[k]));
+                }
             }
         }
     }

@@ -26,13 +26,19 @@ struct FwdWs {
     float* part_ml;    // [row_slots][H][2]
 };
 struct BwdWs {
-    void* stats;       // [n][H] (lse * log2 e, Delta)
+    void* stats;       // [n][H] (lse * log2 e, Delta) (Graph Transformer only)
     float* part_row;   // [row_slots][H*D]
     float* part_col0;  // [col_slots][H*D]
     float* part_col1;  // [col_slots][H*D] (GT only)
     float* da_part;    // [gat_bwd_row_blocks][H*D] (GATv2 only)
     float* ds;         // [nnz][H] dS per edge (Graph Transformer only)
+    void* edge_rec;    // [nnz][gat_edge_record_dwords] (GATv2 only)
 };
+
+// Dwords per edge (over all head groups) of the records the GATv2 CSR
+// backward pass leaves for the transposed pass: (p, dE) per head and one sign
+// bit of z per channel.
+int64_t gat_edge_record_dwords(int dt, int D, int H);
 
 int launch_gt_fwd(const Plan& p, int H, int D, int dt, const int32_t* colidx, const void* Q,
                   const void* K, const void* V, void* out, float* lse, const FwdWs& ws,

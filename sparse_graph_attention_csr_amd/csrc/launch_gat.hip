@@ -102,6 +102,12 @@ int launch_gat_fwd(const Plan& p, int H, int D, int dt, const int32_t* colidx, c
     return SGAT_OK;
 }
 
+int64_t gat_edge_record_dwords(int dt, int D, int H)
+{
+    const Decomp dc = decompose(dt, D, H);
+    return static_cast<int64_t>(dc.n_hg) * gat_rec_dwords(dc.hg, dc.hg * dc.sph);
+}
+
 int launch_gat_bwd(const Plan& p, int H, int D, int dt, const int32_t* colidx, const void* Xs,
                    const void* Xt, const float* att, float slope, const void* O, const float* lse,
                    const void* dO, void* dXs, void* dXt, float* da, const BwdWs& ws,
@@ -120,7 +126,8 @@ int launch_gat_bwd(const Plan& p, int H, int D, int dt, const int32_t* colidx, c
     r.att = att;
     r.slope = slope;
     r.lse = lse;
-    r.stats = static_cast<RowStat*>(ws.stats);
+    r.edge_rec = static_cast<uint32_t*>(ws.edge_rec);
+    r.nnz = p.nnz;
     r.dXs = dXs;
     r.part = ws.part_row;
     r.da_part = ws.da_part;
@@ -131,10 +138,12 @@ int launch_gat_bwd(const Plan& p, int H, int D, int dt, const int32_t* colidx, c
     c.n_hg = dc.n_hg;
     c.H = H;
     c.rowidx = p.dptr<int32_t>(SGAT_ARR_ROWIDX);
-    c.Xs = Xs; c.Xt = Xt; c.dO = dO;
+    c.col_edge = p.dptr<int32_t>(SGAT_ARR_COL_EDGE);
+    c.dO = dO;
     c.att = att;
     c.slope = slope;
-    c.stats = static_cast<const RowStat*>(ws.stats);
+    c.edge_rec = static_cast<const uint32_t*>(ws.edge_rec);
+    c.nnz = p.nnz;
     c.dXt = dXt;
     c.part = ws.part_col0;
 

@@ -261,14 +261,6 @@ __device__ __forceinline__ int wave_inclusive_scan(int x)
     return x;
 }
 
-// LDS traffic of one wave stays in issue order; this keeps the compiler from
-// moving accesses across the phase boundaries either.
-__device__ __forceinline__ void wave_lds_fence()
-{
-    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-}
-
 template <int DT, int NR>
 __global__ __launch_bounds__(kBlock) void reduce_bwd_route(ReduceRouteArgs a)
 {
