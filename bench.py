@@ -98,11 +98,47 @@ def gat_record_bytes(H: int, D: int, b: int) -> int:
     return n_hg * 4 * (2 * hg + ((lanes // 4 + 1) & ~1))
 
 
+# Work items shorter than this many edges at the end of the work list run
+# several to a wavefront (the library's default short-item bound).
+SHORT_ITEM_EDGES = 128
+
+
+def edge_groups(H: int, D: int, b: int) -> int:
+    """Edges a wavefront holds side by side for this layout (64-lane waves,
+    16-byte fragments, head groups of a power of two heads)."""
+    sph = D // (16 // b)
+    want = min(H, 64 // sph)
+    hg = 1
+    while hg < want:
+        hg *= 2
+    return 64 // (hg * sph)
+
+
+def row_item_split(plan) -> dict:
+    """Items and edges of the CSR work list before and from the short suffix
+    (the first item from which every item has fewer than SHORT_ITEM_EDGES)."""
+    import numpy as np
+    from sparse_graph_attention_csr_amd import binding as B
+    ln = plan.export(B.ARR_ROW_ITEMS)["len"].astype(np.int64)
+    long_at = np.flatnonzero(ln >= SHORT_ITEM_EDGES)
+    first_short = int(long_at[-1]) + 1 if long_at.size else 0
+    return {"long_items": first_short, "long_edges": int(ln[:first_short].sum()),
+            "short_items": int(ln.size - first_short), "short_edges": int(ln[first_short:].sum())}
+
+
 def algorithmic_bytes(kernel: str, n: int, e: int, H: int, D: int, b: int,
-                      tw: dict | None = None) -> int | None:
+                      tw: dict | None = None, split: dict | None = None) -> int | None:
     """Bytes a kernel must move: neighbour-row gathers per edge plus the
-    per-node reads and writes of its own rows (R = H*D*b bytes per node row)."""
+    per-node reads and writes of its own rows (R = H*D*b bytes per node row).
+    The GATv2 CSR backward pass runs as two kernels when a wavefront holds
+    several edges (long items, then short items several to a wave): each
+    is charged its own edges and items (an item reads and writes its
+    destination's row data like a node)."""
     R = H * D * b
+    if kernel in ("gat_bwd_rows", "gat_bwd_rows_short") and split is not None:
+        which = "short" if kernel.endswith("_short") else "long"
+        e, n = split[f"{which}_edges"], split[f"{which}_items"]
+        kernel = "gat_bwd_rows"
     if kernel == "gt_bs_fwd" and tw:
         # dense tiles read each node's Q, K, V row once and write out and lse;
         # residual edges gather K_j and V_j; each tile reads its column and mask
@@ -372,6 +408,8 @@ def main():
     g = B.DeviceGraph(rp, ci, device=dev, chunk=args.chunk, block_sparse=args.tiles,
                       locality=bool(args.locality))
     tw = tile_work(g.plan) if args.tiles else None
+    split = (row_item_split(g.plan)
+             if spec.op == "gat" and edge_groups(H, D, nbytes) > 1 else None)
     torch.cuda.synchronize()
     plan_ms = (time.perf_counter() - t0) * 1e3
 
@@ -464,7 +502,7 @@ def main():
     kernels = {}
     for name, (tot, cnt) in per.items():
         avg = tot / cnt
-        ab = algorithmic_bytes(name, n, e, H, D, nbytes, tw)
+        ab = algorithmic_bytes(name, n, e, H, D, nbytes, tw, split)
         kernels[name] = {"ms": round(avg, 4), "launches_per_step": cnt / args.steps,
                          "share": round(tot / max(sum(v[0] for v in per.values()), 1e-12), 4)}
         if ab is not None:

@@ -133,7 +133,10 @@ Layout ws_layout(const Plan& p, int op, int H, int D, int dt)
         sz[0] = static_cast<size_t>(p.nnz) * gat_edge_record_dwords(dt, D, H) * 4; // edge records
         sz[1] = static_cast<size_t>(p.row_slots) * HD * 4;          // dXs partials
         sz[2] = static_cast<size_t>(p.col_slots) * HD * 4;          // dXt partials
-        sz[4] = static_cast<size_t>(gat_bwd_row_blocks(p)) * HD * 4; // da partials
+        {
+            const GatRowGrid gx = gat_bwd_row_grid(p, dt, D, H);
+            sz[4] = static_cast<size_t>(gx.single + gx.shorts) * HD * 4;   // da partials
+        }
         break;
     case SGAT_OP_REDUCE_FWD:                                        // H = 1, D = F
         sz[0] = static_cast<size_t>(p.row_slots) * HD * 4;          // partial values

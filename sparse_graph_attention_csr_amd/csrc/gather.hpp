@@ -168,9 +168,15 @@ __global__ __launch_bounds__(kBlock) void gt_fwd_rows(GtFwdArgs a)
                            a.part_ml);
 }
 
+// Work items [0, n_single) get one wavefront each (head group per unit as
+// usual); the rest, all short, come EPW to a wavefront: edge group q of the
+// wave owns item n_single + EPW*k + q and walks its edges U at a time, so the
+// dependent chain of one short row (item, colidx, gathers) overlaps with the
+// other rows of the wave instead of running alone.
 struct GatFwdArgs {
     const sgat_work_item* items;
     int64_t n_units;
+    int64_t n_items, n_single;
     int n_hg, H;
     const int32_t* colidx;
     const void *Xs, *Xt;
@@ -181,21 +187,56 @@ struct GatFwdArgs {
     float *part_acc, *part_ml;
 };
 
-template <int DT, int D, int EPW, int U>
-__global__ __launch_bounds__(kBlock) void gat_fwd_rows(GatFwdArgs a)
+// One GATv2 online-softmax step over U gathered neighbour rows (rows with
+// ok == false take no part). a LeakyReLU(z) = z g with g = a for z > 0 and
+// a * slope otherwise; at/as hold a and a * slope, both scaled by log2(e).
+template <int DT, int VEC, int SPH, int U>
+__device__ __forceinline__ void gat_online_step(Online<VEC>& st, const Frag (&xf)[U],
+                                                const bool (&ok)[U], const float (&xs)[VEC],
+                                                const float (&at)[VEC], const float (&as)[VEC])
 {
-    using G = Geo<DT, D, EPW>;
-    constexpr int VEC = G::VEC;
-    const int64_t unit = logical_block() * kWavesPerBlock + wave_id();
-    if (unit >= a.n_units) return;
-    const int64_t ii = unit / a.n_hg;
-    const int hg = static_cast<int>(unit - ii * a.n_hg);
-    const sgat_work_item it = a.items[ii];
-    const G g(hg, a.H);
-    const int64_t HD = static_cast<int64_t>(a.H) * D;
+    float s[U];
+    float mb = kNegInf;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        float x[VEC];
+        to_f32<DT>(xf[u], x);
+        float part = 0.f;
+#pragma unroll
+        for (int k = 0; k < VEC; ++k) {
+            const float z = xs[k] + x[k];
+            part = fmaf(z, z > 0.f ? at[k] : as[k], part);
+        }
+        const float hs = head_sum<SPH>(part);
+        s[u] = ok[u] ? hs : kNegInf;
+        mb = fmaxf(mb, s[u]);
+    }
+    const float mn = fmaxf(st.m, mb);
+    const float corr = mn == kNegInf ? 1.f : fast_exp2(st.m - mn);
+    st.l *= corr;
+#pragma unroll
+    for (int k = 0; k < VEC; ++k) st.acc[k] *= corr;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const float p = ok[u] ? fast_exp2(s[u] - mn) : 0.f;
+        st.l += p;
+        float x[VEC];
+        to_f32<DT>(xf[u], x);
+#pragma unroll
+        for (int k = 0; k < VEC; ++k) st.acc[k] = fmaf(p, x[k], st.acc[k]);
+    }
+    st.m = mn;
+}
 
-    // a_d LeakyReLU(z_d) = z_d g_d with g_d = a_d for z_d > 0, a_d * slope otherwise
-    float xs[VEC] = {}, at[VEC] = {}, as[VEC];
+template <int DT, int D, int EPW>
+__device__ __forceinline__ void gat_fwd_prologue(const GatFwdArgs& a, const Geo<DT, D, EPW>& g,
+                                                 const sgat_work_item& it, int64_t HD,
+                                                 float (&xs)[Elem<DT>::VEC], float (&at)[Elem<DT>::VEC],
+                                                 float (&as)[Elem<DT>::VEC])
+{
+    constexpr int VEC = Elem<DT>::VEC;
+#pragma unroll
+    for (int k = 0; k < VEC; ++k) xs[k] = at[k] = 0.f;
     if (g.hvalid) {
         to_f32<DT>(ldg<DT>(a.Xs, static_cast<int64_t>(it.row) * HD + g.col), xs);
         ld_f32<VEC>(a.att + g.col, at);
@@ -205,6 +246,18 @@ __global__ __launch_bounds__(kBlock) void gat_fwd_rows(GatFwdArgs a)
         at[k] *= kLog2e;
         as[k] = at[k] * a.slope;
     }
+}
+
+template <int DT, int D, int EPW, int U>
+__device__ __forceinline__ void gat_fwd_one(const GatFwdArgs& a, int64_t ii, int hg)
+{
+    using G = Geo<DT, D, EPW>;
+    constexpr int VEC = G::VEC;
+    const sgat_work_item it = a.items[ii];
+    const G g(hg, a.H);
+    const int64_t HD = static_cast<int64_t>(a.H) * D;
+    float xs[VEC], at[VEC], as[VEC];
+    gat_fwd_prologue<DT, D, EPW>(a, g, it, HD, xs, at, as);
     Online<VEC> st;
     const int32_t* ci = a.colidx + it.begin;
     for (int base = 0; base < it.len; base += kWave) {
@@ -221,43 +274,67 @@ __global__ __launch_bounds__(kBlock) void gat_fwd_rows(GatFwdArgs a)
                 xf[u] = frag_zero();
                 if (ok[u] && g.hvalid) xf[u] = ldg<DT>(a.Xt, j * HD + g.col);
             }
-            float s[U];
-            float mb = kNegInf;
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                float x[VEC];
-                to_f32<DT>(xf[u], x);
-                float part = 0.f;
-#pragma unroll
-                for (int k = 0; k < VEC; ++k) {
-                    const float z = xs[k] + x[k];
-                    part = fmaf(z, z > 0.f ? at[k] : as[k], part);
-                }
-                const float hs = head_sum<G::SPH>(part);
-                s[u] = ok[u] ? hs : kNegInf;
-                mb = fmaxf(mb, s[u]);
-            }
-            const float mn = fmaxf(st.m, mb);
-            const float corr = mn == kNegInf ? 1.f : fast_exp2(st.m - mn);
-            st.l *= corr;
-#pragma unroll
-            for (int k = 0; k < VEC; ++k) st.acc[k] *= corr;
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const float p = ok[u] ? fast_exp2(s[u] - mn) : 0.f;
-                st.l += p;
-                float x[VEC];
-                to_f32<DT>(xf[u], x);
-#pragma unroll
-                for (int k = 0; k < VEC; ++k) st.acc[k] = fmaf(p, x[k], st.acc[k]);
-            }
-            st.m = mn;
+            gat_online_step<DT, VEC, G::SPH, U>(st, xf, ok, xs, at, as);
         }
     }
     if constexpr (EPW > 1) merge_groups<VEC, G::LPE>(st);
     if (g.sub == 0 && g.hvalid)
         fwd_store<DT, VEC>(st, it, HD, a.H, g.head, g.col, g.leader, a.out, a.lse, a.part_acc,
                            a.part_ml);
+}
+
+// EPW short items per wave, one per edge group (all lanes of a group share
+// the group's trip counts, so the in-group shuffles read active lanes only).
+template <int DT, int D, int EPW, int U>
+__device__ __forceinline__ void gat_fwd_multi(const GatFwdArgs& a, int64_t first, int hg)
+{
+    using G = Geo<DT, D, EPW>;
+    constexpr int VEC = G::VEC;
+    static_assert(G::LPE % U == 0, "a step must not cross the group's index block");
+    const G g(hg, a.H);
+    const int64_t HD = static_cast<int64_t>(a.H) * D;
+    const int64_t idx = first + g.sub;
+    const bool has = idx < a.n_items;
+    sgat_work_item it{0, 0, 0, -1, 0};
+    if (has) it = a.items[idx];
+    float xs[VEC], at[VEC], as[VEC];
+    gat_fwd_prologue<DT, D, EPW>(a, g, it, HD, xs, at, as);
+    Online<VEC> st;
+    const int32_t* ci = a.colidx + it.begin;
+    const int lead = g.sub * G::LPE;
+    for (int base = 0; base < it.len; base += G::LPE) {
+        const int nb = min(G::LPE, it.len - base);
+        const int cj = g.pos < nb ? ci[base + g.pos] : 0;
+        for (int t = 0; t < nb; t += U) {
+            Frag xf[U];
+            bool ok[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                ok[u] = t + u < nb;
+                const int64_t j = __shfl(cj, lead + t + u);
+                xf[u] = frag_zero();
+                if (ok[u] && g.hvalid) xf[u] = ldg<DT>(a.Xt, j * HD + g.col);
+            }
+            gat_online_step<DT, VEC, G::SPH, U>(st, xf, ok, xs, at, as);
+        }
+    }
+    if (has && g.hvalid)
+        fwd_store<DT, VEC>(st, it, HD, a.H, g.head, g.col, g.leader, a.out, a.lse, a.part_acc,
+                           a.part_ml);
+}
+
+template <int DT, int D, int EPW, int U, int UM>
+__global__ __launch_bounds__(kBlock) void gat_fwd_rows(GatFwdArgs a)
+{
+    const int64_t unit = logical_block() * kWavesPerBlock + wave_id();
+    if (unit >= a.n_units) return;
+    const int64_t wi = unit / a.n_hg;
+    const int hg = static_cast<int>(unit - wi * a.n_hg);
+    if (EPW == 1 || wi < a.n_single)
+        gat_fwd_one<DT, D, EPW, U>(a, wi, hg);
+    else if constexpr (EPW > 1)
+        gat_fwd_multi<DT, D, EPW, (UM < Geo<DT, D, EPW>::LPE ? UM : Geo<DT, D, EPW>::LPE)>(
+            a, a.n_single + (wi - a.n_single) * EPW, hg);
 }
 
 // Merges of split rows. Grid: (split, block of channels). A block covers EB =
@@ -530,7 +607,7 @@ __host__ __device__ constexpr int gat_rec_dwords(int hg, int lanes)
 
 struct GatBwdRowArgs {
     const sgat_work_item* items;
-    int64_t n_items;
+    int64_t n_items, n_single;   // items [n_single, n_items) come EPW to a wave, as in the forward
     int H;
     const int32_t* colidx;
     const void *Xs, *Xt, *O, *dO;
@@ -544,106 +621,201 @@ struct GatBwdRowArgs {
     float* da_part;   // [gridDim.x][H*D]
 };
 
-template <int DT, int D, int EPW, int U>
-__global__ __launch_bounds__(kBlock) void gat_bwd_rows(GatBwdRowArgs a)
+// Per-destination state of the GATv2 CSR backward pass.
+template <int VEC>
+struct GatRowState {
+    float xs[VEC];
+    Frag dof;
+    float lse2, delta;
+};
+
+template <int DT, int D, int EPW>
+__device__ __forceinline__ GatRowState<Elem<DT>::VEC> gat_row_state(const GatBwdRowArgs& a,
+                                                                     const Geo<DT, D, EPW>& g,
+                                                                     const sgat_work_item& it,
+                                                                     bool load)
+{
+    constexpr int VEC = Elem<DT>::VEC;
+    GatRowState<VEC> r;
+    const int64_t ro = static_cast<int64_t>(it.row) * a.H * D + g.col;
+    Frag of = frag_zero();
+    r.dof = frag_zero();
+    r.lse2 = 0.f;
+#pragma unroll
+    for (int k = 0; k < VEC; ++k) r.xs[k] = 0.f;
+    if (load && g.hvalid) {
+        to_f32<DT>(ldg<DT>(a.Xs, ro), r.xs);
+        r.dof = ldg<DT>(a.dO, ro);
+        of = ldg<DT>(a.O, ro);
+        r.lse2 = a.lse[static_cast<int64_t>(it.row) * a.H + g.head] * kLog2e;
+    }
+    r.delta = head_sum<Geo<DT, D, EPW>::SPH>(dot<DT>(r.dof, of));
+    return r;
+}
+
+// One edge (i, j) for the lane's channels: p = exp(e_ij - lse_i), dE =
+// p (dO_i . Xt_j - Delta_i); adds dE g to dXs and dE LeakyReLU(z) to da, and
+// stages (p, dE) and the signs of z in the edge's LDS record. g_d =
+// a_d LeakyReLU'(z_d) is a_d for z_d > 0, a_d * slope otherwise, and
+// a_d LeakyReLU(z_d) = z_d g_d.
+template <int DT, int D, int EPW>
+__device__ __forceinline__ void gat_bwd_edge(const Geo<DT, D, EPW>& g, const Frag& xf, bool ok,
+                                             const GatRowState<Elem<DT>::VEC>& r,
+                                             const float (&at)[Elem<DT>::VEC],
+                                             const float (&as)[Elem<DT>::VEC], float slope,
+                                             float (&dxs)[Elem<DT>::VEC],
+                                             float (&da)[Elem<DT>::VEC], uint32_t* lr)
+{
+    using G = Geo<DT, D, EPW>;
+    constexpr int VEC = G::VEC;
+    float x[VEC], z[VEC], gz[VEC];
+    to_f32<DT>(xf, x);
+    float part = 0.f;
+#pragma unroll
+    for (int k = 0; k < VEC; ++k) {
+        z[k] = r.xs[k] + x[k];
+        gz[k] = z[k] > 0.f ? at[k] : as[k];
+        part = fmaf(z[k], gz[k], part);
+    }
+    const float e2 = head_sum<G::SPH>(part) * kLog2e;
+    const float dp = head_sum<G::SPH>(dot<DT>(r.dof, xf));
+    const float p = ok ? fast_exp2(e2 - r.lse2) : 0.f;
+    const float dE = p * (dp - r.delta);
+    uint32_t zbits = 0;
+#pragma unroll
+    for (int k = 0; k < VEC; ++k) {
+        dxs[k] = fmaf(dE, gz[k], dxs[k]);
+        da[k] = fmaf(dE, z[k] > 0.f ? z[k] : slope * z[k], da[k]);
+        zbits |= (z[k] > 0.f ? 1u : 0u) << k;
+    }
+    reinterpret_cast<uint8_t*>(lr + 2 * G::HG)[g.pos] = static_cast<uint8_t>(zbits);
+    if (g.leader) {
+        const int hl = g.pos / G::SPH;   // head within the group
+        lr[2 * hl] = __float_as_uint(p);
+        lr[2 * hl + 1] = __float_as_uint(dE);
+    }
+}
+
+// SHORT = false: the items [0, n_single), one wave each; SHORT = true: the
+// items [n_single, n_items), EPW to a wave. Each launch writes one da
+// partial per workgroup into its own da_part.
+// Waves per SIMD asked of the short-item instance: 5 for the bf16 layouts
+// whose short path fits 96 VGPRs without spilling (D = 64, and D = 128 with 4
+// edge groups); the others keep the compiler's choice.
+constexpr int gat_short_rows_waves(int dt, int D, int epw)
+{
+    return dt == SGAT_BF16 && (D == 64 || (D == 128 && epw == 4)) ? 5 : 1;
+}
+
+template <int DT, int D, int EPW, int U, int UMAX, bool SHORT>
+__global__ __launch_bounds__(kBlock)
+__attribute__((amdgpu_waves_per_eu(SHORT ? gat_short_rows_waves(DT, D, EPW) : 1)))
+void gat_bwd_rows(GatBwdRowArgs a)
 {
     using G = Geo<DT, D, EPW>;
     constexpr int VEC = G::VEC;
     constexpr int RS = gat_rec_dwords(G::HG, G::LPE);
+    constexpr int UM = UMAX < G::LPE ? UMAX : G::LPE;   // per-group step of the short items
     __shared__ float red[kWavesPerBlock][G::LPE * VEC];
-    // records of one 64-edge block, written out contiguously once per block
-    // (per-edge global stores inside the loop would make each wait for the
-    // next loads also wait for them)
+    // records of one block of edges (64 for a single item, LPE per group for
+    // short items), written out contiguously once per block: per-edge global
+    // stores inside the loop would make each wait for the next loads also
+    // wait for them
     __shared__ __align__(16) uint32_t recbuf[kWavesPerBlock][kWave * RS];
     const int hg = blockIdx.y;
     const G g(hg, a.H);
     const int64_t HD = static_cast<int64_t>(a.H) * D;
     const int wid = wave_id();
-    const int hl = g.pos / G::SPH;   // head within the group
     uint32_t* const lrec = recbuf[wid];
 
-    // g_d = a_d LeakyReLU'(z_d): a_d for z_d > 0, a_d * slope otherwise; then
-    // a_d LeakyReLU(z_d) = z_d g_d and the dXs term is dE g_d
     float at[VEC] = {}, as[VEC];
     if (g.hvalid) ld_f32<VEC>(a.att + g.col, at);
 #pragma unroll
     for (int k = 0; k < VEC; ++k) as[k] = at[k] * a.slope;
     float da[VEC] = {};
 
+    const int64_t n_wunits = SHORT ? (a.n_items - a.n_single + EPW - 1) / EPW : a.n_single;
     const int64_t stride = static_cast<int64_t>(gridDim.x) * kWavesPerBlock;
-    for (int64_t ii = static_cast<int64_t>(blockIdx.x) * kWavesPerBlock + wid; ii < a.n_items;
-         ii += stride) {
-        const sgat_work_item it = a.items[ii];
-        const int64_t ro = static_cast<int64_t>(it.row) * HD + g.col;
-        float xs[VEC] = {};
-        Frag dof = frag_zero(), of = frag_zero();
-        float lse2 = 0.f;
-        if (g.hvalid) {
-            to_f32<DT>(ldg<DT>(a.Xs, ro), xs);
-            dof = ldg<DT>(a.dO, ro);
-            of = ldg<DT>(a.O, ro);
-            lse2 = a.lse[static_cast<int64_t>(it.row) * a.H + g.head] * kLog2e;
-        }
-        const float delta = head_sum<G::SPH>(dot<DT>(dof, of));
-
-        float dxs[VEC] = {};
-        const int32_t* ci = a.colidx + it.begin;
-        uint32_t* rec = a.edge_rec + (static_cast<int64_t>(hg) * a.nnz + it.begin) * RS;
-        for (int base = 0; base < it.len; base += kWave) {
-            const int nb = min(kWave, it.len - base);
-            const int cj = g.lane < nb ? ci[base + g.lane] : 0;
-            for (int t = 0; t < nb; t += EPW * U) {
-                Frag xf[U];
-                bool ok[U];
+    for (int64_t wi = static_cast<int64_t>(blockIdx.x) * kWavesPerBlock + wid; wi < n_wunits;
+         wi += stride) {
+        if constexpr (!SHORT) {
+            // one item for the whole wave, EPW edges side by side
+            const sgat_work_item it = a.items[wi];
+            const GatRowState<VEC> r = gat_row_state<DT, D, EPW>(a, g, it, true);
+            float dxs[VEC] = {};
+            const int32_t* ci = a.colidx + it.begin;
+            uint32_t* rec = a.edge_rec + (static_cast<int64_t>(hg) * a.nnz + it.begin) * RS;
+            for (int base = 0; base < it.len; base += kWave) {
+                const int nb = min(kWave, it.len - base);
+                const int cj = g.lane < nb ? ci[base + g.lane] : 0;
+                for (int t = 0; t < nb; t += EPW * U) {
+                    Frag xf[U];
+                    bool ok[U];
 #pragma unroll
-                for (int u = 0; u < U; ++u) {
-                    const int e = t + u * EPW + g.sub;
-                    ok[u] = e < nb;
-                    const int64_t j = bcast<EPW>(cj, e);
-                    xf[u] = frag_zero();
-                    if (ok[u] && g.hvalid) xf[u] = ldg<DT>(a.Xt, j * HD + g.col);
+                    for (int u = 0; u < U; ++u) {
+                        const int e = t + u * EPW + g.sub;
+                        ok[u] = e < nb;
+                        const int64_t j = bcast<EPW>(cj, e);
+                        xf[u] = frag_zero();
+                        if (ok[u] && g.hvalid) xf[u] = ldg<DT>(a.Xt, j * HD + g.col);
+                    }
+#pragma unroll
+                    for (int u = 0; u < U; ++u)   // t + u*EPW + sub < 64: EPW*U divides 64
+                        gat_bwd_edge<DT, D, EPW>(g, xf[u], ok[u], r, at, as, a.slope, dxs, da,
+                                                 lrec + (t + u * EPW + g.sub) * RS);
                 }
-#pragma unroll
-                for (int u = 0; u < U; ++u) {
-                    float x[VEC], z[VEC], gz[VEC];
-                    to_f32<DT>(xf[u], x);
-                    float part = 0.f;
-#pragma unroll
-                    for (int k = 0; k < VEC; ++k) {
-                        z[k] = xs[k] + x[k];
-                        gz[k] = z[k] > 0.f ? at[k] : as[k];
-                        part = fmaf(z[k], gz[k], part);
-                    }
-                    const float e2 = head_sum<G::SPH>(part) * kLog2e;
-                    const float dp = head_sum<G::SPH>(dot<DT>(dof, xf[u]));
-                    const float p = ok[u] ? fast_exp2(e2 - lse2) : 0.f;
-                    const float dE = p * (dp - delta);
-                    uint32_t zbits = 0;
-#pragma unroll
-                    for (int k = 0; k < VEC; ++k) {
-                        dxs[k] = fmaf(dE, gz[k], dxs[k]);
-                        da[k] = fmaf(dE, z[k] > 0.f ? z[k] : a.slope * z[k], da[k]);
-                        zbits |= (z[k] > 0.f ? 1u : 0u) << k;
-                    }
-                    // t + u*EPW + sub < 64: EPW*U divides the block of 64 edges
-                    uint32_t* lr = lrec + (t + u * EPW + g.sub) * RS;
-                    reinterpret_cast<uint8_t*>(lr + 2 * G::HG)[g.pos] = static_cast<uint8_t>(zbits);
-                    if (g.leader) {
-                        lr[2 * hl] = __float_as_uint(p);
-                        lr[2 * hl + 1] = __float_as_uint(dE);
-                    }
+                wave_lds_fence();
+                {
+                    uint2* dst = reinterpret_cast<uint2*>(rec + static_cast<int64_t>(base) * RS);
+                    const uint2* src = reinterpret_cast<const uint2*>(lrec);
+                    for (int w = g.lane; w < nb * (RS / 2); w += kWave) dst[w] = src[w];
                 }
+                wave_lds_fence();
             }
-            wave_lds_fence();
-            {
-                uint2* dst = reinterpret_cast<uint2*>(rec + static_cast<int64_t>(base) * RS);
-                const uint2* src = reinterpret_cast<const uint2*>(lrec);
-                for (int w = g.lane; w < nb * (RS / 2); w += kWave) dst[w] = src[w];
+            if constexpr (EPW > 1) sum_groups<VEC, G::LPE>(dxs);
+            if (g.sub == 0 && g.hvalid) grad_store<DT, VEC>(dxs, 1.f, it, HD, g.col, a.dXs, a.part);
+        } else {
+            // EPW short items, one per edge group; all lanes of a group share
+            // its trip counts, so the in-group shuffles read active lanes only
+            static_assert(EPW > 1, "short items need several edge groups per wave");
+            const int64_t idx = a.n_single + wi * EPW + g.sub;
+            const bool has = idx < a.n_items;
+            sgat_work_item it{0, 0, 0, -1, 0};
+            if (has) it = a.items[idx];
+            const GatRowState<VEC> r = gat_row_state<DT, D, EPW>(a, g, it, has);
+            float dxs[VEC] = {};
+            const int32_t* ci = a.colidx + it.begin;
+            uint32_t* rec = a.edge_rec + (static_cast<int64_t>(hg) * a.nnz + it.begin) * RS;
+            uint32_t* const grec = lrec + g.sub * G::LPE * RS;   // the group's LPE records
+            const int lead = g.sub * G::LPE;
+            for (int base = 0; base < it.len; base += G::LPE) {
+                const int nb = min(G::LPE, it.len - base);
+                const int cj = g.pos < nb ? ci[base + g.pos] : 0;
+                for (int t = 0; t < nb; t += UM) {
+                    Frag xf[UM];
+                    bool ok[UM];
+#pragma unroll
+                    for (int u = 0; u < UM; ++u) {
+                        ok[u] = t + u < nb;
+                        const int64_t j = __shfl(cj, lead + t + u);
+                        xf[u] = frag_zero();
+                        if (ok[u] && g.hvalid) xf[u] = ldg<DT>(a.Xt, j * HD + g.col);
+                    }
+#pragma unroll
+                    for (int u = 0; u < UM; ++u)   // t + u < LPE: UM divides LPE
+                        gat_bwd_edge<DT, D, EPW>(g, xf[u], ok[u], r, at, as, a.slope, dxs, da,
+                                                 grec + (t + u) * RS);
+                }
+                wave_lds_fence();
+                {
+                    uint2* dst = reinterpret_cast<uint2*>(rec + static_cast<int64_t>(base) * RS);
+                    const uint2* src = reinterpret_cast<const uint2*>(grec);
+                    for (int w = g.pos; w < nb * (RS / 2); w += G::LPE) dst[w] = src[w];
+                }
+                wave_lds_fence();
             }
-            wave_lds_fence();
+            if (has && g.hvalid) grad_store<DT, VEC>(dxs, 1.f, it, HD, g.col, a.dXs, a.part);
         }
-        if constexpr (EPW > 1) sum_groups<VEC, G::LPE>(dxs);
-        if (g.sub == 0 && g.hvalid) grad_store<DT, VEC>(dxs, 1.f, it, HD, g.col, a.dXs, a.part);
     }
     // da: edge groups, then the waves of the block, in fixed order
     if constexpr (EPW > 1) sum_groups<VEC, G::LPE>(da);

@@ -18,8 +18,12 @@ struct Decomp {
 };
 Decomp decompose(int dt, int D, int H);
 
-// Grid of the GATv2 CSR backward pass (its da partials are one per workgroup).
-int gat_bwd_row_blocks(const Plan& p);
+// Grids of the GATv2 CSR backward pass: the long items one per wave, the
+// short ones several per wave (its da partials are one per workgroup of both).
+struct GatRowGrid {
+    int single, shorts;
+};
+GatRowGrid gat_bwd_row_grid(const Plan& p, int dt, int D, int H);
 
 struct FwdWs {
     float* part_acc;   // [row_slots][H*D]
@@ -30,7 +34,7 @@ struct BwdWs {
     float* part_row;   // [row_slots][H*D]
     float* part_col0;  // [col_slots][H*D]
     float* part_col1;  // [col_slots][H*D] (GT only)
-    float* da_part;    // [gat_bwd_row_blocks][H*D] (GATv2 only)
+    float* da_part;    // [single + shorts workgroups][H*D] (GATv2 only)
     float* ds;         // [nnz][H] dS per edge (Graph Transformer only)
     void* edge_rec;    // [nnz][gat_edge_record_dwords] (GATv2 only)
 };

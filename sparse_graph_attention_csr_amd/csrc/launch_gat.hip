@@ -18,6 +18,18 @@ namespace sgat {
 #ifndef SGAT_UNROLL_ROWS
 #define SGAT_UNROLL_ROWS 8
 #endif
+// Items shorter than 2^SGAT_SHORT_LOG2 edges at the end of the work list go
+// several to a wavefront (one per edge group) when a wave has more than one
+// edge group; SGAT_UNROLL_MULTI neighbour rows per group and step.
+#ifndef SGAT_SHORT_LOG2
+#define SGAT_SHORT_LOG2 7
+#endif
+#ifndef SGAT_UNROLL_MULTI
+#define SGAT_UNROLL_MULTI 4
+#endif
+#ifndef SGAT_UNROLL_MULTI_BWD
+#define SGAT_UNROLL_MULTI_BWD 1
+#endif
 
 namespace {
 // With several edges per wave side by side, each unrolled step already holds
@@ -46,10 +58,19 @@ __global__ __launch_bounds__(kBlock) void da_reduce(DaReduceArgs a)
     if (threadIdx.x == 0) a.da[e] = red[0];
 }
 
-int gat_bwd_row_blocks(const Plan& p)
+GatRowGrid gat_bwd_row_grid(const Plan& p, int dt, int D, int H)
 {
-    const int64_t need = (static_cast<int64_t>(p.row_items.size()) + kWavesPerBlock - 1) / kWavesPerBlock;
-    return static_cast<int>(std::max<int64_t>(1, std::min<int64_t>(need, kGatBwdMaxBlocks)));
+    const Decomp dc = decompose(dt, D, H);
+    const int64_t n_items = static_cast<int64_t>(p.row_items.size());
+    const int64_t n_single = dc.epw > 1 ? p.row_short_from[SGAT_SHORT_LOG2] : n_items;
+    const int64_t short_units = (n_items - n_single + dc.epw - 1) / dc.epw;
+    auto blocks = [](int64_t waves) {
+        const int64_t need = (waves + kWavesPerBlock - 1) / kWavesPerBlock;
+        return static_cast<int>(std::min<int64_t>(need, kGatBwdMaxBlocks));
+    };
+    GatRowGrid g{blocks(n_single), blocks(short_units)};
+    if (g.single + g.shorts == 0) g.single = 1;   // da is still written (as zeros)
+    return g;
 }
 
 int launch_da_zero(float* da, int HD, hipStream_t s)
@@ -66,7 +87,9 @@ int launch_gat_fwd(const Plan& p, int H, int D, int dt, const int32_t* colidx, c
     const Decomp dc = decompose(dt, D, H);
     GatFwdArgs a;
     a.items = p.dptr<sgat_work_item>(SGAT_ARR_ROW_ITEMS);
-    a.n_units = static_cast<int64_t>(p.row_items.size()) * dc.n_hg;
+    a.n_items = static_cast<int64_t>(p.row_items.size());
+    a.n_single = dc.epw > 1 ? p.row_short_from[SGAT_SHORT_LOG2] : a.n_items;
+    a.n_units = (a.n_single + (a.n_items - a.n_single + dc.epw - 1) / dc.epw) * dc.n_hg;
     a.n_hg = dc.n_hg;
     a.H = H;
     a.colidx = colidx;
@@ -79,7 +102,7 @@ int launch_gat_fwd(const Plan& p, int H, int D, int dt, const int32_t* colidx, c
     a.part_ml = ws.part_ml;
     const void* fn = nullptr;
 #define X(DT_, D_, E_) \
-    if (dt == DT_ && D == D_ && dc.epw == E_) fn = reinterpret_cast<const void*>(&gat_fwd_rows<DT_, D_, E_, unroll_fwd(E_)>);
+    if (dt == DT_ && D == D_ && dc.epw == E_) fn = reinterpret_cast<const void*>(&gat_fwd_rows<DT_, D_, E_, unroll_fwd(E_), SGAT_UNROLL_MULTI>);
     SGAT_GATHER_CONFIGS(X)
 #undef X
     if (!fn) return SGAT_INVALID_ARGUMENT;
@@ -115,11 +138,12 @@ int launch_gat_bwd(const Plan& p, int H, int D, int dt, const int32_t* colidx, c
 {
     const Decomp dc = decompose(dt, D, H);
     const int HD = H * D;
-    const int gx = gat_bwd_row_blocks(p);
+    const GatRowGrid gx = gat_bwd_row_grid(p, dt, D, H);
 
     GatBwdRowArgs r;
     r.items = p.dptr<sgat_work_item>(SGAT_ARR_ROW_ITEMS);
     r.n_items = static_cast<int64_t>(p.row_items.size());
+    r.n_single = dc.epw > 1 ? p.row_short_from[SGAT_SHORT_LOG2] : r.n_items;
     r.H = H;
     r.colidx = colidx;
     r.Xs = Xs; r.Xt = Xt; r.O = O; r.dO = dO;
@@ -147,24 +171,38 @@ int launch_gat_bwd(const Plan& p, int H, int D, int dt, const int32_t* colidx, c
     c.dXt = dXt;
     c.part = ws.part_col0;
 
-    const void *fr = nullptr, *fc = nullptr;
-#define X(DT_, D_, E_)                                                                 \
-    if (dt == DT_ && D == D_ && dc.epw == E_) {                                        \
-        fr = reinterpret_cast<const void*>(&gat_bwd_rows<DT_, D_, E_, unroll_bwd(E_)>);    \
-        fc = reinterpret_cast<const void*>(&gat_bwd_cols<DT_, D_, E_, unroll_bwd(E_)>);    \
+    const void *fr = nullptr, *frs = nullptr, *fc = nullptr;
+#define X(DT_, D_, E_)                                                                        \
+    if (dt == DT_ && D == D_ && dc.epw == E_) {                                               \
+        fr = reinterpret_cast<const void*>(                                                   \
+            &gat_bwd_rows<DT_, D_, E_, unroll_bwd(E_), SGAT_UNROLL_MULTI_BWD, false>);        \
+        if constexpr (E_ > 1)                                                                 \
+            frs = reinterpret_cast<const void*>(                                              \
+                &gat_bwd_rows<DT_, D_, E_, unroll_bwd(E_), SGAT_UNROLL_MULTI_BWD, true>);     \
+        fc = reinterpret_cast<const void*>(&gat_bwd_cols<DT_, D_, E_, unroll_bwd(E_)>);       \
     }
     SGAT_GATHER_CONFIGS(X)
 #undef X
-    if (!fr || !fc) return SGAT_INVALID_ARGUMENT;
+    if (!fr || !fc || (gx.shorts > 0 && !frs)) return SGAT_INVALID_ARGUMENT;
     int rc;
-    // the row pass always runs: it writes the da partials of every workgroup
-    if ((rc = launch("gat_bwd_rows", fr, dim3(static_cast<unsigned>(gx), static_cast<unsigned>(dc.n_hg)),
+    // every workgroup of the row passes writes its da partial (zeros if it had no item)
+    if (gx.single > 0 &&
+        (rc = launch("gat_bwd_rows", fr,
+                     dim3(static_cast<unsigned>(gx.single), static_cast<unsigned>(dc.n_hg)),
                      dim3(kBlock), &r, s)))
         return rc;
+    if (gx.shorts > 0) {
+        GatBwdRowArgs rs = r;
+        rs.da_part = ws.da_part + static_cast<int64_t>(gx.single) * HD;
+        if ((rc = launch("gat_bwd_rows_short", frs,
+                         dim3(static_cast<unsigned>(gx.shorts), static_cast<unsigned>(dc.n_hg)),
+                         dim3(kBlock), &rs, s)))
+            return rc;
+    }
     if ((rc = merge_sum("gat_bwd_rows_merge", p.row_splits, p.dptr<sgat_split>(SGAT_ARR_ROW_SPLITS),
                         HD, ws.part_row, 1.f, dXs, nullptr, 0.f, nullptr, dt, s)))
         return rc;
-    DaReduceArgs d{ws.da_part, gx, HD, da};
+    DaReduceArgs d{ws.da_part, gx.single + gx.shorts, HD, da};
     if ((rc = launch("gat_bwd_da_reduce", reinterpret_cast<const void*>(&da_reduce),
                      dim3(static_cast<unsigned>(HD)), dim3(kBlock), &d, s)))
         return rc;

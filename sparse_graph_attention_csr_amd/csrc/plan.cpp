@@ -87,6 +87,20 @@ void build_work_list(int64_t n, const int64_t* ptr, int64_t chunk,
     }
 }
 
+void short_suffixes(const std::vector<sgat_work_item>& items, int64_t out[33])
+{
+    // the suffix maximum of the lengths never increases along the list, so
+    // the items from out[b] on are exactly the suffix whose maximum is < 2^b
+    const int64_t m = static_cast<int64_t>(items.size());
+    int64_t longest = 0;
+    for (int b = 0; b <= 32; ++b) out[b] = m;
+    for (int64_t i = m - 1; i >= 0; --i) {
+        longest = std::max<int64_t>(longest, items[static_cast<size_t>(i)].len);
+        for (int b = 0; b <= 32; ++b)
+            if ((int64_t{1} << b) > longest) out[b] = i;
+    }
+}
+
 std::vector<int32_t> cuthill_mckee_rank(int64_t n, const int64_t* rowptr, const int32_t* colidx,
                                         const int64_t* colptr, const int32_t* rowidx)
 {
@@ -343,6 +357,8 @@ int sgat_plan_create(int64_t n, int64_t nnz, const int64_t* rowptr, const int32_
         const int32_t* rk = loc ? rank.data() : nullptr;
         sgat::build_work_list(n, rowptr, chunk, p.row_items, p.row_splits, p.row_slots, rk);
         sgat::build_work_list(n, p.colptr.data(), chunk, p.col_items, p.col_splits, p.col_slots, rk);
+        sgat::short_suffixes(p.row_items, p.row_short_from);
+        sgat::short_suffixes(p.col_items, p.col_short_from);
         if (bs) {
             sgat::build_tiles(n, rowptr, colidx, tmin, p.tile_rowptr, p.tile_col, p.tile_mask,
                               p.res_rowptr, p.res_colidx, p.tile_edges);

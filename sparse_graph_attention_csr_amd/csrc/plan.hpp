@@ -27,6 +27,9 @@ struct Plan {
     std::vector<sgat_work_item> row_items;
     std::vector<sgat_split> row_splits;
     int64_t row_slots = 0;
+    // short_from[b]: first work item from which every item has fewer than 2^b edges
+    int64_t row_short_from[33] = {};
+    int64_t col_short_from[33] = {};
 
     std::vector<int64_t> colptr;
     std::vector<int32_t> rowidx;
@@ -68,6 +71,9 @@ int validate_csr(int64_t n, int64_t nnz, const int64_t* rowptr, const int32_t* c
 void build_work_list(int64_t n, const int64_t* ptr, int64_t chunk,
                      std::vector<sgat_work_item>& items, std::vector<sgat_split>& splits,
                      int64_t& nslots, const int32_t* rank = nullptr);
+
+// out[b] = first index from which every item has fewer than 2^b edges (b = 0..32).
+void short_suffixes(const std::vector<sgat_work_item>& items, int64_t out[33]);
 
 // Cuthill-McKee rank of every node of the undirected simple graph underlying
 // the CSR (in- and out-neighbours, self-loops and repeats dropped).

@@ -76,6 +76,38 @@ def test_gat_parity(dt, H, D, chunk):
     assert rel_err(host(da), ra) <= TOL[dt]
 
 
+@pytest.mark.parametrize("dt,H,D", [("bf16", 1, 32), ("f32", 1, 32), ("bf16", 2, 64),
+                                    ("f32", 2, 64), ("bf16", 3, 32)])
+def test_gat_short_and_long_items(dt, H, D):
+    """Rows below 128 edges go several to a wavefront (one per edge group),
+    longer ones one per wavefront: degrees straddle that boundary (126..130),
+    with empty rows, split rows (chunk 64) and an item count that leaves the
+    last wavefront partly empty, under layouts with 2, 4, 8 and 16 edge
+    groups per wavefront and a padded head."""
+    note(f"gat short/long dt={dt} H={H} D={D}")
+    rng = np.random.default_rng(31 + H + D)
+    n = 389
+    deg = rng.choice([0, 1, 2, 7, 63, 126, 127, 128, 129, 130, 300], size=n)
+    rp = np.zeros(n + 1, dtype=np.int64)
+    rp[1:] = np.cumsum(deg)
+    ci = rng.integers(0, n, size=int(rp[-1])).astype(np.int32)
+    t = tensors(5, n, H, D, dt, ["xs", "xt", "dout"])
+    a = rng.standard_normal((H, D)).astype(np.float32) / np.sqrt(D)
+    ro, rl = oracle.gat_fwd(rp, ci, t["xs"], t["xt"], a)
+    rs, rt, ra = oracle.gat_bwd(rp, ci, t["xs"], t["xt"], a, t["dout"])
+    for chunk in (0, 64):
+        r = Runner(rp, ci, chunk=chunk)
+        xs, xt, do = (dev(t[x]) for x in ("xs", "xt", "dout"))
+        ad = dev(a)
+        out, lse = r.gat_fwd(xs, xt, ad)
+        assert rel_err(host(out), ro) <= TOL[dt]
+        assert rel_err(host(lse), rl) <= TOL[dt]
+        dxs, dxt, da = r.gat_bwd(xs, xt, ad, out, lse, do)
+        assert rel_err(host(dxs), rs) <= TOL[dt]
+        assert rel_err(host(dxt), rt) <= TOL[dt]
+        assert rel_err(host(da), ra) <= TOL[dt]
+
+
 def test_er_workload_forward_full():
     """The fp32 Erdos-Renyi workload (N=1000, H=4, D=32), every output element."""
     note("gt_er1k_h4d32_f32 forward")
