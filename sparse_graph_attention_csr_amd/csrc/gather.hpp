@@ -935,6 +935,7 @@ __global__ __launch_bounds__(kBlock) void gt_bwd_cols(GtBwdColArgs a)
 struct GatBwdColArgs {
     const sgat_work_item* items;
     int64_t n_units;
+    int64_t n_items, n_single;   // items [n_single, n_items) come EPW to a wave
     int n_hg, H;
     const int32_t* rowidx;
     const int32_t* col_edge;    // CSR edge id of each transposed entry
@@ -947,18 +948,36 @@ struct GatBwdColArgs {
     float* part;
 };
 
+// dXt_j += p_ij dO_i + dE_ij g_ij for U edges (ok[u] == false: no edge), g =
+// a LeakyReLU'(z_ij) from the sign bits of the edge record.
+template <int DT, int VEC, int U>
+__device__ __forceinline__ void gat_col_step(float (&dxt)[VEC], const Frag (&df)[U],
+                                             const float2 (&pd)[U], const uint32_t (&zb)[U],
+                                             const float (&at)[VEC], const float (&as)[VEC])
+{
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        float dx[VEC];
+        to_f32<DT>(df[u], dx);
+#pragma unroll
+        for (int k = 0; k < VEC; ++k) {
+            const float gz = (zb[u] >> k) & 1u ? at[k] : as[k];
+            dxt[k] = fmaf(pd[u].x, dx[k], fmaf(pd[u].y, gz, dxt[k]));
+        }
+    }
+}
+
 // dXt_j = sum over i of p_ij dO_i + dE_ij g_ij, g = a LeakyReLU'(z_ij): the
 // per-edge p, dE and signs of z come from the CSR pass; only dO_i is gathered.
-template <int DT, int D, int EPW, int U>
+template <int DT, int D, int EPW, int U, int UM>
 __global__ __launch_bounds__(kBlock) void gat_bwd_cols(GatBwdColArgs a)
 {
     using G = Geo<DT, D, EPW>;
     constexpr int VEC = G::VEC;
     const int64_t unit = logical_block() * kWavesPerBlock + wave_id();
     if (unit >= a.n_units) return;
-    const int64_t ii = unit / a.n_hg;
-    const int hg = static_cast<int>(unit - ii * a.n_hg);
-    const sgat_work_item it = a.items[ii];
+    const int64_t wi = unit / a.n_hg;
+    const int hg = static_cast<int>(unit - wi * a.n_hg);
     const G g(hg, a.H);
     const int64_t HD = static_cast<int64_t>(a.H) * D;
     constexpr int RS = gat_rec_dwords(G::HG, G::LPE);
@@ -971,45 +990,75 @@ __global__ __launch_bounds__(kBlock) void gat_bwd_cols(GatBwdColArgs a)
 #pragma unroll
     for (int k = 0; k < VEC; ++k) as[k] = at[k] * a.slope;
     float dxt[VEC] = {};
-    const int32_t* ri = a.rowidx + it.begin;
-    const int32_t* re = a.col_edge + it.begin;
-    for (int base = 0; base < it.len; base += kWave) {
-        const int nb = min(kWave, it.len - base);
-        const int ci = g.lane < nb ? ri[base + g.lane] : 0;
-        const int ce = g.lane < nb ? re[base + g.lane] : 0;
-        for (int t = 0; t < nb; t += EPW * U) {
-            Frag df[U];
-            float2 pd[U];
-            uint32_t zb[U];
+    if (EPW == 1 || wi < a.n_single) {
+        const sgat_work_item it = a.items[wi];
+        const int32_t* ri = a.rowidx + it.begin;
+        const int32_t* re = a.col_edge + it.begin;
+        for (int base = 0; base < it.len; base += kWave) {
+            const int nb = min(kWave, it.len - base);
+            const int ci = g.lane < nb ? ri[base + g.lane] : 0;
+            const int ce = g.lane < nb ? re[base + g.lane] : 0;
+            for (int t = 0; t < nb; t += EPW * U) {
+                Frag df[U];
+                float2 pd[U];
+                uint32_t zb[U];
 #pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int e = t + u * EPW + g.sub;
-                const int64_t i = bcast<EPW>(ci, e);
-                const int64_t eid = bcast<EPW>(ce, e);
-                df[u] = frag_zero();
-                pd[u] = make_float2(0.f, 0.f);
-                zb[u] = 0;
-                if (e < nb && g.hvalid) {
-                    const uint32_t* r = rbase + eid * RS;
-                    df[u] = ldg<DT>(a.dO, i * HD + g.col);
-                    pd[u] = *reinterpret_cast<const float2*>(r + 2 * hl);
-                    zb[u] = r[zl] >> zsh;
+                for (int u = 0; u < U; ++u) {
+                    const int e = t + u * EPW + g.sub;
+                    const int64_t i = bcast<EPW>(ci, e);
+                    const int64_t eid = bcast<EPW>(ce, e);
+                    df[u] = frag_zero();
+                    pd[u] = make_float2(0.f, 0.f);
+                    zb[u] = 0;
+                    if (e < nb && g.hvalid) {
+                        const uint32_t* r = rbase + eid * RS;
+                        df[u] = ldg<DT>(a.dO, i * HD + g.col);
+                        pd[u] = *reinterpret_cast<const float2*>(r + 2 * hl);
+                        zb[u] = r[zl] >> zsh;
+                    }
                 }
-            }
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                float dx[VEC];
-                to_f32<DT>(df[u], dx);
-#pragma unroll
-                for (int k = 0; k < VEC; ++k) {
-                    const float gz = (zb[u] >> k) & 1u ? at[k] : as[k];
-                    dxt[k] = fmaf(pd[u].x, dx[k], fmaf(pd[u].y, gz, dxt[k]));
-                }
+                gat_col_step<DT, VEC, U>(dxt, df, pd, zb, at, as);
             }
         }
+        if constexpr (EPW > 1) sum_groups<VEC, G::LPE>(dxt);
+        if (g.sub == 0 && g.hvalid) grad_store<DT, VEC>(dxt, 1.f, it, HD, g.col, a.dXt, a.part);
+    } else if constexpr (EPW > 1) {
+        // EPW short items, one per edge group (in-group shuffles only)
+        constexpr int V = UM < G::LPE ? UM : G::LPE;
+        const int64_t idx = a.n_single + (wi - a.n_single) * EPW + g.sub;
+        const bool has = idx < a.n_items;
+        sgat_work_item it{0, 0, 0, -1, 0};
+        if (has) it = a.items[idx];
+        const int32_t* ri = a.rowidx + it.begin;
+        const int32_t* re = a.col_edge + it.begin;
+        const int lead = g.sub * G::LPE;
+        for (int base = 0; base < it.len; base += G::LPE) {
+            const int nb = min(G::LPE, it.len - base);
+            const int ci = g.pos < nb ? ri[base + g.pos] : 0;
+            const int ce = g.pos < nb ? re[base + g.pos] : 0;
+            for (int t = 0; t < nb; t += V) {
+                Frag df[V];
+                float2 pd[V];
+                uint32_t zb[V];
+#pragma unroll
+                for (int u = 0; u < V; ++u) {
+                    const int64_t i = __shfl(ci, lead + t + u);
+                    const int64_t eid = __shfl(ce, lead + t + u);
+                    df[u] = frag_zero();
+                    pd[u] = make_float2(0.f, 0.f);
+                    zb[u] = 0;
+                    if (t + u < nb && g.hvalid) {
+                        const uint32_t* r = rbase + eid * RS;
+                        df[u] = ldg<DT>(a.dO, i * HD + g.col);
+                        pd[u] = *reinterpret_cast<const float2*>(r + 2 * hl);
+                        zb[u] = r[zl] >> zsh;
+                    }
+                }
+                gat_col_step<DT, VEC, V>(dxt, df, pd, zb, at, as);
+            }
+        }
+        if (has && g.hvalid) grad_store<DT, VEC>(dxt, 1.f, it, HD, g.col, a.dXt, a.part);
     }
-    if constexpr (EPW > 1) sum_groups<VEC, G::LPE>(dxt);
-    if (g.sub == 0 && g.hvalid) grad_store<DT, VEC>(dxt, 1.f, it, HD, g.col, a.dXt, a.part);
 }
 
 }  // namespace sgat

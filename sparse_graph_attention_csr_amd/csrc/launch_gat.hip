@@ -30,6 +30,9 @@ namespace sgat {
 #ifndef SGAT_UNROLL_MULTI_BWD
 #define SGAT_UNROLL_MULTI_BWD 1
 #endif
+#ifndef SGAT_UNROLL_MULTI_COLS
+#define SGAT_UNROLL_MULTI_COLS 1
+#endif
 
 namespace {
 // With several edges per wave side by side, each unrolled step already holds
@@ -158,7 +161,9 @@ int launch_gat_bwd(const Plan& p, int H, int D, int dt, const int32_t* colidx, c
 
     GatBwdColArgs c;
     c.items = p.dptr<sgat_work_item>(SGAT_ARR_COL_ITEMS);
-    c.n_units = static_cast<int64_t>(p.col_items.size()) * dc.n_hg;
+    c.n_items = static_cast<int64_t>(p.col_items.size());
+    c.n_single = dc.epw > 1 ? p.col_short_from[SGAT_SHORT_LOG2] : c.n_items;
+    c.n_units = (c.n_single + (c.n_items - c.n_single + dc.epw - 1) / dc.epw) * dc.n_hg;
     c.n_hg = dc.n_hg;
     c.H = H;
     c.rowidx = p.dptr<int32_t>(SGAT_ARR_ROWIDX);
@@ -179,7 +184,8 @@ int launch_gat_bwd(const Plan& p, int H, int D, int dt, const int32_t* colidx, c
         if constexpr (E_ > 1)                                                                 \
             frs = reinterpret_cast<const void*>(                                              \
                 &gat_bwd_rows<DT_, D_, E_, unroll_bwd(E_), SGAT_UNROLL_MULTI_BWD, true>);     \
-        fc = reinterpret_cast<const void*>(&gat_bwd_cols<DT_, D_, E_, unroll_bwd(E_)>);       \
+        fc = reinterpret_cast<const void*>(                                                   \
+            &gat_bwd_cols<DT_, D_, E_, unroll_bwd(E_), SGAT_UNROLL_MULTI_COLS>);              \
     }
     SGAT_GATHER_CONFIGS(X)
 #undef X
