@@ -213,10 +213,11 @@ int gt_fwd(const sgat_plan* plan, int64_t n, int64_t nnz,
            void* out, float* lse, void* ws, size_t ws_bytes, int use_tiles, void* stream);
 
 /* Backward of L = sum(out * dout): dQ, dK, dV. Recomputes alpha_ij from lse
- * (the forward's output) without any stored edge value. Delta_i = dout_i . out_i
- * per head; dS_ij = alpha_ij (dout_i . V_j - Delta_i). dQ is accumulated over
- * the CSR, dK and dV over the transposed CSR, so no atomics are needed.
- * All gradients are overwritten (not accumulated into). */
+ * (the forward's output); nothing per edge is kept from the forward.
+ * Delta_i = dout_i . out_i per head; dS_ij = alpha_ij (dout_i . V_j - Delta_i).
+ * The transposed-CSR pass computes dK, dV and dS, leaving dS per (edge, head)
+ * in the workspace; the CSR pass then accumulates dQ from it, so no atomics are
+ * needed. All gradients are overwritten (not accumulated into). */
 int gt_bwd(const sgat_plan* plan, int64_t n, int64_t nnz,
            const int64_t* rowptr, const int32_t* colidx,
            int H, int D, int dtype, const void* Q, const void* K, const void* V,
@@ -236,8 +237,11 @@ int gat_fwd(const sgat_plan* plan, int64_t n, int64_t nnz,
             void* out, float* lse, void* ws, size_t ws_bytes, void* stream);
 
 /* Backward of L = sum(out * dout): dx_dst, dx_nbr (input dtype, [n,H,D]) and
- * da (fp32 [H,D]), all overwritten. da is reduced from per-workgroup partials
- * in fixed order. */
+ * da (fp32 [H,D]), all overwritten. The CSR pass recomputes alpha_ij from lse,
+ * accumulates dx_dst and per-workgroup da partials, and leaves per edge the
+ * weight, dE_ij = alpha_ij (dout_i . x_nbr[j] - Delta_i) and the signs of z in
+ * the workspace; the transposed-CSR pass reads them and gathers only dout_i
+ * for dx_nbr. da is reduced from the partials in fixed order. */
 int gat_bwd(const sgat_plan* plan, int64_t n, int64_t nnz,
             const int64_t* rowptr, const int32_t* colidx,
             int H, int D, int dtype, const void* x_dst, const void* x_nbr,

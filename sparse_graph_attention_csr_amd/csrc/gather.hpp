@@ -230,7 +230,7 @@ __device__ __forceinline__ void gat_online_step(Online<VEC>& st, const Frag (&xf
 
 template <int DT, int D, int EPW>
 __device__ __forceinline__ void gat_fwd_prologue(const GatFwdArgs& a, const Geo<DT, D, EPW>& g,
-                                                 const sgat_work_item& it, int64_t HD,
+                                                 const sgat_work_item& it, bool has, int64_t HD,
                                                  float (&xs)[Elem<DT>::VEC], float (&at)[Elem<DT>::VEC],
                                                  float (&as)[Elem<DT>::VEC])
 {
@@ -238,7 +238,7 @@ __device__ __forceinline__ void gat_fwd_prologue(const GatFwdArgs& a, const Geo<
 #pragma unroll
     for (int k = 0; k < VEC; ++k) xs[k] = at[k] = 0.f;
     if (g.hvalid) {
-        to_f32<DT>(ldg<DT>(a.Xs, static_cast<int64_t>(it.row) * HD + g.col), xs);
+        if (has) to_f32<DT>(ldg<DT>(a.Xs, static_cast<int64_t>(it.row) * HD + g.col), xs);
         ld_f32<VEC>(a.att + g.col, at);
     }
 #pragma unroll
@@ -257,7 +257,7 @@ __device__ __forceinline__ void gat_fwd_one(const GatFwdArgs& a, int64_t ii, int
     const G g(hg, a.H);
     const int64_t HD = static_cast<int64_t>(a.H) * D;
     float xs[VEC], at[VEC], as[VEC];
-    gat_fwd_prologue<DT, D, EPW>(a, g, it, HD, xs, at, as);
+    gat_fwd_prologue<DT, D, EPW>(a, g, it, true, HD, xs, at, as);
     Online<VEC> st;
     const int32_t* ci = a.colidx + it.begin;
     for (int base = 0; base < it.len; base += kWave) {
@@ -298,7 +298,7 @@ __device__ __forceinline__ void gat_fwd_multi(const GatFwdArgs& a, int64_t first
     sgat_work_item it{0, 0, 0, -1, 0};
     if (has) it = a.items[idx];
     float xs[VEC], at[VEC], as[VEC];
-    gat_fwd_prologue<DT, D, EPW>(a, g, it, HD, xs, at, as);
+    gat_fwd_prologue<DT, D, EPW>(a, g, it, has, HD, xs, at, as);
     Online<VEC> st;
     const int32_t* ci = a.colidx + it.begin;
     const int lead = g.sub * G::LPE;
