@@ -388,10 +388,11 @@ __global__ __launch_bounds__(kBlock) void reduce_bwd_gather(ReduceGatherArgs a)
     const E* ent = static_cast<const E*>(a.entries);
     const int32_t* ri = a.rowidx + it.begin;
     const int32_t* ce = a.col_edge + it.begin;
-    // Every load below is unconditional, at an index clamped into the row's
-    // block of F pairs; only the LDS update is masked. (A load under a
-    // lane-dependent branch is waited for inside that branch, which would
-    // serialise the edges.)
+    // Every load below is unconditional; only the LDS update is masked. (A
+    // load under a lane-dependent branch is waited for inside that branch,
+    // which would serialise the edges.) Lanes past an edge's count load the
+    // edge's last pair again (index clamped to the slice, and to the row's F
+    // pairs), so they fetch no memory beyond the slice.
     for (int base = 0; base < it.len; base += kWave) {
         const int nb = min(kWave, it.len - base);
         const int lc = min(lane, nb - 1);
@@ -408,7 +409,8 @@ __global__ __launch_bounds__(kBlock) void reduce_bwd_gather(ReduceGatherArgs a)
                 row[u] = __builtin_amdgcn_readlane(li, e);
                 cnt[u] = t + u < nb ? sv >> 16 : 0u;
                 st[u] = sv & 0xffffu;
-                const int64_t k = min(static_cast<int64_t>(st[u]) + lane, F - 1);
+                const uint32_t last = cnt[u] > 0 ? cnt[u] - 1 : 0u;
+                const int64_t k = min(static_cast<int64_t>(st[u] + min(static_cast<uint32_t>(lane), last)), F - 1);
                 x[u] = ent[row[u] * F + k];
             }
             // pairs inside [start, start + count) were written by this call's
@@ -425,7 +427,8 @@ __global__ __launch_bounds__(kBlock) void reduce_bwd_gather(ReduceGatherArgs a)
 #pragma unroll
             for (int u = 0; u < U; ++u)
                 for (uint32_t c0 = kWave; c0 < cnt[u]; c0 += kWave) {
-                    const int64_t k = min(static_cast<int64_t>(st[u] + c0) + lane, F - 1);
+                    const uint32_t o = min(c0 + static_cast<uint32_t>(lane), cnt[u] - 1);
+                    const int64_t k = min(static_cast<int64_t>(st[u] + o), F - 1);
                     const E y = ent[row[u] * F + k];
                     const bool live = c0 + lane < cnt[u];
                     acc[live ? route_feature<DT>(y) : spare] += route_value<DT>(y) * (live ? 1.f : 0.f);
