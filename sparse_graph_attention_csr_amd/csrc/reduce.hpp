@@ -265,7 +265,9 @@ template <int DT, int NR>
 __global__ __launch_bounds__(kBlock) void reduce_bwd_route(ReduceRouteArgs a)
 {
     constexpr int VEC = Elem<DT>::VEC;
-    __shared__ int32_t hist_all[kWavesPerBlock][kRouteWindow];
+    // the window's counters, then one spare counter per lane that entries
+    // outside the window update (so the atomics need no lane-dependent branch)
+    __shared__ int32_t hist_all[kWavesPerBlock][kRouteWindow + kWave];
     const int64_t unit = logical_block() * kWavesPerBlock + wave_id();
     if (unit >= a.n_items) return;
     const sgat_work_item it = a.items[unit];
@@ -303,12 +305,13 @@ __global__ __launch_bounds__(kBlock) void reduce_bwd_route(ReduceRouteArgs a)
         const int nb = static_cast<int>(d - w0 < kRouteWindow ? d - w0 : kRouteWindow);
         for (int b = lane; b < nb; b += kWave) hist[b] = 0;
         wave_lds_fence();
+        const int spare = kRouteWindow + lane;
 #pragma unroll
         for (int k = 0; k < NR; ++k)
 #pragma unroll
             for (int v = 0; v < VEC; ++v) {
                 const int32_t b = q[k][v] - w0;
-                if (fv[k] && b >= 0 && b < nb) atomicAdd(&hist[b], 1);
+                atomicAdd(&hist[fv[k] && b >= 0 && b < nb ? b : spare], 1);
             }
         wave_lds_fence();
         for (int b0 = 0; b0 < nb; b0 += kWave) {
@@ -323,18 +326,26 @@ __global__ __launch_bounds__(kBlock) void reduce_bwd_route(ReduceRouteArgs a)
             total += __builtin_amdgcn_readlane(incl, 63);
         }
         wave_lds_fence();
+        // all slots first (the atomics issue back to back), then the stores
+        int slot[NR][VEC];
+#pragma unroll
+        for (int k = 0; k < NR; ++k)
+#pragma unroll
+            for (int v = 0; v < VEC; ++v) {
+                const int32_t b = q[k][v] - w0;
+                slot[k][v] = atomicAdd(&hist[fv[k] && b >= 0 && b < nb ? b : spare], 1);
+            }
 #pragma unroll
         for (int k = 0; k < NR; ++k)
 #pragma unroll
             for (int v = 0; v < VEC; ++v) {
                 const int32_t b = q[k][v] - w0;
                 if (fv[k] && b >= 0 && b < nb) {
-                    const int slot = atomicAdd(&hist[b], 1);
                     const uint32_t f = static_cast<uint32_t>((k * kWave + lane) * VEC + v);
                     if constexpr (DT == SGAT_BF16)
-                        ent[slot] = f | (__float_as_uint(dv[k][v]) & 0xffff0000u);
+                        ent[slot[k][v]] = f | (__float_as_uint(dv[k][v]) & 0xffff0000u);
                     else
-                        ent[slot] = make_uint2(f, __float_as_uint(dv[k][v]));
+                        ent[slot[k][v]] = make_uint2(f, __float_as_uint(dv[k][v]));
                 }
             }
         wave_lds_fence();
