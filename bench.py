@@ -75,10 +75,11 @@ def mfma_flops(kernel: str, H: int, D: int, tw: dict) -> float | None:
     the weighted sum (16xDx16), 2 flops per multiply-add each."""
     if not tw:
         return None
-    per = {"gt_bs_fwd": 2, "gt_bs_bwd_rows": 3, "gt_bs_bwd_cols": 4}.get(kernel)
+    per = {"gt_bs_fwd": 2, "gt_bs_bwd_rows": 3, "gt_bs_bwd_cols": 2}.get(kernel)
     if per is None:
         return None
-    # forward: S, PV; rows: S, dP, dS K; cols: S, dP, dS^T Q, P^T dO
+    # forward: S, PV; rows: S, dP, dS K; cols: dS^T Q, P^T dO (P and dS come
+    # from the row pass)
     return float((tw["tiles"] + tw["pseudo_tiles"]) * H * per * (2 * 16 * 16 * D))
 
 
@@ -144,14 +145,17 @@ def algorithmic_bytes(kernel: str, n: int, e: int, H: int, D: int, b: int,
         # residual edges gather K_j and V_j; each tile reads its column and mask
         return (4 * R + 4 * H + 16) * n + (2 * R + 4) * tw["residual_edges"] + 36 * tw["tiles"]
     if kernel == "gt_bs_bwd_rows" and tw:
-        # Q, dO, O, lse read and dQ, (lse, Delta) written per node; K, V once per
-        # node through the tiles; residual edges gather K_j, V_j
-        return (6 * R + 12 * H + 16) * n + (2 * R + 4) * tw["residual_edges"] + 36 * tw["tiles"]
+        # Q, dO, O, lse read and dQ written per node; K, V once per node through
+        # the tiles; residual edges gather K_j, V_j; P and dS written for the
+        # column pass: 2 x 512 bytes per (tile, head), 4 bytes per (residual edge, head)
+        return ((6 * R + 4 * H + 16) * n + (2 * R + 4 + 4 * H) * tw["residual_edges"]
+                + (36 + 1024 * H) * tw["tiles"])
     if kernel == "gt_bs_bwd_cols" and tw:
-        # K, V read and dK, dV written per node; Q, dO and (lse, Delta) once per
-        # node through the tiles; residual edges gather Q_i, dO_i, (lse_i, Delta_i)
-        return ((6 * R + 8 * H + 16) * n + (2 * R + 8 * H + 4) * tw["residual_edges"]
-                + 40 * tw["tiles"])
+        # dK, dV written per node; Q, dO once per node through the tiles, with
+        # the tiles' P and dS; residual edges gather Q_i, dO_i and read their
+        # destination, residual edge id and (P, dS)
+        return ((4 * R + 16) * n + (2 * R + 8 + 4 * H) * tw["residual_edges"]
+                + (8 + 1024 * H) * tw["tiles"])
     model = {
         # K_j, V_j and colidx per edge; Q_i read, out_i and lse_i written per node
         "gt_fwd_rows": (2 * R + 4, 2 * R + 4 * H + 8),

@@ -134,7 +134,9 @@ typedef enum sgat_array {
     SGAT_ARR_RES_COLPTR = 14, /* int64 [n+1]: residual edges grouped by source          */
     SGAT_ARR_RES_ROWIDX = 15, /* int32 [residual_edges]: their destinations             */
     SGAT_ARR_COL_EDGE = 16,   /* int32 [nnz]: CSR edge id of each transposed-CSR entry  */
-    SGAT_ARR_COUNT = 17
+    SGAT_ARR_RES_COL_EDGE = 17,/* int32 [residual_edges]: residual-CSR edge id of each
+                                 transposed residual entry                              */
+    SGAT_ARR_COUNT = 18
 } sgat_array;
 
 /* One unit of work of the gather kernels: `len` consecutive edges starting at
@@ -217,7 +219,9 @@ int gt_fwd(const sgat_plan* plan, int64_t n, int64_t nnz,
  * Delta_i = dout_i . out_i per head; dS_ij = alpha_ij (dout_i . V_j - Delta_i).
  * The transposed-CSR pass computes dK, dV and dS, leaving dS per (edge, head)
  * in the workspace; the CSR pass then accumulates dQ from it, so no atomics are
- * needed. All gradients are overwritten (not accumulated into). */
+ * needed. With use_tiles = 1 the order is reversed: the tile-row pass computes
+ * dQ and leaves P and dS per edge for the tile-column pass (dK, dV).
+ * All gradients are overwritten (not accumulated into). */
 int gt_bwd(const sgat_plan* plan, int64_t n, int64_t nnz,
            const int64_t* rowptr, const int32_t* colidx,
            int H, int D, int dtype, const void* Q, const void* K, const void* V,

@@ -107,7 +107,7 @@ int check_tensor(const void* p, int64_t n)
 }
 
 struct Layout {
-    size_t off[6] = {};
+    size_t off[8] = {};
     size_t total = 0;
 };
 
@@ -115,7 +115,7 @@ struct Layout {
 Layout ws_layout(const Plan& p, int op, int H, int D, int dt)
 {
     const size_t HD = static_cast<size_t>(H) * D;
-    size_t sz[6] = {};
+    size_t sz[8] = {};
     switch (op) {
     case SGAT_OP_GT_FWD:
     case SGAT_OP_GAT_FWD:
@@ -128,6 +128,10 @@ Layout ws_layout(const Plan& p, int op, int H, int D, int dt)
         sz[2] = static_cast<size_t>(p.col_slots) * HD * 4;          // dK partials
         sz[3] = static_cast<size_t>(p.col_slots) * HD * 4;          // dV partials
         sz[4] = static_cast<size_t>(p.nnz) * H * 4;                 // dS per edge
+        if (p.block_sparse) {   // the tile path's edge weights (P, dS)
+            sz[6] = static_cast<size_t>(p.tile_col.size()) * H * 2 * 64 * 8;   // per tile, head
+            sz[7] = static_cast<size_t>(p.res_colidx.size()) * H * 4;         // per residual edge, head
+        }
         break;
     case SGAT_OP_GAT_BWD:
         sz[0] = static_cast<size_t>(p.nnz) * gat_edge_record_dwords(dt, D, H) * 4; // edge records
@@ -152,7 +156,7 @@ Layout ws_layout(const Plan& p, int op, int H, int D, int dt)
     }
     Layout L;
     size_t off = 0;
-    for (int r = 0; r < 6; ++r) {
+    for (int r = 0; r < 8; ++r) {
         L.off[r] = off;
         off = align_up(off + sz[r]);
     }
@@ -268,7 +272,8 @@ int gt_bwd(const sgat_plan* plan, int64_t n, int64_t nnz, const int64_t* rowptr,
     if (n == 0) return SGAT_OK;
     if (use_tiles)
         return launch_gt_bs_bwd(plan->p, H, D, Q, K, V, out, lse, dout, dQ, dK, dV,
-                                at<void>(ws, L.off[0]), static_cast<hipStream_t>(stream));
+                                at<void>(ws, L.off[6]), at<void>(ws, L.off[7]),
+                                static_cast<hipStream_t>(stream));
     BwdWs w{at<void>(ws, L.off[0]), at<float>(ws, L.off[1]), at<float>(ws, L.off[2]),
             at<float>(ws, L.off[3]), nullptr, at<float>(ws, L.off[4])};
     return launch_gt_bwd(plan->p, H, D, dtype, colidx, Q, K, V, out, lse, dout, dQ, dK, dV, w,

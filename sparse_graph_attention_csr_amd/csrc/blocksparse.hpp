@@ -361,8 +361,10 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
 }
 
 // ---------------------------------------------------------------------------
-// backward: recompute S and dP per tile from the forward's lse, no stored
-// edge values; dQ per tile row, dK and dV per tile column, no atomics
+// backward: the tile-row pass recomputes S and dP per tile from the forward's
+// lse (nothing per edge is kept from the forward), accumulates dQ and hands P
+// and dS of every edge to the tile-column pass, which accumulates dK and dV;
+// no atomics
 // ---------------------------------------------------------------------------
 
 struct BsBwdArgs {
@@ -378,9 +380,15 @@ struct BsBwdArgs {
     const int32_t* res_colidx;
     const int64_t* res_colptr;
     const int32_t* res_rowidx;
+    const int32_t* res_col_edge;
     const void *Q, *K, *V, *O, *dO;
     const float* lse;
-    RowStat* stats;
+    // weights and dS of every edge, from the tile-row pass to the tile-column
+    // pass: per (dense tile, head) the P^T and dS^T operand fragments of the
+    // 64 lanes (8 bytes each), per (residual edge, head) one word (bf16 P low,
+    // bf16 dS high)
+    uint2* tile_pd;      // [tiles][H][2][64]
+    uint32_t* res_pd;    // [residual_edges][H]
     void *dQ, *dK, *dV;
     float scale2, oscale;
 };
@@ -421,20 +429,27 @@ __device__ __forceinline__ void row_bwd_phase_a(const RowBwdTile<D>& tl,
     store_operand_tile<D>(ks, tl.kf, i, g);
 }
 
+// Tile-row step, phase B: P and dS of the lane's four entries (also staged
+// row-major in the wave's LDS tiles pt, for hand_off()), dQ^T += K^T dS^T from
+// LDS.
 template <int D>
 __device__ __forceinline__ void row_bwd_phase_b(const f32x4_t& st, const f32x4_t& dp,
                                                 uint32_t valid, float lse2, float delta,
                                                 f32x4_t (&acc)[Shape<D>::NB], const uint16_t* ks,
-                                                float scale2, int i, int g)
+                                                float scale2, int i, int g,
+                                                uint16_t (*pt)[kTileDim * kTileDim])
 {
     using S = Shape<D>;
-    short dsb[4];
+    short pb[4], dsb[4];
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
         const float p = ((valid >> k) & 1u) ? fast_exp2(st[k] * scale2 - lse2) : 0.f;
+        pb[k] = bf16_bits(p);
         dsb[k] = bf16_bits(p * (dp[k] - delta));
     }
     const s16x4_t b = {dsb[0], dsb[1], dsb[2], dsb[3]};
+    *reinterpret_cast<s16x4_t*>(&pt[0][i * kTileDim + 4 * g]) = s16x4_t{pb[0], pb[1], pb[2], pb[3]};
+    *reinterpret_cast<s16x4_t*>(&pt[1][i * kTileDim + 4 * g]) = b;
     __builtin_amdgcn_wave_barrier();
     const uint16_t* kt = operand_tr_base<D>(ks, i, g);
 #pragma unroll
@@ -445,11 +460,39 @@ __device__ __forceinline__ void row_bwd_phase_b(const f32x4_t& st, const f32x4_t
     __builtin_amdgcn_wave_barrier();
 }
 
+// Hands tile k's P and dS, staged row-major in pt by phase B, to the
+// tile-column pass. Dense tile: read back with the transposing read so that
+// lane (c, g) holds rows 4g..4g+3 of column c (the column pass's B operand),
+// and stored as that lane's 8 bytes. Residual pseudo-tile: lane c < 16 stores
+// the pair of its column's edge e (at the edge's row) as one word.
+__device__ __forceinline__ void hand_off(const BsBwdArgs& a, const RowTiles& tiles, int64_t k,
+                                         int h, uint16_t (*pt)[kTileDim * kTileDim], int l,
+                                         int i, int g)
+{
+    if (k < tiles.nd) {
+        // lane m of a 16-lane group addresses row 4g + m / 4, columns 4 (m % 4)..+3
+        const int off = (4 * g + i / 4) * kTileDim + 4 * (i % 4);
+        uint2* dst = a.tile_pd + (static_cast<int64_t>(tiles.tb + k) * a.H + h) * 2 * kWave;
+        dst[l] = __builtin_bit_cast(uint2, lds_read_tr16(&pt[0][off]));
+        dst[kWave + l] = __builtin_bit_cast(uint2, lds_read_tr16(&pt[1][off]));
+    } else {
+        const int64_t e = tiles.rb + (k - tiles.nd) * 16 + l;   // column l is residual edge e
+        if (l < kTileDim && e < tiles.re) {
+            const int r = tiles.starts.row_of(e);
+            a.res_pd[e * a.H + h] = static_cast<uint32_t>(pt[0][r * kTileDim + l]) |
+                                    (static_cast<uint32_t>(pt[1][r * kTileDim + l]) << 16);
+        }
+    }
+    __builtin_amdgcn_wave_barrier();
+}
+
 template <int D>
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) void gt_bs_bwd_rows(BsBwdArgs a)
 {
     using S = Shape<D>;
     __shared__ __attribute__((aligned(16))) uint16_t ks_all[kWavesPerBlock][16 * S::LDV];
+    // one 16x16 bf16 tile of P and one of dS, row-major, to transpose them
+    __shared__ __attribute__((aligned(16))) uint16_t pt_all[kWavesPerBlock][2][kTileDim * kTileDim];
     const int64_t br = logical_block();
     if (br >= a.n_blocks) return;
     const int w = wave_id();
@@ -491,7 +534,6 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
         dsum += __shfl_xor(dsum, 16);
         dsum += __shfl_xor(dsum, 32);
         if (row_ok) lse2 = a.lse[row * a.H + h] * kLog2e;
-        if (row_ok && g == 0) a.stats[row * a.H + h] = RowStat{lse2, dsum};
         f32x4_t acc[S::NB];
 #pragma unroll
         for (int s = 0; s < S::NB; ++s) acc[s] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -519,7 +561,8 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
                 if (k + 2 < nt) tiles.fetch(k + 2, i, col2, word2);
                 tile.load(a.K, a.V, rnext.src * HD + hoff, g);
             }
-            row_bwd_phase_b<D>(st, dp, valid, lse2, dsum, acc, ks, a.scale2, i, g);
+            row_bwd_phase_b<D>(st, dp, valid, lse2, dsum, acc, ks, a.scale2, i, g, pt_all[w]);
+            hand_off(a, tiles, k, h, pt_all[w], l, i, g);
         }
         if (row_ok) {
 #pragma unroll
@@ -539,63 +582,66 @@ struct ColTiles {
     int H, h;
     const int32_t* tile_bycol;
     const int32_t* tile_row;
-    const uint16_t* tile_mask;
     const int32_t* res_rowidx;
-    const RowStat* stats;
+    const int32_t* res_col_edge;
+    const uint2* tile_pd;
+    const uint32_t* res_pd;
     BlockStarts starts;
 
     __device__ __forceinline__ int64_t count() const { return nd + (rce - rcb + 15) / 16; }
 
-    // dense tile: t = tile id; residual pseudo-tile: dst = destination of row l%16
-    __device__ __forceinline__ void fetch(int64_t k, int c, int32_t& t, int32_t& dst) const
+    // dense tile: t = tile id; residual pseudo-tile: dst = destination of row
+    // l%16 and re = its residual-CSR edge id
+    __device__ __forceinline__ void fetch(int64_t k, int c, int32_t& t, int32_t& dst,
+                                          int32_t& re) const
     {
         if (k < nd) {
             t = tile_bycol[tcb + k];
             dst = 0;
+            re = 0;
         } else {
             const int64_t e = rcb + (k - nd) * 16 + c;
             t = 0;
             dst = e < rce ? res_rowidx[e] : 0;
+            re = e < rce ? res_col_edge[e] : -1;
         }
     }
 };
 
+// One tile of the column pass: the Q and dO rows of its 16 destinations (A
+// operand layout) and this lane's P^T and dS^T fragments (rows 4g..4g+3 of
+// column l%16), both left by the tile-row pass.
 template <int D>
 struct ColBwdTile {
     Frag qa[Shape<D>::KS], oa[Shape<D>::KS];
-    RowStat st[4];
-    uint32_t valid;
+    s16x4_t pt, dt;
 
     __device__ __forceinline__ void load(const ColTiles& T, int64_t k, int32_t t, int32_t dst,
-                                         const void* Q, const void* dO, int64_t HD, int64_t hoff,
-                                         int c, int g)
+                                         int32_t re, const void* Q, const void* dO, int64_t HD,
+                                         int64_t hoff, int l, int c, int g)
     {
         int64_t arow = 0;
-        valid = 0;
         if (k < T.nd) {
-            const int64_t r0 = static_cast<int64_t>(T.tile_row[t]) * kTileDim;
-            arow = min(r0 + c, T.n - 1);
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const uint32_t bit =
-                    (static_cast<uint32_t>(T.tile_mask[static_cast<int64_t>(t) * kTileDim + 4 * g + q]) >> c) & 1u;
-                valid |= bit << q;
-                st[q] = RowStat{0.f, 0.f};
-                if (bit) st[q] = T.stats[(r0 + 4 * g + q) * T.H + T.h];
-            }
+            arow = min(static_cast<int64_t>(T.tile_row[t]) * kTileDim + c, T.n - 1);
+            const uint2* f = T.tile_pd + (static_cast<int64_t>(t) * T.H + T.h) * 2 * kWave;
+            pt = __builtin_bit_cast(s16x4_t, f[l]);
+            dt = __builtin_bit_cast(s16x4_t, f[kWave + l]);
         } else {
             const int64_t e = T.rcb + (k - T.nd) * 16 + c;   // row c of this pseudo-tile is edge e
             const int cc = e < T.rce ? T.starts.row_of(e) : -1;
+            const uint32_t w = re >= 0 ? T.res_pd[static_cast<int64_t>(re) * T.H + T.h] : 0u;
             arow = dst;
+            short pb[4], db[4];
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                const int lq = 4 * g + q;
+                const int lq = 4 * g + q;   // entry (row 4g + q, column c)
                 const bool bit = __shfl(cc, lq) == c;
-                const int64_t dr = __shfl(dst, lq);
-                valid |= (bit ? 1u : 0u) << q;
-                st[q] = RowStat{0.f, 0.f};
-                if (bit) st[q] = T.stats[dr * T.H + T.h];
+                const uint32_t wq = __shfl(w, lq);
+                pb[q] = static_cast<short>(bit ? (wq & 0xffffu) : 0u);
+                db[q] = static_cast<short>(bit ? (wq >> 16) : 0u);
             }
+            pt = s16x4_t{pb[0], pb[1], pb[2], pb[3]};
+            dt = s16x4_t{db[0], db[1], db[2], db[3]};
         }
         const int64_t qbase = arow * HD + hoff;
 #pragma unroll
@@ -606,66 +652,32 @@ struct ColBwdTile {
     }
 };
 
-// Tile-column step: S = Q K^T and dP = dO V^T in the lane layout of rows
-// 4g..4g+3, column l%16; dK^T += Q^T dS, dV^T += dO^T P (Q and dO transposed
-// through LDS).
-// Phase A consumes the tile registers (S, dP; Q and dO into LDS); phase B
-// forms P and dS and accumulates from LDS while the next tile's loads refill
-// the registers (the row statistics and edge bits are kept aside).
+// Tile-column step: dK^T += Q^T dS, dV^T += dO^T P, Q and dO transposed
+// through LDS. Phase A stores the tile's Q and dO rows (so the next tile's
+// loads can refill the registers), phase B accumulates from LDS.
 template <int D>
-__device__ __forceinline__ void col_bwd_phase_a(const ColBwdTile<D>& tl,
-                                                const bf16x8_t (&kf)[Shape<D>::KS],
-                                                const bf16x8_t (&vf)[Shape<D>::KS], f32x4_t& sc,
-                                                f32x4_t& dp, uint16_t* qs, uint16_t* os, int c,
-                                                int g)
-{
-    using S = Shape<D>;
-    sc = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    dp = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int s = 0; s < S::KS; ++s) {
-        sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, tl.qa[s]), kf[s],
-                                                     sc, 0, 0, 0);
-        dp = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, tl.oa[s]), vf[s],
-                                                     dp, 0, 0, 0);
-    }
-    store_operand_tile<D>(qs, tl.qa, c, g);
-    store_operand_tile<D>(os, tl.oa, c, g);
-}
-
-template <int D>
-__device__ __forceinline__ void col_bwd_phase_b(const f32x4_t& sc, const f32x4_t& dp,
-                                                const RowStat (&rs)[4], uint32_t valid,
+__device__ __forceinline__ void col_bwd_phase_b(const s16x4_t& pt, const s16x4_t& dt,
                                                 f32x4_t (&dk)[Shape<D>::NB],
                                                 f32x4_t (&dv)[Shape<D>::NB], const uint16_t* qs,
-                                                const uint16_t* os, float scale2, int c, int g)
+                                                const uint16_t* os, int c, int g)
 {
     using S = Shape<D>;
-    short pb[4], db[4];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        const float p = ((valid >> k) & 1u) ? fast_exp2(sc[k] * scale2 - rs[k].lse2) : 0.f;
-        pb[k] = bf16_bits(p);
-        db[k] = bf16_bits(p * (dp[k] - rs[k].delta));
-    }
-    const s16x4_t P = {pb[0], pb[1], pb[2], pb[3]};
-    const s16x4_t Sd = {db[0], db[1], db[2], db[3]};
     __builtin_amdgcn_wave_barrier();
     const uint16_t* qt = operand_tr_base<D>(qs, c, g);
     const uint16_t* ot = operand_tr_base<D>(os, c, g);
 #pragma unroll
     for (int s = 0; s < S::NB; ++s) {
         // Q[4g + kk][16s + c] and dO[4g + kk][16s + c], kk = 0..3
-        dk[s] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(lds_read_tr16(qt + 16 * s), Sd, dk[s],
+        dk[s] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(lds_read_tr16(qt + 16 * s), dt, dk[s],
                                                           0, 0, 0);
-        dv[s] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(lds_read_tr16(ot + 16 * s), P, dv[s],
+        dv[s] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(lds_read_tr16(ot + 16 * s), pt, dv[s],
                                                           0, 0, 0);
     }
     __builtin_amdgcn_wave_barrier();
 }
 
 template <int D>
-__global__ __launch_bounds__(kBlock) void gt_bs_bwd_cols(BsBwdArgs a)
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) void gt_bs_bwd_cols(BsBwdArgs a)
 {
     using S = Shape<D>;
     __shared__ __attribute__((aligned(16))) uint16_t qs_all[kWavesPerBlock][16 * S::LDV];
@@ -686,9 +698,10 @@ __global__ __launch_bounds__(kBlock) void gt_bs_bwd_cols(BsBwdArgs a)
     T.H = a.H;
     T.tile_bycol = a.tile_bycol;
     T.tile_row = a.tile_row;
-    T.tile_mask = a.tile_mask;
     T.res_rowidx = a.res_rowidx;
-    T.stats = a.stats;
+    T.res_col_edge = a.res_col_edge;
+    T.tile_pd = a.tile_pd;
+    T.res_pd = a.res_pd;
     T.starts.load(a.res_colptr, c_lo, c_hi);
     const int64_t nt = T.count();
     const int64_t j = c_lo + c;
@@ -699,16 +712,6 @@ __global__ __launch_bounds__(kBlock) void gt_bs_bwd_cols(BsBwdArgs a)
     for (int h = w; h < a.H; h += kWavesPerBlock) {
         T.h = h;
         const int64_t hoff = static_cast<int64_t>(h) * D;
-        bf16x8_t kf[S::KS], vf[S::KS];
-#pragma unroll
-        for (int s = 0; s < S::KS; ++s) {
-            kf[s] = bf16x8_t{};
-            vf[s] = bf16x8_t{};
-            if (j_ok) {
-                kf[s] = ld_bf16x8(a.K, j * HD + hoff + 32 * s + 8 * g);
-                vf[s] = ld_bf16x8(a.V, j * HD + hoff + 32 * s + 8 * g);
-            }
-        }
         f32x4_t dk[S::NB], dv[S::NB];
 #pragma unroll
         for (int s = 0; s < S::NB; ++s) {
@@ -716,26 +719,25 @@ __global__ __launch_bounds__(kBlock) void gt_bs_bwd_cols(BsBwdArgs a)
             dv[s] = f32x4_t{0.f, 0.f, 0.f, 0.f};
         }
         // pipeline: descriptions two tiles ahead; tile k+1's data refills the
-        // tile registers once phase A of tile k has consumed them
+        // tile registers once phase A of tile k has put them into LDS
         ColBwdTile<D> tile;
-        int32_t t2 = 0, d2 = 0;
+        int32_t t2 = 0, d2 = 0, r2 = 0;
         if (nt > 0) {
-            int32_t t0, d0;
-            T.fetch(0, c, t0, d0);
-            tile.load(T, 0, t0, d0, a.Q, a.dO, HD, hoff, c, g);
+            int32_t t0, d0, r0;
+            T.fetch(0, c, t0, d0, r0);
+            tile.load(T, 0, t0, d0, r0, a.Q, a.dO, HD, hoff, l, c, g);
         }
-        if (nt > 1) T.fetch(1, c, t2, d2);
+        if (nt > 1) T.fetch(1, c, t2, d2, r2);
         for (int64_t k = 0; k < nt; ++k) {
-            const uint32_t valid = tile.valid;
-            const RowStat rs[4] = {tile.st[0], tile.st[1], tile.st[2], tile.st[3]};
-            f32x4_t sc, dp;
-            col_bwd_phase_a<D>(tile, kf, vf, sc, dp, qs, os, c, g);
+            const s16x4_t pt = tile.pt, dt = tile.dt;
+            store_operand_tile<D>(qs, tile.qa, c, g);
+            store_operand_tile<D>(os, tile.oa, c, g);
             if (k + 1 < nt) {
-                const int32_t t1 = t2, d1 = d2;
-                if (k + 2 < nt) T.fetch(k + 2, c, t2, d2);
-                tile.load(T, k + 1, t1, d1, a.Q, a.dO, HD, hoff, c, g);
+                const int32_t t1 = t2, d1 = d2, r1 = r2;
+                if (k + 2 < nt) T.fetch(k + 2, c, t2, d2, r2);
+                tile.load(T, k + 1, t1, d1, r1, a.Q, a.dO, HD, hoff, l, c, g);
             }
-            col_bwd_phase_b<D>(sc, dp, rs, valid, dk, dv, qs, os, a.scale2, c, g);
+            col_bwd_phase_b<D>(pt, dt, dk, dv, qs, os, c, g);
         }
         if (j_ok) {
 #pragma unroll

@@ -66,7 +66,7 @@ int launch_gt_bs_fwd(const Plan& p, int H, int D, const void* Q, const void* K, 
 // dK and dV per tile column. `stats` is the [n][H] (lse*log2 e, Delta) region.
 int launch_gt_bs_bwd(const Plan& p, int H, int D, const void* Q, const void* K, const void* V,
                      const void* O, const float* lse, const void* dO, void* dQ, void* dK, void* dV,
-                     void* stats, hipStream_t s);
+                     void* tile_pd, void* res_pd, hipStream_t s);
 
 // Min/max aggregation: lanes per edge and fragments per lane for F features.
 constexpr int kReduceMaxF = 2048;

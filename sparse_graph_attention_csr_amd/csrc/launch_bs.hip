@@ -30,7 +30,7 @@ int launch_gt_bs_fwd(const Plan& p, int H, int D, const void* Q, const void* K, 
 
 int launch_gt_bs_bwd(const Plan& p, int H, int D, const void* Q, const void* K, const void* V,
                      const void* O, const float* lse, const void* dO, void* dQ, void* dK, void* dV,
-                     void* stats, hipStream_t s)
+                     void* tile_pd, void* res_pd, hipStream_t s)
 {
     BsBwdArgs a;
     a.n = p.n;
@@ -46,9 +46,11 @@ int launch_gt_bs_bwd(const Plan& p, int H, int D, const void* Q, const void* K, 
     a.res_colidx = p.dptr<int32_t>(SGAT_ARR_RES_COLIDX);
     a.res_colptr = p.dptr<int64_t>(SGAT_ARR_RES_COLPTR);
     a.res_rowidx = p.dptr<int32_t>(SGAT_ARR_RES_ROWIDX);
+    a.res_col_edge = p.dptr<int32_t>(SGAT_ARR_RES_COL_EDGE);
     a.Q = Q; a.K = K; a.V = V; a.O = O; a.dO = dO;
     a.lse = lse;
-    a.stats = static_cast<RowStat*>(stats);
+    a.tile_pd = static_cast<uint2*>(tile_pd);
+    a.res_pd = static_cast<uint32_t*>(res_pd);
     a.dQ = dQ; a.dK = dK; a.dV = dV;
     a.scale2 = kLog2e / sqrtf(static_cast<float>(D));
     a.oscale = 1.f / sqrtf(static_cast<float>(D));

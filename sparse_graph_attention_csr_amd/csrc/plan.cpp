@@ -278,6 +278,7 @@ const void* Plan::host_array(int id) const
     case SGAT_ARR_TILE_BYCOL: return tile_bycol.data();
     case SGAT_ARR_RES_COLPTR: return res_colptr.data();
     case SGAT_ARR_RES_ROWIDX: return res_rowidx.data();
+    case SGAT_ARR_RES_COL_EDGE: return res_col_edge.data();
     case SGAT_ARR_COL_EDGE: return col_edge.data();
     default: return nullptr;
     }
@@ -301,6 +302,7 @@ void Plan::layout()
     bytes[SGAT_ARR_TILE_BYCOL] = tile_bycol.size() * sizeof(int32_t);
     bytes[SGAT_ARR_RES_COLPTR] = res_colptr.size() * sizeof(int64_t);
     bytes[SGAT_ARR_RES_ROWIDX] = res_rowidx.size() * sizeof(int32_t);
+    bytes[SGAT_ARR_RES_COL_EDGE] = res_col_edge.size() * sizeof(int32_t);
     bytes[SGAT_ARR_COL_EDGE] = col_edge.size() * sizeof(int32_t);
     size_t off = 0;
     for (int a = 0; a < SGAT_ARR_COUNT; ++a) {
@@ -365,7 +367,7 @@ int sgat_plan_create(int64_t n, int64_t nnz, const int64_t* rowptr, const int32_
             sgat::build_tile_columns(n, p.tile_rowptr, p.tile_col, p.tile_row, p.tile_colptr,
                                      p.tile_bycol);
             sgat::build_transpose(n, p.res_rowptr.data(), p.res_colidx.data(), p.res_colptr,
-                                  p.res_rowidx);
+                                  p.res_rowidx, &p.res_col_edge);
         }
         p.layout();
     } catch (const std::bad_alloc&) {

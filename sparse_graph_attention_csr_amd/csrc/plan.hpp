@@ -48,6 +48,7 @@ struct Plan {
     std::vector<int32_t> tile_bycol;
     std::vector<int64_t> res_colptr;    // transposed residual CSR
     std::vector<int32_t> res_rowidx;
+    std::vector<int32_t> res_col_edge;  // residual-CSR edge id of each transposed residual entry
     int64_t tile_edges = 0;
 
     // device image: every array at a 256-byte aligned offset of one buffer

@@ -39,9 +39,10 @@ def check_plan(rowptr, colidx, chunk, tmin=0, bs=False, loc=False):
         assert np.array_equal(p.export(B.ARR_TILE_ROW), trow)
         assert np.array_equal(p.export(B.ARR_TILE_COLPTR), tcp)
         assert np.array_equal(p.export(B.ARR_TILE_BYCOL), tbc)
-        rcp, rri = S.transpose(rr, rc)
+        rcp, rri, rce = S.transpose(rr, rc, edge_ids=True)
         assert np.array_equal(p.export(B.ARR_RES_COLPTR), rcp)
         assert np.array_equal(p.export(B.ARR_RES_ROWIDX), rri)
+        assert np.array_equal(p.export(B.ARR_RES_COL_EDGE), rce)
     return p
 
 
