@@ -49,11 +49,22 @@ def kernel_family(kernel: str) -> str:
     return "reduce" if kernel.startswith("reduce_") else "gather"
 
 
+def _code_only(text: str) -> str:
+    """C++ source without comments, blank lines or trailing spaces (so that a
+    comment edit does not disown counters taken on the same code)."""
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    return "\n".join(line.rstrip() for line in text.splitlines() if line.strip())
+
+
 def kernel_source_hash(kernel: str) -> str:
+    """Hash of the code of the sources a kernel family is built from; counter
+    summaries under profiles/ record it, and bench.py uses a summary's HBM
+    traffic only while the code still hashes the same."""
     h = hashlib.sha256()
     for p in KERNEL_SOURCES[kernel_family(kernel)]:
-        with open(os.path.join(ROOT, p), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, p), encoding="utf-8") as f:
+            h.update(_code_only(f.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -275,7 +275,7 @@ int gt_bwd(const sgat_plan* plan, int64_t n, int64_t nnz, const int64_t* rowptr,
                                 at<void>(ws, L.off[6]), at<void>(ws, L.off[7]),
                                 static_cast<hipStream_t>(stream));
     BwdWs w{at<void>(ws, L.off[0]), at<float>(ws, L.off[1]), at<float>(ws, L.off[2]),
-            at<float>(ws, L.off[3]), nullptr, at<float>(ws, L.off[4])};
+            at<float>(ws, L.off[3]), nullptr, at<float>(ws, L.off[4]), nullptr};
     return launch_gt_bwd(plan->p, H, D, dtype, colidx, Q, K, V, out, lse, dout, dQ, dK, dV, w,
                          static_cast<hipStream_t>(stream));
 }

@@ -1,6 +1,7 @@
 // Gather-path kernels: one wavefront per work item (a whole row, or one chunk
-// of a split row), neighbour rows gathered straight from HBM in 16-byte lane
-// fragments, scores and weights kept in registers.
+// of a split row; in the GATv2 kernels short items go several to a wavefront,
+// one per edge group), neighbour rows gathered straight from HBM in 16-byte
+// lane fragments, scores and weights kept in registers.
 //
 // The fused forward computes, per destination i and head h, the scores of its
 // in-edges, an online softmax and the weighted sum of neighbour rows in one
@@ -16,7 +17,8 @@
 // transposed-CSR pass runs first; it holds K_j and V_j of its source, gathers
 // Q_i and dout_i, forms dS_ij and writes it (H floats per edge) for the CSR
 // pass, which then gathers only K_j for dQ. GATv2: the CSR pass (dXs, da,
-// Delta) runs first and the transposed pass (dXt) recomputes everything.
+// Delta) runs first and leaves per edge p_ij, dE_ij and the signs of z_ij, so
+// the transposed pass (dXt) gathers only dout_i.
 #pragma once
 
 #include "device.hpp"
