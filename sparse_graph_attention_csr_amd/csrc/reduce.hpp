@@ -233,7 +233,7 @@ __global__ __launch_bounds__(kBlock) void reduce_merge(ReduceMergeArgs a)
 // source, in transposed-CSR order, add its pairs into an LDS accumulator of F
 // values; one edge's pairs name distinct features, so lanes never collide,
 // and a feature receives the edges' contributions in a fixed order.
-constexpr int kRouteWindow = 1024;        // histogram bins per wave
+constexpr int kRouteWindow = 512;         // histogram bins per wave
 
 template <int DT> struct RouteEntry;      // (feature, dout) pair of one winner
 template <> struct RouteEntry<SGAT_BF16> { using T = uint32_t; };   // f | bf16 bits << 16
@@ -268,6 +268,13 @@ __global__ __launch_bounds__(kBlock) void reduce_bwd_route(ReduceRouteArgs a)
     // the window's counters, then one spare counter per lane that entries
     // outside the window update (so the atomics need no lane-dependent branch)
     __shared__ int32_t hist_all[kWavesPerBlock][kRouteWindow + kWave];
+    // Where a row's pairs fit 4 KB, they are placed at their slots in LDS and
+    // written out with contiguous stores once per window, instead of one
+    // scattered 4- or 8-byte store per feature.
+    using E = typename RouteEntry<DT>::T;
+    constexpr int kRowPairs = NR * kWave * VEC;
+    constexpr bool kStage = kRowPairs * sizeof(E) <= 4096;
+    __shared__ E stage_all[kWavesPerBlock][kStage ? kRowPairs : 1];
     const int64_t unit = logical_block() * kWavesPerBlock + wave_id();
     if (unit >= a.n_items) return;
     const sgat_work_item it = a.items[unit];
@@ -298,8 +305,8 @@ __global__ __launch_bounds__(kBlock) void reduce_bwd_route(ReduceRouteArgs a)
         for (int v = 0; v < VEC; ++v) q[k][v] = w[v] - static_cast<int32_t>(r0);
     }
 
-    using E = typename RouteEntry<DT>::T;
     E* ent = static_cast<E*>(a.entries) + rowF;
+    E* stage = stage_all[wave_id()];
     int total = 0;
     for (int32_t w0 = 0; w0 < d; w0 += kRouteWindow) {
         const int nb = static_cast<int>(d - w0 < kRouteWindow ? d - w0 : kRouteWindow);
@@ -314,6 +321,7 @@ __global__ __launch_bounds__(kBlock) void reduce_bwd_route(ReduceRouteArgs a)
                 atomicAdd(&hist[fv[k] && b >= 0 && b < nb ? b : spare], 1);
             }
         wave_lds_fence();
+        const int win_lo = total;   // this window's pairs take slots [win_lo, total)
         for (int b0 = 0; b0 < nb; b0 += kWave) {
             const int b = b0 + lane;
             const int c = b < nb ? hist[b] : 0;
@@ -342,13 +350,22 @@ __global__ __launch_bounds__(kBlock) void reduce_bwd_route(ReduceRouteArgs a)
                 const int32_t b = q[k][v] - w0;
                 if (fv[k] && b >= 0 && b < nb) {
                     const uint32_t f = static_cast<uint32_t>((k * kWave + lane) * VEC + v);
+                    E x;
                     if constexpr (DT == SGAT_BF16)
-                        ent[slot[k][v]] = f | (__float_as_uint(dv[k][v]) & 0xffff0000u);
+                        x = f | (__float_as_uint(dv[k][v]) & 0xffff0000u);
                     else
-                        ent[slot[k][v]] = make_uint2(f, __float_as_uint(dv[k][v]));
+                        x = make_uint2(f, __float_as_uint(dv[k][v]));
+                    if constexpr (kStage)
+                        stage[slot[k][v]] = x;   // slots are below F <= kRowPairs
+                    else
+                        ent[slot[k][v]] = x;
                 }
             }
         wave_lds_fence();
+        if constexpr (kStage) {
+            for (int sl = win_lo + lane; sl < total; sl += kWave) ent[sl] = stage[sl];
+            wave_lds_fence();
+        }
     }
 }
 
