@@ -54,8 +54,9 @@ def test_gt_parity(dt, H, D, chunk):
 
 
 @pytest.mark.parametrize("chunk", [0, 5])
-@pytest.mark.parametrize("dt,H,D", [("f32", 2, 64), ("f32", 4, 32), ("bf16", 2, 64),
-                                    ("bf16", 4, 128), ("bf16", 8, 64), ("bf16", 3, 32)])
+@pytest.mark.parametrize("dt,H,D", [("f32", 2, 64), ("f32", 4, 32), ("f32", 1, 128), ("bf16", 2, 64),
+                                    ("bf16", 4, 128), ("bf16", 8, 64), ("bf16", 3, 32),
+                                    ("bf16", 1, 128), ("bf16", 16, 64)])
 def test_gat_parity(dt, H, D, chunk):
     note(f"gat parity dt={dt} H={H} D={D} chunk={chunk}")
     rp, ci = graph(200 + H + D)
