@@ -259,7 +259,7 @@ def cpu_baseline(w, seconds: float):
         e, t = run(r)
     reps = 1
     if r == n and t < seconds / 2:          # the whole workload is quick: repeat it
-        reps = int(np.ceil(seconds / 2 / max(t, 1e-9)))
+        reps = int(np.ceil(seconds / max(t, 1e-9)))
         t = sum(run(r)[1] for _ in range(reps))
     rate = reps * e * spec.heads / t / 1e9
     return {"value": rate, "unit": "GEdge\u00b7head/s", "cores": oracle.num_threads(),
