@@ -1,0 +1,50 @@
+"""bench.py's output contract: one JSON line with the metric, the whole-step
+throughput, the roofline of the dominant kernel and the CPU baseline, run in
+a child process on the small Erdos-Renyi workload (fp32, 1,000 nodes)."""
+import json
+import os
+import subprocess
+import sys
+
+import pytest
+
+from tests.gpu_util import note
+
+pytestmark = pytest.mark.gpu
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_bench_json_line():
+    note("bench.py on gt_er1k_h4d32_f32")
+    r = subprocess.run([sys.executable, "bench.py", "--workload", "gt_er1k_h4d32_f32",
+                        "--steps", "3", "--warmup", "1", "--cpu-seconds", "1"],
+                       cwd=ROOT, capture_output=True, text=True, timeout=240)
+    assert r.returncode == 0, r.stderr[-2000:]
+    lines = [l for l in r.stdout.splitlines() if l.startswith("{")]
+    assert len(lines) == 1, r.stdout[-2000:]
+    d = json.loads(lines[0])
+    for k in ("metric", "value", "unit", "n_gpus", "steps", "warmup", "ms_per_step",
+              "higher_is_better", "scaling", "vs_baseline", "dtype", "data", "config",
+              "roofline", "cpu_baseline"):
+        assert k in d, k
+    assert d["n_gpus"] == 1 and d["steps"] == 3 and d["warmup"] == 1
+    assert d["higher_is_better"] is True and d["value"] > 0 and d["ms_per_step"] > 0
+    assert d["config"]["workload"] == "gt_er1k_h4d32_f32"
+    # value is E * H per step time
+    c = d["config"]
+    assert abs(d["value"] - c["edges"] * c["heads"] / (d["ms_per_step"] * 1e-3) / 1e9) \
+        <= 1e-3 * d["value"] + 1e-4
+    roof = d["roofline"]
+    for k in ("bound", "achieved", "peak", "unit", "frac", "traffic"):
+        assert k in roof, k
+    assert roof["bound"] == "hbm" and roof["unit"] == "GB/s" and roof["peak"] == 8000.0
+    assert abs(roof["frac"] - roof["achieved"] / roof["peak"]) < 1e-3
+    cb = d["cpu_baseline"]
+    assert cb["kind"] == "oracle" and cb["value"] > 0 and cb["cores"] >= 1 and cb["sample"]
+
+
+def test_bench_refuses_several_gpus():
+    r = subprocess.run([sys.executable, "bench.py", "--gpus", "2"], cwd=ROOT,
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode != 0 and "one GPU" in r.stderr
