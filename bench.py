@@ -145,7 +145,9 @@ def algorithmic_bytes(kernel: str, n: int, e: int, H: int, D: int, b: int,
     The GATv2 CSR backward pass runs as two kernels when a wavefront holds
     several edges (long items, then short items several to a wave): each
     is charged its own edges and items (an item reads and writes its
-    destination's row data like a node)."""
+    destination's row data like a node). The per-workgroup da partials of
+    the GATv2 backward (H*D*4 bytes each, under 1% of either pass) are not
+    counted."""
     R = H * D * b
     if kernel in ("gat_bwd_rows", "gat_bwd_rows_short") and split is not None:
         which = "short" if kernel.endswith("_short") else "long"
@@ -182,8 +184,9 @@ def algorithmic_bytes(kernel: str, n: int, e: int, H: int, D: int, b: int,
         # Xt_j, colidx read and the edge record written per edge; Xs_i, dO_i,
         # O_i, lse_i read, dXs_i written
         "gat_bwd_rows": (R + 4 + gat_record_bytes(H, D, b), 4 * R + 4 * H + 8),
-        # dO_i, rowidx, edge id and the edge record per edge; dXt_j written
-        "gat_bwd_cols": (R + 8 + gat_record_bytes(H, D, b), R + 8),
+        # dO_i, rowidx, edge id and the edge record per edge; Xt_j read (for
+        # its da term) and dXt_j written per node
+        "gat_bwd_cols": (R + 8 + gat_record_bytes(H, D, b), 2 * R + 8),
         # min/max aggregation (H = 1, D = F): X_j and colidx per edge; out_i and
         # the int32 winners arg_i written per node
         "reduce_fwd_rows": (R + 4, R + 4 * D),

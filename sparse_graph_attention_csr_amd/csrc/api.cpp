@@ -139,7 +139,7 @@ Layout ws_layout(const Plan& p, int op, int H, int D, int dt)
         sz[2] = static_cast<size_t>(p.col_slots) * HD * 4;          // dXt partials
         {
             const GatRowGrid gx = gat_bwd_row_grid(p, dt, D, H);
-            sz[4] = static_cast<size_t>(gx.single + gx.shorts) * HD * 4;   // da partials
+            sz[4] = static_cast<size_t>(gat_da_part_rows(gx)) * HD * 4;   // da partials
         }
         break;
     case SGAT_OP_REDUCE_FWD:                                        // H = 1, D = F

@@ -655,39 +655,70 @@ __device__ __forceinline__ GatRowState<Elem<DT>::VEC> gat_row_state(const GatBwd
     return r;
 }
 
+// da without a per-edge term. a LeakyReLU(z) = a (z s) with s = 1 for z > 0
+// and the slope otherwise, and z_ij = Xs_i + Xt_j, so
+//   da = sum_ij dE_ij LeakyReLU(z_ij) = sum_i Xs_i . T_i + sum_j Xt_j . U_j
+// with T_i = sum_j dE_ij s_ij (the CSR pass; dXs_i = a . T_i) and U_j =
+// sum_i dE_ij s_ij (the transposed pass; its share of dXt_j is a . U_j), all
+// per channel. Each pass adds its per-row terms, once per item, into per-lane
+// LDS slots, and sums them per workgroup at its end in fixed order (waves,
+// then edge groups).
+template <int VEC>
+__device__ __forceinline__ void da_add(float* slot, const float (&x)[VEC], const float (&t)[VEC])
+{
+#pragma unroll
+    for (int k = 0; k < VEC; ++k) slot[k] = fmaf(x[k], t[k], slot[k]);
+}
+
+template <int VEC, int LPE, int HG, int D>
+__device__ __forceinline__ void da_block_partial(const float (*dal)[kWave * VEC], int hg, int H,
+                                                 float* da_part_block)
+{
+    constexpr int W = LPE * VEC;        // HG heads * D channels
+    constexpr int EPW = kWave / LPE;
+    __syncthreads();
+    for (int t = threadIdx.x; t < W; t += kBlock) {
+        const int head = hg * HG + t / D;
+        if (head >= H) continue;
+        float s = 0.f;
+#pragma unroll
+        for (int w = 0; w < kWavesPerBlock; ++w)
+#pragma unroll
+            for (int q = 0; q < EPW; ++q) s += dal[w][q * W + t];   // lane q*LPE + t/VEC
+        da_part_block[head * D + (t % D)] = s;
+    }
+}
+
 // One edge (i, j) for the lane's channels: p = exp(e_ij - lse_i), dE =
-// p (dO_i . Xt_j - Delta_i); adds dE g to dXs and dE LeakyReLU(z) to da, and
-// stages (p, dE) and the signs of z in the edge's LDS record. g_d =
-// a_d LeakyReLU'(z_d) is a_d for z_d > 0, a_d * slope otherwise, and
-// a_d LeakyReLU(z_d) = z_d g_d.
+// p (dO_i . Xt_j - Delta_i); adds dE s to T (s = 1 for z > 0, the slope
+// otherwise; dXs = a . T) and stages (p, dE) and the signs of z in the edge's
+// LDS record. The score uses a LeakyReLU(z) = z g, g = a s.
 template <int DT, int D, int EPW>
 __device__ __forceinline__ void gat_bwd_edge(const Geo<DT, D, EPW>& g, const Frag& xf, bool ok,
                                              const GatRowState<Elem<DT>::VEC>& r,
                                              const float (&at)[Elem<DT>::VEC],
                                              const float (&as)[Elem<DT>::VEC], float slope,
-                                             float (&dxs)[Elem<DT>::VEC],
-                                             float (&da)[Elem<DT>::VEC], uint32_t* lr)
+                                             float (&tsum)[Elem<DT>::VEC], uint32_t* lr)
 {
     using G = Geo<DT, D, EPW>;
     constexpr int VEC = G::VEC;
-    float x[VEC], z[VEC], gz[VEC];
+    float x[VEC], z[VEC];
     to_f32<DT>(xf, x);
     float part = 0.f;
 #pragma unroll
     for (int k = 0; k < VEC; ++k) {
         z[k] = r.xs[k] + x[k];
-        gz[k] = z[k] > 0.f ? at[k] : as[k];
-        part = fmaf(z[k], gz[k], part);
+        part = fmaf(z[k], z[k] > 0.f ? at[k] : as[k], part);
     }
     const float e2 = head_sum<G::SPH>(part) * kLog2e;
     const float dp = head_sum<G::SPH>(dot<DT>(r.dof, xf));
     const float p = ok ? fast_exp2(e2 - r.lse2) : 0.f;
     const float dE = p * (dp - r.delta);
+    const float dEs = dE * slope;
     uint32_t zbits = 0;
 #pragma unroll
     for (int k = 0; k < VEC; ++k) {
-        dxs[k] = fmaf(dE, gz[k], dxs[k]);
-        da[k] = fmaf(dE, z[k] > 0.f ? z[k] : slope * z[k], da[k]);
+        tsum[k] += z[k] > 0.f ? dE : dEs;
         zbits |= (z[k] > 0.f ? 1u : 0u) << k;
     }
     reinterpret_cast<uint8_t*>(lr + 2 * G::HG)[g.pos] = static_cast<uint8_t>(zbits);
@@ -701,12 +732,12 @@ __device__ __forceinline__ void gat_bwd_edge(const Geo<DT, D, EPW>& g, const Fra
 // SHORT = false: the items [0, n_single), one wave each; SHORT = true: the
 // items [n_single, n_items), EPW to a wave. Each launch writes one da
 // partial per workgroup into its own da_part.
-// Waves per SIMD asked of the short-item instance: 5 for the bf16 layouts
-// whose short path fits 96 VGPRs without spilling (D = 64, and D = 128 with 4
+// Waves per SIMD asked of the short-item instance: 6 for the bf16 layouts
+// whose short path fits 80 VGPRs without spilling (D = 64, and D = 128 with 4
 // edge groups); the others keep the compiler's choice.
 constexpr int gat_short_rows_waves(int dt, int D, int epw)
 {
-    return dt == SGAT_BF16 && (D == 64 || (D == 128 && epw == 4)) ? 5 : 1;
+    return dt == SGAT_BF16 && (D == 64 || (D == 128 && epw == 4)) ? 6 : 1;
 }
 
 template <int DT, int D, int EPW, int U, int UMAX, bool SHORT>
@@ -718,7 +749,7 @@ void gat_bwd_rows(GatBwdRowArgs a)
     constexpr int VEC = G::VEC;
     constexpr int RS = gat_rec_dwords(G::HG, G::LPE);
     constexpr int UM = UMAX < G::LPE ? UMAX : G::LPE;   // per-group step of the short items
-    __shared__ float red[kWavesPerBlock][G::LPE * VEC];
+    __shared__ float dal[kWavesPerBlock][kWave * VEC];  // per-lane da sums
     // records of one block of edges (64 for a single item, LPE per group for
     // short items), written out contiguously once per block: per-edge global
     // stores inside the loop would make each wait for the next loads also
@@ -729,12 +760,14 @@ void gat_bwd_rows(GatBwdRowArgs a)
     const int64_t HD = static_cast<int64_t>(a.H) * D;
     const int wid = wave_id();
     uint32_t* const lrec = recbuf[wid];
+    float* const myda = &dal[wid][g.lane * VEC];
+#pragma unroll
+    for (int k = 0; k < VEC; ++k) myda[k] = 0.f;
 
     float at[VEC] = {}, as[VEC];
     if (g.hvalid) ld_f32<VEC>(a.att + g.col, at);
 #pragma unroll
     for (int k = 0; k < VEC; ++k) as[k] = at[k] * a.slope;
-    float da[VEC] = {};
 
     const int64_t n_wunits = SHORT ? (a.n_items - a.n_single + EPW - 1) / EPW : a.n_single;
     const int64_t stride = static_cast<int64_t>(gridDim.x) * kWavesPerBlock;
@@ -744,7 +777,7 @@ void gat_bwd_rows(GatBwdRowArgs a)
             // one item for the whole wave, EPW edges side by side
             const sgat_work_item it = a.items[wi];
             const GatRowState<VEC> r = gat_row_state<DT, D, EPW>(a, g, it, true);
-            float dxs[VEC] = {};
+            float ts[VEC] = {};
             const int32_t* ci = a.colidx + it.begin;
             uint32_t* rec = a.edge_rec + (static_cast<int64_t>(hg) * a.nnz + it.begin) * RS;
             for (int base = 0; base < it.len; base += kWave) {
@@ -763,7 +796,7 @@ void gat_bwd_rows(GatBwdRowArgs a)
                     }
 #pragma unroll
                     for (int u = 0; u < U; ++u)   // t + u*EPW + sub < 64: EPW*U divides 64
-                        gat_bwd_edge<DT, D, EPW>(g, xf[u], ok[u], r, at, as, a.slope, dxs, da,
+                        gat_bwd_edge<DT, D, EPW>(g, xf[u], ok[u], r, at, as, a.slope, ts,
                                                  lrec + (t + u * EPW + g.sub) * RS);
                 }
                 wave_lds_fence();
@@ -774,8 +807,14 @@ void gat_bwd_rows(GatBwdRowArgs a)
                 }
                 wave_lds_fence();
             }
-            if constexpr (EPW > 1) sum_groups<VEC, G::LPE>(dxs);
-            if (g.sub == 0 && g.hvalid) grad_store<DT, VEC>(dxs, 1.f, it, HD, g.col, a.dXs, a.part);
+            if constexpr (EPW > 1) sum_groups<VEC, G::LPE>(ts);
+            if (g.sub == 0 && g.hvalid) {
+                float dxs[VEC];
+#pragma unroll
+                for (int k = 0; k < VEC; ++k) dxs[k] = at[k] * ts[k];
+                grad_store<DT, VEC>(dxs, 1.f, it, HD, g.col, a.dXs, a.part);
+                da_add<VEC>(myda, r.xs, ts);
+            }
         } else {
             // EPW short items, one per edge group; all lanes of a group share
             // its trip counts, so the in-group shuffles read active lanes only
@@ -785,7 +824,7 @@ void gat_bwd_rows(GatBwdRowArgs a)
             sgat_work_item it{0, 0, 0, -1, 0};
             if (has) it = a.items[idx];
             const GatRowState<VEC> r = gat_row_state<DT, D, EPW>(a, g, it, has);
-            float dxs[VEC] = {};
+            float ts[VEC] = {};
             const int32_t* ci = a.colidx + it.begin;
             uint32_t* rec = a.edge_rec + (static_cast<int64_t>(hg) * a.nnz + it.begin) * RS;
             uint32_t* const grec = lrec + g.sub * G::LPE * RS;   // the group's LPE records
@@ -805,7 +844,7 @@ void gat_bwd_rows(GatBwdRowArgs a)
                     }
 #pragma unroll
                     for (int u = 0; u < UM; ++u)   // t + u < LPE: UM divides LPE
-                        gat_bwd_edge<DT, D, EPW>(g, xf[u], ok[u], r, at, as, a.slope, dxs, da,
+                        gat_bwd_edge<DT, D, EPW>(g, xf[u], ok[u], r, at, as, a.slope, ts,
                                                  grec + (t + u) * RS);
                 }
                 wave_lds_fence();
@@ -816,25 +855,17 @@ void gat_bwd_rows(GatBwdRowArgs a)
                 }
                 wave_lds_fence();
             }
-            if (has && g.hvalid) grad_store<DT, VEC>(dxs, 1.f, it, HD, g.col, a.dXs, a.part);
+            if (has && g.hvalid) {
+                float dxs[VEC];
+#pragma unroll
+                for (int k = 0; k < VEC; ++k) dxs[k] = at[k] * ts[k];
+                grad_store<DT, VEC>(dxs, 1.f, it, HD, g.col, a.dXs, a.part);
+                da_add<VEC>(myda, r.xs, ts);
+            }
         }
     }
-    // da: edge groups, then the waves of the block, in fixed order
-    if constexpr (EPW > 1) sum_groups<VEC, G::LPE>(da);
-    if (g.sub == 0) {
-#pragma unroll
-        for (int k = 0; k < VEC; ++k) red[wid][g.pos * VEC + k] = da[k];
-    }
-    __syncthreads();
-    constexpr int W = G::LPE * VEC;   // HG heads * D channels
-    for (int t = threadIdx.x; t < W; t += kBlock) {
-        const int head = hg * G::HG + t / D;
-        if (head >= a.H) continue;
-        float s = 0.f;
-#pragma unroll
-        for (int w = 0; w < kWavesPerBlock; ++w) s += red[w][t];
-        a.da_part[static_cast<int64_t>(blockIdx.x) * HD + head * D + (t % D)] = s;
-    }
+    da_block_partial<VEC, G::LPE, G::HG, D>(dal, hg, a.H,
+                                            a.da_part + static_cast<int64_t>(blockIdx.x) * HD);
 }
 
 struct DaReduceArgs {
@@ -936,131 +967,160 @@ __global__ __launch_bounds__(kBlock) void gt_bwd_cols(GtBwdColArgs a)
 
 struct GatBwdColArgs {
     const sgat_work_item* items;
-    int64_t n_units;
     int64_t n_items, n_single;   // items [n_single, n_items) come EPW to a wave
-    int n_hg, H;
+    int H;
     const int32_t* rowidx;
     const int32_t* col_edge;    // CSR edge id of each transposed entry
-    const void* dO;
+    const void *Xt, *dO;        // Xt: the sources' own rows, for their da terms
     const float* att;
     float slope;
     const uint32_t* edge_rec;   // written by the CSR pass
     int64_t nnz;
     void* dXt;
     float* part;
+    float* da_part;             // [gridDim.x][H*D]
 };
 
-// dXt_j += p_ij dO_i + dE_ij g_ij for U edges (ok[u] == false: no edge), g =
-// a LeakyReLU'(z_ij) from the sign bits of the edge record.
+// Adds U edges (ok == false: no edge) to pacc += p dO_i and uacc += dE s,
+// s from the sign bits of the edge record (1 for z > 0, the slope otherwise).
 template <int DT, int VEC, int U>
-__device__ __forceinline__ void gat_col_step(float (&dxt)[VEC], const Frag (&df)[U],
-                                             const float2 (&pd)[U], const uint32_t (&zb)[U],
-                                             const float (&at)[VEC], const float (&as)[VEC])
+__device__ __forceinline__ void gat_col_step(float (&pacc)[VEC], float (&uacc)[VEC],
+                                             const Frag (&df)[U], const float2 (&pd)[U],
+                                             const uint32_t (&zb)[U], float slope)
 {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         float dx[VEC];
         to_f32<DT>(df[u], dx);
+        const float dEs = pd[u].y * slope;
 #pragma unroll
         for (int k = 0; k < VEC; ++k) {
-            const float gz = (zb[u] >> k) & 1u ? at[k] : as[k];
-            dxt[k] = fmaf(pd[u].x, dx[k], fmaf(pd[u].y, gz, dxt[k]));
+            pacc[k] = fmaf(pd[u].x, dx[k], pacc[k]);
+            uacc[k] += (zb[u] >> k) & 1u ? pd[u].y : dEs;
         }
     }
 }
 
-// dXt_j = sum over i of p_ij dO_i + dE_ij g_ij, g = a LeakyReLU'(z_ij): the
-// per-edge p, dE and signs of z come from the CSR pass; only dO_i is gathered.
+// dXt_j = sum over i of p_ij dO_i + a . U_j (U_j = sum_i dE_ij s_ij): the
+// per-edge p, dE and signs of z come from the CSR pass; only dO_i is
+// gathered. Grid-stride over the items with a fixed grid (blockIdx.y = head
+// group), so the da partials are one per workgroup.
 template <int DT, int D, int EPW, int U, int UM>
 __global__ __launch_bounds__(kBlock) void gat_bwd_cols(GatBwdColArgs a)
 {
     using G = Geo<DT, D, EPW>;
     constexpr int VEC = G::VEC;
-    const int64_t unit = logical_block() * kWavesPerBlock + wave_id();
-    if (unit >= a.n_units) return;
-    const int64_t wi = unit / a.n_hg;
-    const int hg = static_cast<int>(unit - wi * a.n_hg);
+    __shared__ float dal[kWavesPerBlock][kWave * VEC];   // per-lane da sums
+    const int hg = blockIdx.y;
     const G g(hg, a.H);
     const int64_t HD = static_cast<int64_t>(a.H) * D;
+    const int wid = wave_id();
     constexpr int RS = gat_rec_dwords(G::HG, G::LPE);
     const uint32_t* const rbase = a.edge_rec + static_cast<int64_t>(hg) * a.nnz * RS;
     const int hl = g.pos / G::SPH;
     const int zl = 2 * G::HG + g.pos / 4, zsh = 8 * (g.pos % 4);   // the lane's sign byte
+    float* const myda = &dal[wid][g.lane * VEC];
+#pragma unroll
+    for (int k = 0; k < VEC; ++k) myda[k] = 0.f;
 
-    float at[VEC] = {}, as[VEC];
-    if (g.hvalid) ld_f32<VEC>(a.att + g.col, at);
+    const int64_t n_wunits =
+        EPW == 1 ? a.n_items : a.n_single + (a.n_items - a.n_single + EPW - 1) / EPW;
+    // logical_block() keeps runs of consecutive units on one XCD (the grid is
+    // a multiple of the remap's quantum)
+    const int64_t stride = static_cast<int64_t>(gridDim.x) * kWavesPerBlock;
+    for (int64_t wi = logical_block() * kWavesPerBlock + wid; wi < n_wunits; wi += stride) {
+        float pacc[VEC] = {}, uacc[VEC] = {};
+        if (EPW == 1 || wi < a.n_single) {
+            const sgat_work_item it = a.items[wi];
+            const int32_t* ri = a.rowidx + it.begin;
+            const int32_t* re = a.col_edge + it.begin;
+            for (int base = 0; base < it.len; base += kWave) {
+                const int nb = min(kWave, it.len - base);
+                const int ci = g.lane < nb ? ri[base + g.lane] : 0;
+                const int ce = g.lane < nb ? re[base + g.lane] : 0;
+                for (int t = 0; t < nb; t += EPW * U) {
+                    Frag df[U];
+                    float2 pd[U];
+                    uint32_t zb[U];
 #pragma unroll
-    for (int k = 0; k < VEC; ++k) as[k] = at[k] * a.slope;
-    float dxt[VEC] = {};
-    if (EPW == 1 || wi < a.n_single) {
-        const sgat_work_item it = a.items[wi];
-        const int32_t* ri = a.rowidx + it.begin;
-        const int32_t* re = a.col_edge + it.begin;
-        for (int base = 0; base < it.len; base += kWave) {
-            const int nb = min(kWave, it.len - base);
-            const int ci = g.lane < nb ? ri[base + g.lane] : 0;
-            const int ce = g.lane < nb ? re[base + g.lane] : 0;
-            for (int t = 0; t < nb; t += EPW * U) {
-                Frag df[U];
-                float2 pd[U];
-                uint32_t zb[U];
-#pragma unroll
-                for (int u = 0; u < U; ++u) {
-                    const int e = t + u * EPW + g.sub;
-                    const int64_t i = bcast<EPW>(ci, e);
-                    const int64_t eid = bcast<EPW>(ce, e);
-                    df[u] = frag_zero();
-                    pd[u] = make_float2(0.f, 0.f);
-                    zb[u] = 0;
-                    if (e < nb && g.hvalid) {
-                        const uint32_t* r = rbase + eid * RS;
-                        df[u] = ldg<DT>(a.dO, i * HD + g.col);
-                        pd[u] = *reinterpret_cast<const float2*>(r + 2 * hl);
-                        zb[u] = r[zl] >> zsh;
+                    for (int u = 0; u < U; ++u) {
+                        const int e = t + u * EPW + g.sub;
+                        const int64_t i = bcast<EPW>(ci, e);
+                        const int64_t eid = bcast<EPW>(ce, e);
+                        df[u] = frag_zero();
+                        pd[u] = make_float2(0.f, 0.f);
+                        zb[u] = 0;
+                        if (e < nb && g.hvalid) {
+                            const uint32_t* r = rbase + eid * RS;
+                            df[u] = ldg<DT>(a.dO, i * HD + g.col);
+                            pd[u] = *reinterpret_cast<const float2*>(r + 2 * hl);
+                            zb[u] = r[zl] >> zsh;
+                        }
                     }
+                    gat_col_step<DT, VEC, U>(pacc, uacc, df, pd, zb, a.slope);
                 }
-                gat_col_step<DT, VEC, U>(dxt, df, pd, zb, at, as);
+            }
+            if constexpr (EPW > 1) {
+                sum_groups<VEC, G::LPE>(pacc);
+                sum_groups<VEC, G::LPE>(uacc);
+            }
+            if (g.sub == 0 && g.hvalid) {
+                float dxt[VEC], xt[VEC], at[VEC];
+                ld_f32<VEC>(a.att + g.col, at);   // a is read per item, not held
+#pragma unroll
+                for (int k = 0; k < VEC; ++k) dxt[k] = fmaf(at[k], uacc[k], pacc[k]);
+                grad_store<DT, VEC>(dxt, 1.f, it, HD, g.col, a.dXt, a.part);
+                to_f32<DT>(ldg<DT>(a.Xt, static_cast<int64_t>(it.row) * HD + g.col), xt);
+                da_add<VEC>(myda, xt, uacc);
+            }
+        } else if constexpr (EPW > 1) {
+            // EPW short items, one per edge group (in-group shuffles only)
+            constexpr int V = UM < G::LPE ? UM : G::LPE;
+            const int64_t idx = a.n_single + (wi - a.n_single) * EPW + g.sub;
+            const bool has = idx < a.n_items;
+            sgat_work_item it{0, 0, 0, -1, 0};
+            if (has) it = a.items[idx];
+            const int32_t* ri = a.rowidx + it.begin;
+            const int32_t* re = a.col_edge + it.begin;
+            const int lead = g.sub * G::LPE;
+            for (int base = 0; base < it.len; base += G::LPE) {
+                const int nb = min(G::LPE, it.len - base);
+                const int ci = g.pos < nb ? ri[base + g.pos] : 0;
+                const int ce = g.pos < nb ? re[base + g.pos] : 0;
+                for (int t = 0; t < nb; t += V) {
+                    Frag df[V];
+                    float2 pd[V];
+                    uint32_t zb[V];
+#pragma unroll
+                    for (int u = 0; u < V; ++u) {
+                        const int64_t i = __shfl(ci, lead + t + u);
+                        const int64_t eid = __shfl(ce, lead + t + u);
+                        df[u] = frag_zero();
+                        pd[u] = make_float2(0.f, 0.f);
+                        zb[u] = 0;
+                        if (t + u < nb && g.hvalid) {
+                            const uint32_t* r = rbase + eid * RS;
+                            df[u] = ldg<DT>(a.dO, i * HD + g.col);
+                            pd[u] = *reinterpret_cast<const float2*>(r + 2 * hl);
+                            zb[u] = r[zl] >> zsh;
+                        }
+                    }
+                    gat_col_step<DT, VEC, V>(pacc, uacc, df, pd, zb, a.slope);
+                }
+            }
+            if (has && g.hvalid) {
+                float dxt[VEC], xt[VEC], at[VEC];
+                ld_f32<VEC>(a.att + g.col, at);   // a is read per item, not held
+#pragma unroll
+                for (int k = 0; k < VEC; ++k) dxt[k] = fmaf(at[k], uacc[k], pacc[k]);
+                grad_store<DT, VEC>(dxt, 1.f, it, HD, g.col, a.dXt, a.part);
+                to_f32<DT>(ldg<DT>(a.Xt, static_cast<int64_t>(it.row) * HD + g.col), xt);
+                da_add<VEC>(myda, xt, uacc);
             }
         }
-        if constexpr (EPW > 1) sum_groups<VEC, G::LPE>(dxt);
-        if (g.sub == 0 && g.hvalid) grad_store<DT, VEC>(dxt, 1.f, it, HD, g.col, a.dXt, a.part);
-    } else if constexpr (EPW > 1) {
-        // EPW short items, one per edge group (in-group shuffles only)
-        constexpr int V = UM < G::LPE ? UM : G::LPE;
-        const int64_t idx = a.n_single + (wi - a.n_single) * EPW + g.sub;
-        const bool has = idx < a.n_items;
-        sgat_work_item it{0, 0, 0, -1, 0};
-        if (has) it = a.items[idx];
-        const int32_t* ri = a.rowidx + it.begin;
-        const int32_t* re = a.col_edge + it.begin;
-        const int lead = g.sub * G::LPE;
-        for (int base = 0; base < it.len; base += G::LPE) {
-            const int nb = min(G::LPE, it.len - base);
-            const int ci = g.pos < nb ? ri[base + g.pos] : 0;
-            const int ce = g.pos < nb ? re[base + g.pos] : 0;
-            for (int t = 0; t < nb; t += V) {
-                Frag df[V];
-                float2 pd[V];
-                uint32_t zb[V];
-#pragma unroll
-                for (int u = 0; u < V; ++u) {
-                    const int64_t i = __shfl(ci, lead + t + u);
-                    const int64_t eid = __shfl(ce, lead + t + u);
-                    df[u] = frag_zero();
-                    pd[u] = make_float2(0.f, 0.f);
-                    zb[u] = 0;
-                    if (t + u < nb && g.hvalid) {
-                        const uint32_t* r = rbase + eid * RS;
-                        df[u] = ldg<DT>(a.dO, i * HD + g.col);
-                        pd[u] = *reinterpret_cast<const float2*>(r + 2 * hl);
-                        zb[u] = r[zl] >> zsh;
-                    }
-                }
-                gat_col_step<DT, VEC, V>(dxt, df, pd, zb, at, as);
-            }
-        }
-        if (has && g.hvalid) grad_store<DT, VEC>(dxt, 1.f, it, HD, g.col, a.dXt, a.part);
     }
+    da_block_partial<VEC, G::LPE, G::HG, D>(dal, hg, a.H,
+                                            a.da_part + static_cast<int64_t>(blockIdx.x) * HD);
 }
 
 }  // namespace sgat

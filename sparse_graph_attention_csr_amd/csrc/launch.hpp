@@ -18,12 +18,15 @@ struct Decomp {
 };
 Decomp decompose(int dt, int D, int H);
 
-// Grids of the GATv2 CSR backward pass: the long items one per wave, the
-// short ones several per wave (its da partials are one per workgroup of both).
+// Grids of the GATv2 backward: the CSR pass's long items one per wave, its
+// short ones several per wave, and the transposed pass (a multiple of the XCD
+// remap quantum); da partials are one per workgroup of all three.
 struct GatRowGrid {
-    int single, shorts;
+    int single, shorts, cols;
 };
 GatRowGrid gat_bwd_row_grid(const Plan& p, int dt, int D, int H);
+// rows of H*D floats the da partials (and their reduction) take in the workspace
+int64_t gat_da_part_rows(const GatRowGrid& g);
 
 struct FwdWs {
     float* part_acc;   // [row_slots][H*D]
@@ -34,7 +37,7 @@ struct BwdWs {
     float* part_row;   // [row_slots][H*D]
     float* part_col0;  // [col_slots][H*D]
     float* part_col1;  // [col_slots][H*D] (GT only)
-    float* da_part;    // [single + shorts workgroups][H*D] (GATv2 only)
+    float* da_part;    // [single + shorts + cols workgroups][H*D] (GATv2 only)
     float* ds;         // [nnz][H] dS per edge (Graph Transformer only)
     void* edge_rec;    // [nnz][gat_edge_record_dwords] (GATv2 only)
 };

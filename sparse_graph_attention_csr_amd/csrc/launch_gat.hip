@@ -30,6 +30,11 @@ namespace sgat {
 #ifndef SGAT_UNROLL_MULTI_BWD
 #define SGAT_UNROLL_MULTI_BWD 1
 #endif
+// one source row per step and edge group in the transposed pass: with its
+// per-node da terms a second one costs occupancy
+#ifndef SGAT_UNROLL_COLS
+#define SGAT_UNROLL_COLS 1
+#endif
 #ifndef SGAT_UNROLL_MULTI_COLS
 #define SGAT_UNROLL_MULTI_COLS 1
 #endif
@@ -40,7 +45,34 @@ namespace {
 // registers.
 constexpr int unroll_fwd(int epw) { return epw >= 4 ? (SGAT_UNROLL_FWD + 3) / 4 : SGAT_UNROLL_FWD; }
 constexpr int unroll_bwd(int epw) { return epw >= 4 ? (SGAT_UNROLL_BWD + 1) / 2 : SGAT_UNROLL_BWD; }
-constexpr int kGatBwdMaxBlocks = 4096;
+// The backward passes take one work unit per wave up to this grid and
+// stride beyond it; every workgroup writes one row of da partials.
+constexpr int kGatBwdMaxBlocks = 1 << 20;
+// da partials summed per run of this many by the first reduction level
+constexpr int kDaRun = 64;
+// above this many partials the reduction takes two levels
+constexpr int kDaOneLevel = 1024;
+}
+
+int64_t gat_da_part_rows(const GatRowGrid& g)
+{
+    const int64_t n = static_cast<int64_t>(g.single) + g.shorts + g.cols;
+    return n > kDaOneLevel ? n + (n + kDaRun - 1) / kDaRun : n;
+}
+
+// First level of the da reduction when there are many partials: workgroup b
+// sums partials [b*kDaRun, (b+1)*kDaRun) in order, one thread per element.
+__global__ __launch_bounds__(kBlock) void da_reduce_runs(DaReduceArgs a)
+{
+    const int64_t b0 = static_cast<int64_t>(blockIdx.x) * kDaRun;
+    const int nb = static_cast<int>(std::min<int64_t>(kDaRun, a.G - b0));
+    for (int e = threadIdx.x; e < a.HD; e += kBlock) {
+        const float* src = a.da_part + b0 * a.HD + e;
+        float s = 0.f;
+#pragma unroll 8
+        for (int r = 0; r < nb; ++r) s += src[static_cast<int64_t>(r) * a.HD];
+        a.da[static_cast<int64_t>(blockIdx.x) * a.HD + e] = s;
+    }
 }
 
 // Fixed-order sum of the per-workgroup da partials: one workgroup per element
@@ -67,12 +99,16 @@ GatRowGrid gat_bwd_row_grid(const Plan& p, int dt, int D, int H)
     const int64_t n_items = static_cast<int64_t>(p.row_items.size());
     const int64_t n_single = dc.epw > 1 ? p.row_short_from[SGAT_SHORT_LOG2] : n_items;
     const int64_t short_units = (n_items - n_single + dc.epw - 1) / dc.epw;
+    const int64_t c_items = static_cast<int64_t>(p.col_items.size());
+    const int64_t c_single = dc.epw > 1 ? p.col_short_from[SGAT_SHORT_LOG2] : c_items;
+    const int64_t c_units = c_single + (c_items - c_single + dc.epw - 1) / dc.epw;
     auto blocks = [](int64_t waves) {
         const int64_t need = (waves + kWavesPerBlock - 1) / kWavesPerBlock;
         return static_cast<int>(std::min<int64_t>(need, kGatBwdMaxBlocks));
     };
-    GatRowGrid g{blocks(n_single), blocks(short_units)};
-    if (g.single + g.shorts == 0) g.single = 1;   // da is still written (as zeros)
+    GatRowGrid g{blocks(n_single), blocks(short_units),
+                 static_cast<int>(std::min<int64_t>(wave_grid(c_units), kGatBwdMaxBlocks))};
+    if (g.cols == 0) g.cols = kGridQuantum;   // da is still written (as zeros)
     return g;
 }
 
@@ -163,11 +199,10 @@ int launch_gat_bwd(const Plan& p, int H, int D, int dt, const int32_t* colidx, c
     c.items = p.dptr<sgat_work_item>(SGAT_ARR_COL_ITEMS);
     c.n_items = static_cast<int64_t>(p.col_items.size());
     c.n_single = dc.epw > 1 ? p.col_short_from[SGAT_SHORT_LOG2] : c.n_items;
-    c.n_units = (c.n_single + (c.n_items - c.n_single + dc.epw - 1) / dc.epw) * dc.n_hg;
-    c.n_hg = dc.n_hg;
     c.H = H;
     c.rowidx = p.dptr<int32_t>(SGAT_ARR_ROWIDX);
     c.col_edge = p.dptr<int32_t>(SGAT_ARR_COL_EDGE);
+    c.Xt = Xt;
     c.dO = dO;
     c.att = att;
     c.slope = slope;
@@ -175,6 +210,7 @@ int launch_gat_bwd(const Plan& p, int H, int D, int dt, const int32_t* colidx, c
     c.nnz = p.nnz;
     c.dXt = dXt;
     c.part = ws.part_col0;
+    c.da_part = ws.da_part + static_cast<int64_t>(gx.single + gx.shorts) * HD;
 
     const void *fr = nullptr, *frs = nullptr, *fc = nullptr;
 #define X(DT_, D_, E_)                                                                        \
@@ -185,7 +221,7 @@ int launch_gat_bwd(const Plan& p, int H, int D, int dt, const int32_t* colidx, c
             frs = reinterpret_cast<const void*>(                                              \
                 &gat_bwd_rows<DT_, D_, E_, unroll_bwd(E_), SGAT_UNROLL_MULTI_BWD, true>);     \
         fc = reinterpret_cast<const void*>(                                                   \
-            &gat_bwd_cols<DT_, D_, E_, unroll_bwd(E_), SGAT_UNROLL_MULTI_COLS>);              \
+            &gat_bwd_cols<DT_, D_, E_, SGAT_UNROLL_COLS, SGAT_UNROLL_MULTI_COLS>);            \
     }
     SGAT_GATHER_CONFIGS(X)
 #undef X
@@ -208,16 +244,27 @@ int launch_gat_bwd(const Plan& p, int H, int D, int dt, const int32_t* colidx, c
     if ((rc = merge_sum("gat_bwd_rows_merge", p.row_splits, p.dptr<sgat_split>(SGAT_ARR_ROW_SPLITS),
                         HD, ws.part_row, 1.f, dXs, nullptr, 0.f, nullptr, dt, s)))
         return rc;
-    DaReduceArgs d{ws.da_part, gx.single + gx.shorts, HD, da};
-    if ((rc = launch("gat_bwd_da_reduce", reinterpret_cast<const void*>(&da_reduce),
-                     dim3(static_cast<unsigned>(HD)), dim3(kBlock), &d, s)))
-        return rc;
-    if (c.n_units > 0 &&
-        (rc = launch("gat_bwd_cols", fc, dim3(static_cast<unsigned>(wave_grid(c.n_units))),
+    // every workgroup of the transposed pass writes its da partial too
+    if ((rc = launch("gat_bwd_cols", fc,
+                     dim3(static_cast<unsigned>(gx.cols), static_cast<unsigned>(dc.n_hg)),
                      dim3(kBlock), &c, s)))
         return rc;
-    return merge_sum("gat_bwd_cols_merge", p.col_splits, p.dptr<sgat_split>(SGAT_ARR_COL_SPLITS),
-                     HD, ws.part_col0, 1.f, dXt, nullptr, 0.f, nullptr, dt, s);
+    if ((rc = merge_sum("gat_bwd_cols_merge", p.col_splits, p.dptr<sgat_split>(SGAT_ARR_COL_SPLITS),
+                        HD, ws.part_col0, 1.f, dXt, nullptr, 0.f, nullptr, dt, s)))
+        return rc;
+    DaReduceArgs d{ws.da_part, gx.single + gx.shorts + gx.cols, HD, da};
+    if (d.G > kDaOneLevel) {
+        // runs of kDaRun partials first, into the rows after the partials
+        const int runs = (d.G + kDaRun - 1) / kDaRun;
+        float* lvl = ws.da_part + static_cast<int64_t>(d.G) * HD;
+        DaReduceArgs r{ws.da_part, d.G, HD, lvl};
+        if ((rc = launch("gat_bwd_da_reduce_runs", reinterpret_cast<const void*>(&da_reduce_runs),
+                         dim3(static_cast<unsigned>(runs)), dim3(kBlock), &r, s)))
+            return rc;
+        d = DaReduceArgs{lvl, runs, HD, da};
+    }
+    return launch("gat_bwd_da_reduce", reinterpret_cast<const void*>(&da_reduce),
+                  dim3(static_cast<unsigned>(HD)), dim3(kBlock), &d, s);
 }
 
 }  // namespace sgat
