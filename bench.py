@@ -266,9 +266,41 @@ def cpu_baseline(w, seconds: float):
         t = sum(run(r)[1] for _ in range(reps))
     rate = reps * e * spec.heads / t / 1e9
     return {"value": rate, "unit": "GEdge\u00b7head/s", "cores": oracle.num_threads(),
-            "kind": "oracle",
+            "cpu": cpu_model(), "kind": "oracle",
             "sample": f"destination rows 0..{r - 1} of {n} ({e} of {int(rp[-1])} edges), "
                       f"{spec.passes}, fp64, {reps} run(s), {t:.1f} s"}
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo", encoding="utf-8") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def per_step_ms(step, reps: int, flush=None) -> dict:
+    """Each step timed alone with events on the stream the library launches
+    on (torch's current stream); `flush`, if given, runs before each step,
+    outside its events. Median and minimum over the reps, in ms."""
+    import statistics
+
+    import torch
+    times = []
+    for _ in range(reps):
+        if flush is not None:
+            flush()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        step()
+        b.record()
+        b.synchronize()
+        times.append(a.elapsed_time(b))
+    return {"median": round(statistics.median(times), 4), "min": round(min(times), 4),
+            "reps": reps}
 
 
 def load_workload(name: str, cache_dir: str) -> dict:
@@ -512,6 +544,16 @@ def main():
     ms_per_step = elapsed * 1e3 / args.steps
     value = e * H / (ms_per_step / 1e3) / 1e9
 
+    # the same steps timed one by one, warm and then cold: 1 GiB written
+    # between steps (outside the timing) leaves none of the inputs in the
+    # Infinity Cache
+    steps_ms = {"warm": per_step_ms(step, args.steps)}
+    flush_buf = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+    steps_ms["cold"] = per_step_ms(step, args.steps, flush=lambda: flush_buf.fill_(1.0))
+    del flush_buf
+    for v in steps_ms.values():
+        v["value"] = round(e * H / (v["median"] / 1e3) / 1e9, 4)
+
     per = {}
     for name, ms in recs:
         d = per.setdefault(name, [0.0, 0])
@@ -564,6 +606,7 @@ def main():
                    "reorder": args.reorder, "locality": args.locality},
         "roofline": roofline,
         "kernels": kernels,
+        "steps_ms": steps_ms,
         "plan_ms": round(plan_ms, 1),
     }
     if args.compare_unfused:

@@ -42,8 +42,12 @@ def test_bench_json_line():
         assert k in roof, k
     assert roof["bound"] == "hbm" and roof["unit"] == "GB/s" and roof["peak"] == 8000.0
     assert abs(roof["frac"] - roof["achieved"] / roof["peak"]) < 1e-3
+    for kind in ("warm", "cold"):          # each step timed alone, median and minimum
+        st = d["steps_ms"][kind]
+        assert 0 < st["min"] <= st["median"] and st["reps"] == 3 and st["value"] > 0
     cb = d["cpu_baseline"]
     assert cb["kind"] == "oracle" and cb["value"] > 0 and cb["cores"] >= 1 and cb["sample"]
+    assert cb["cpu"]
 
 
 def test_bench_refuses_several_gpus():
