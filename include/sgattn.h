@@ -291,8 +291,12 @@ const char* sgat_status_string(int status);
  * bracketed by two HIP events recorded on the launch stream. After the caller
  * has synchronised the stream, sgat_trace_count / sgat_trace_get return the
  * kernel names and elapsed milliseconds in launch order. Off by default;
- * enabling it changes no result. Not thread-safe. */
+ * enabling it changes no result, but each event pair adds a few microseconds
+ * between kernels. sgat_trace_only(name) restricts the trace to the kernels
+ * of that name (as sgat_trace_get reports it; the string is copied), and
+ * sgat_trace_only(NULL) or "" restores every kernel. Not thread-safe. */
 int sgat_trace_enable(int on);
+int sgat_trace_only(const char* name);
 int sgat_trace_clear(void);
 int sgat_trace_count(void);
 int sgat_trace_get(int index, char* name, size_t name_len, float* ms);

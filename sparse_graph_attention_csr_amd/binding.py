@@ -93,6 +93,7 @@ _SIGS = {
     "reduce_bwd": (_i32, [_vp, _i64, _i64, _vp, _vp, _i32, _i32, _vp, _vp, _vp, _vp, _sz, _vp]),
     "sgat_status_string": (ctypes.c_char_p, [_i32]),
     "sgat_trace_enable": (_i32, [_i32]),
+    "sgat_trace_only": (_i32, [ctypes.c_char_p]),
     "sgat_trace_clear": (_i32, []),
     "sgat_trace_count": (_i32, []),
     "sgat_trace_get": (_i32, [_i32, ctypes.c_char_p, _sz, ctypes.POINTER(_f)]),
@@ -375,6 +376,11 @@ def reduce_bwd(plan: Plan, rowptr, colidx, arg, dout, dx, ws, stream=None):
 
 def trace_enable(on: bool = True):
     _check("sgat_trace_enable", lib().sgat_trace_enable(int(bool(on))))
+
+
+def trace_only(name: str | None = None):
+    """Trace only the kernels of this name (None: every kernel)."""
+    _check("sgat_trace_only", lib().sgat_trace_only(name.encode() if name else None))
 
 
 def trace_clear():

@@ -43,6 +43,7 @@ struct TraceRec {
     hipEvent_t start = nullptr, stop = nullptr;
 };
 bool g_trace = false;
+std::string g_trace_only;   // empty: every kernel
 std::vector<TraceRec> g_recs;
 size_t g_used = 0;
 }  // namespace
@@ -51,7 +52,7 @@ int launch(const char* name, const void* fn, dim3 grid, dim3 block, void* arg, h
 {
     void* args[] = {arg};
     TraceRec* rec = nullptr;
-    if (g_trace) {
+    if (g_trace && (g_trace_only.empty() || g_trace_only == name)) {
         if (g_used == g_recs.size()) {
             TraceRec r;
             if (hipEventCreate(&r.start) != hipSuccess || hipEventCreate(&r.stop) != hipSuccess)
@@ -358,6 +359,12 @@ int reduce_bwd(const sgat_plan* plan, int64_t n, int64_t nnz, const int64_t* row
 int sgat_trace_enable(int on)
 {
     g_trace = on != 0;
+    return SGAT_OK;
+}
+
+int sgat_trace_only(const char* name)
+{
+    g_trace_only = name ? name : "";
     return SGAT_OK;
 }
 

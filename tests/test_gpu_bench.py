@@ -18,7 +18,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 def test_bench_json_line():
     note("bench.py on gt_er1k_h4d32_f32")
     r = subprocess.run([sys.executable, "bench.py", "--workload", "gt_er1k_h4d32_f32",
-                        "--steps", "3", "--warmup", "1", "--cpu-seconds", "1"],
+                        "--steps", "3", "--warmup", "1", "--cpu-seconds", "1", "--step-times"],
                        cwd=ROOT, capture_output=True, text=True, timeout=240)
     assert r.returncode == 0, r.stderr[-2000:]
     lines = [l for l in r.stdout.splitlines() if l.startswith("{")]
@@ -54,3 +54,47 @@ def test_bench_refuses_several_gpus():
     r = subprocess.run([sys.executable, "bench.py", "--gpus", "2"], cwd=ROOT,
                        capture_output=True, text=True, timeout=120)
     assert r.returncode != 0 and "one GPU" in r.stderr
+
+
+def test_trace_only_brackets_one_kernel():
+    """The timing trace records every launch, or with trace_only(name) just the
+    launches of that kernel, and tracing changes no result."""
+    import numpy as np
+    import torch
+
+    from sparse_graph_attention_csr_amd import binding as B
+    from sparse_graph_attention_csr_amd import inputs as I
+    from tests.gpu_util import Runner
+
+    rng = np.random.default_rng(3)
+    rp, ci = I.random_csr(300, 9, rng, heavy_rows=1, heavy_deg=900)
+    r = Runner(rp, ci, device=torch.device("cuda:0"), chunk=128)
+    q, k, v, do = (torch.from_numpy(I.normal_tensor(rng, (300, 2, 32), I.F32)).cuda()
+                   for _ in range(4))
+    ref_out, ref_lse = r.gt_fwd(q, k, v)
+    ref = r.gt_bwd(q, k, v, ref_out, ref_lse, do)
+
+    def traced(only):
+        B.trace_clear()
+        B.trace_only(only)
+        B.trace_enable(True)
+        try:
+            out, lse = r.gt_fwd(q, k, v)
+            grads = r.gt_bwd(q, k, v, out, lse, do)
+            torch.cuda.synchronize()
+        finally:
+            B.trace_enable(False)
+            B.trace_only(None)
+        recs = B.trace_read()
+        B.trace_clear()
+        for a, b in zip((out, lse) + grads, (ref_out, ref_lse) + ref):
+            assert torch.equal(a, b)
+        return recs
+
+    every = traced(None)
+    names = [n for n, _ in every]
+    assert {"gt_fwd_rows", "gt_bwd_cols", "gt_bwd_rows"} <= set(names)
+    assert all(ms >= 0 for _, ms in every)
+    one = traced("gt_bwd_cols")
+    assert [n for n, _ in one] == ["gt_bwd_cols"] * names.count("gt_bwd_cols")
+    assert traced("no_such_kernel") == []
