@@ -190,12 +190,15 @@ struct GatFwdArgs {
 };
 
 // One GATv2 online-softmax step over U gathered neighbour rows (rows with
-// ok == false take no part). a LeakyReLU(z) = z g with g = a for z > 0 and
-// a * slope otherwise; at/as hold a and a * slope, both scaled by log2(e).
+// ok == false take no part). a LeakyReLU(z) = c1 z + c2 |z| with
+// c1 = a (1 + slope) / 2 and c2 = a (1 - slope) / 2 (both sides agree for
+// z > 0, z < 0 and z = 0), two multiply-adds per channel with |z| an operand
+// modifier instead of a compare, a select and a multiply-add; c1 and c2 are
+// scaled by log2(e).
 template <int DT, int VEC, int SPH, int U>
 __device__ __forceinline__ void gat_online_step(Online<VEC>& st, const Frag (&xf)[U],
                                                 const bool (&ok)[U], const float (&xs)[VEC],
-                                                const float (&at)[VEC], const float (&as)[VEC])
+                                                const float (&c1)[VEC], const float (&c2)[VEC])
 {
     float s[U];
     float mb = kNegInf;
@@ -207,7 +210,7 @@ __device__ __forceinline__ void gat_online_step(Online<VEC>& st, const Frag (&xf
 #pragma unroll
         for (int k = 0; k < VEC; ++k) {
             const float z = xs[k] + x[k];
-            part = fmaf(z, z > 0.f ? at[k] : as[k], part);
+            part = fmaf(c2[k], fabsf(z), fmaf(c1[k], z, part));
         }
         const float hs = head_sum<SPH>(part);
         s[u] = ok[u] ? hs : kNegInf;
@@ -233,20 +236,22 @@ __device__ __forceinline__ void gat_online_step(Online<VEC>& st, const Frag (&xf
 template <int DT, int D, int EPW>
 __device__ __forceinline__ void gat_fwd_prologue(const GatFwdArgs& a, const Geo<DT, D, EPW>& g,
                                                  const sgat_work_item& it, bool has, int64_t HD,
-                                                 float (&xs)[Elem<DT>::VEC], float (&at)[Elem<DT>::VEC],
-                                                 float (&as)[Elem<DT>::VEC])
+                                                 float (&xs)[Elem<DT>::VEC], float (&c1)[Elem<DT>::VEC],
+                                                 float (&c2)[Elem<DT>::VEC])
 {
     constexpr int VEC = Elem<DT>::VEC;
+    float at[VEC];
 #pragma unroll
     for (int k = 0; k < VEC; ++k) xs[k] = at[k] = 0.f;
     if (g.hvalid) {
         if (has) to_f32<DT>(ldg<DT>(a.Xs, static_cast<int64_t>(it.row) * HD + g.col), xs);
         ld_f32<VEC>(a.att + g.col, at);
     }
+    const float h1 = 0.5f * (1.f + a.slope) * kLog2e, h2 = 0.5f * (1.f - a.slope) * kLog2e;
 #pragma unroll
     for (int k = 0; k < VEC; ++k) {
-        at[k] *= kLog2e;
-        as[k] = at[k] * a.slope;
+        c1[k] = at[k] * h1;
+        c2[k] = at[k] * h2;
     }
 }
 
@@ -258,8 +263,8 @@ __device__ __forceinline__ void gat_fwd_one(const GatFwdArgs& a, int64_t ii, int
     const sgat_work_item it = a.items[ii];
     const G g(hg, a.H);
     const int64_t HD = static_cast<int64_t>(a.H) * D;
-    float xs[VEC], at[VEC], as[VEC];
-    gat_fwd_prologue<DT, D, EPW>(a, g, it, true, HD, xs, at, as);
+    float xs[VEC], c1[VEC], c2[VEC];
+    gat_fwd_prologue<DT, D, EPW>(a, g, it, true, HD, xs, c1, c2);
     Online<VEC> st;
     const int32_t* ci = a.colidx + it.begin;
     for (int base = 0; base < it.len; base += kWave) {
@@ -276,7 +281,7 @@ __device__ __forceinline__ void gat_fwd_one(const GatFwdArgs& a, int64_t ii, int
                 xf[u] = frag_zero();
                 if (ok[u] && g.hvalid) xf[u] = ldg<DT>(a.Xt, j * HD + g.col);
             }
-            gat_online_step<DT, VEC, G::SPH, U>(st, xf, ok, xs, at, as);
+            gat_online_step<DT, VEC, G::SPH, U>(st, xf, ok, xs, c1, c2);
         }
     }
     if constexpr (EPW > 1) merge_groups<VEC, G::LPE>(st);
@@ -299,8 +304,8 @@ __device__ __forceinline__ void gat_fwd_multi(const GatFwdArgs& a, int64_t first
     const bool has = idx < a.n_items;
     sgat_work_item it{0, 0, 0, -1, 0};
     if (has) it = a.items[idx];
-    float xs[VEC], at[VEC], as[VEC];
-    gat_fwd_prologue<DT, D, EPW>(a, g, it, has, HD, xs, at, as);
+    float xs[VEC], c1[VEC], c2[VEC];
+    gat_fwd_prologue<DT, D, EPW>(a, g, it, has, HD, xs, c1, c2);
     Online<VEC> st;
     const int32_t* ci = a.colidx + it.begin;
     const int lead = g.sub * G::LPE;
@@ -317,7 +322,7 @@ __device__ __forceinline__ void gat_fwd_multi(const GatFwdArgs& a, int64_t first
                 xf[u] = frag_zero();
                 if (ok[u] && g.hvalid) xf[u] = ldg<DT>(a.Xt, j * HD + g.col);
             }
-            gat_online_step<DT, VEC, G::SPH, U>(st, xf, ok, xs, at, as);
+            gat_online_step<DT, VEC, G::SPH, U>(st, xf, ok, xs, c1, c2);
         }
     }
     if (has && g.hvalid)

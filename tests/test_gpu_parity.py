@@ -109,6 +109,34 @@ def test_gat_short_and_long_items(dt, H, D):
         assert rel_err(host(da), ra) <= TOL[dt]
 
 
+@pytest.mark.parametrize("dt,H,D", [("bf16", 2, 64), ("f32", 4, 32), ("bf16", 4, 128)])
+def test_gat_da_many_partials(dt, H, D):
+    """da summed over thousands of workgroup partials, which takes the two-level
+    reduction (runs of 64 partials first): 40,000 nodes give at least one
+    transposed-pass workgroup per 16 sources, far above the 1,024 partials a
+    single level takes. Every element of every output against the oracle."""
+    note(f"gat da many partials dt={dt} H={H} D={D}")
+    rng = np.random.default_rng(47 + H + D)
+    n = 40_000
+    rp, ci = I.random_csr(n, 12, rng, empty_frac=0.02, heavy_rows=2, heavy_deg=3000)
+    t = tensors(9, n, H, D, dt, ["xs", "xt", "dout"])
+    a = rng.standard_normal((H, D)).astype(np.float32) / np.sqrt(D)
+    r = Runner(rp, ci)
+    xs, xt, do = (dev(t[x]) for x in ("xs", "xt", "dout"))
+    ad = dev(a)
+    out, lse = r.gat_fwd(xs, xt, ad)
+    dxs, dxt, da = r.gat_bwd(xs, xt, ad, out, lse, do)
+    ro, rl = oracle.gat_fwd(rp, ci, t["xs"], t["xt"], a)
+    rs, rt, ra = oracle.gat_bwd(rp, ci, t["xs"], t["xt"], a, t["dout"])
+    assert rel_err(host(out), ro) <= TOL[dt]
+    assert rel_err(host(dxs), rs) <= TOL[dt]
+    assert rel_err(host(dxt), rt) <= TOL[dt]
+    assert rel_err(host(da), ra) <= TOL[dt]
+    # the same call again gives the same bits (fixed-order reduction)
+    _, _, da2 = r.gat_bwd(xs, xt, ad, out, lse, do)
+    assert np.array_equal(host(da), host(da2))
+
+
 def test_er_workload_forward_full():
     """The fp32 Erdos-Renyi workload (N=1000, H=4, D=32), every output element."""
     note("gt_er1k_h4d32_f32 forward")
