@@ -697,25 +697,28 @@ __device__ __forceinline__ void da_block_partial(const float (*dal)[kWave * VEC]
 // One edge (i, j) for the lane's channels: p = exp(e_ij - lse_i), dE =
 // p (dO_i . Xt_j - Delta_i); adds dE s to T (s = 1 for z > 0, the slope
 // otherwise; dXs = a . T) and stages (p, dE) and the signs of z in the edge's
-// LDS record. The score uses a LeakyReLU(z) = z g, g = a s.
+// LDS record. The score: a LeakyReLU(z) = h1 (a z) + h2 (a |z|) summed over
+// the channels, with h1 = (1 + slope) / 2 and h2 = (1 - slope) / 2 (here
+// also scaled by log2(e)): two multiply-adds per channel on a alone.
 template <int DT, int D, int EPW>
 __device__ __forceinline__ void gat_bwd_edge(const Geo<DT, D, EPW>& g, const Frag& xf, bool ok,
                                              const GatRowState<Elem<DT>::VEC>& r,
-                                             const float (&at)[Elem<DT>::VEC],
-                                             const float (&as)[Elem<DT>::VEC], float slope,
-                                             float (&tsum)[Elem<DT>::VEC], uint32_t* lr)
+                                             const float (&at)[Elem<DT>::VEC], float h1, float h2,
+                                             float slope, float (&tsum)[Elem<DT>::VEC],
+                                             uint32_t* lr)
 {
     using G = Geo<DT, D, EPW>;
     constexpr int VEC = G::VEC;
     float x[VEC], z[VEC];
     to_f32<DT>(xf, x);
-    float part = 0.f;
+    float p1 = 0.f, p2 = 0.f;
 #pragma unroll
     for (int k = 0; k < VEC; ++k) {
         z[k] = r.xs[k] + x[k];
-        part = fmaf(z[k], z[k] > 0.f ? at[k] : as[k], part);
+        p1 = fmaf(at[k], z[k], p1);
+        p2 = fmaf(at[k], fabsf(z[k]), p2);
     }
-    const float e2 = head_sum<G::SPH>(part) * kLog2e;
+    const float e2 = head_sum<G::SPH>(fmaf(h1, p1, h2 * p2));
     const float dp = head_sum<G::SPH>(dot<DT>(r.dof, xf));
     const float p = ok ? fast_exp2(e2 - r.lse2) : 0.f;
     const float dE = p * (dp - r.delta);
@@ -745,7 +748,7 @@ constexpr int gat_short_rows_waves(int dt, int D, int epw)
     return dt == SGAT_BF16 && (D == 64 || (D == 128 && epw == 4)) ? 6 : 1;
 }
 
-template <int DT, int D, int EPW, int U, int UMAX, bool SHORT>
+template <int DT, int D, int EPW, int U, bool SHORT>
 __global__ __launch_bounds__(kBlock)
 __attribute__((amdgpu_waves_per_eu(SHORT ? gat_short_rows_waves(DT, D, EPW) : 1)))
 void gat_bwd_rows(GatBwdRowArgs a)
@@ -753,7 +756,6 @@ void gat_bwd_rows(GatBwdRowArgs a)
     using G = Geo<DT, D, EPW>;
     constexpr int VEC = G::VEC;
     constexpr int RS = gat_rec_dwords(G::HG, G::LPE);
-    constexpr int UM = UMAX < G::LPE ? UMAX : G::LPE;   // per-group step of the short items
     __shared__ float dal[kWavesPerBlock][kWave * VEC];  // per-lane da sums
     // records of one block of edges (64 for a single item, LPE per group for
     // short items), written out contiguously once per block: per-edge global
@@ -769,10 +771,9 @@ void gat_bwd_rows(GatBwdRowArgs a)
 #pragma unroll
     for (int k = 0; k < VEC; ++k) myda[k] = 0.f;
 
-    float at[VEC] = {}, as[VEC];
+    float at[VEC] = {};
     if (g.hvalid) ld_f32<VEC>(a.att + g.col, at);
-#pragma unroll
-    for (int k = 0; k < VEC; ++k) as[k] = at[k] * a.slope;
+    const float h1 = 0.5f * (1.f + a.slope) * kLog2e, h2 = 0.5f * (1.f - a.slope) * kLog2e;
 
     const int64_t n_wunits = SHORT ? (a.n_items - a.n_single + EPW - 1) / EPW : a.n_single;
     const int64_t stride = static_cast<int64_t>(gridDim.x) * kWavesPerBlock;
@@ -788,21 +789,32 @@ void gat_bwd_rows(GatBwdRowArgs a)
             for (int base = 0; base < it.len; base += kWave) {
                 const int nb = min(kWave, it.len - base);
                 const int cj = g.lane < nb ? ci[base + g.lane] : 0;
-                for (int t = 0; t < nb; t += EPW * U) {
-                    Frag xf[U];
-                    bool ok[U];
+                // steps of EPW*U edges over two register buffers: the next
+                // step's rows are in flight while a step is processed (the
+                // short-item loop below explains the unconditional loads)
+                auto fetch = [&](int t, Frag (&xf)[U]) {
 #pragma unroll
                     for (int u = 0; u < U; ++u) {
                         const int e = t + u * EPW + g.sub;
-                        ok[u] = e < nb;
-                        const int64_t j = bcast<EPW>(cj, e);
-                        xf[u] = frag_zero();
-                        if (ok[u] && g.hvalid) xf[u] = ldg<DT>(a.Xt, j * HD + g.col);
+                        const int64_t j = bcast<EPW>(cj, e < nb ? e : nb - 1);
+                        xf[u] = ldg<DT>(a.Xt, g.hvalid ? j * HD + g.col : 0);
                     }
+                };
+                auto step = [&](int t, const Frag (&xf)[U]) {
 #pragma unroll
-                    for (int u = 0; u < U; ++u)   // t + u*EPW + sub < 64: EPW*U divides 64
-                        gat_bwd_edge<DT, D, EPW>(g, xf[u], ok[u], r, at, as, a.slope, ts,
-                                                 lrec + (t + u * EPW + g.sub) * RS);
+                    for (int u = 0; u < U; ++u) {   // t + u*EPW + sub < 64: EPW*U divides 64
+                        const int e = t + u * EPW + g.sub;
+                        gat_bwd_edge<DT, D, EPW>(g, xf[u], e < nb, r, at, h1, h2, a.slope, ts,
+                                                 lrec + e * RS);
+                    }
+                };
+                Frag xa[U], xb[U];
+                fetch(0, xa);
+                for (int t = 0; t < nb; t += 2 * EPW * U) {
+                    fetch(t + EPW * U, xb);
+                    step(t, xa);
+                    fetch(t + 2 * EPW * U, xa);
+                    if (t + EPW * U < nb) step(t + EPW * U, xb);   // uniform over the wave
                 }
                 wave_lds_fence();
                 {
@@ -837,20 +849,25 @@ void gat_bwd_rows(GatBwdRowArgs a)
             for (int base = 0; base < it.len; base += G::LPE) {
                 const int nb = min(G::LPE, it.len - base);
                 const int cj = g.pos < nb ? ci[base + g.pos] : 0;
-                for (int t = 0; t < nb; t += UM) {
-                    Frag xf[UM];
-                    bool ok[UM];
-#pragma unroll
-                    for (int u = 0; u < UM; ++u) {
-                        ok[u] = t + u < nb;
-                        const int64_t j = __shfl(cj, lead + t + u);
-                        xf[u] = frag_zero();
-                        if (ok[u] && g.hvalid) xf[u] = ldg<DT>(a.Xt, j * HD + g.col);
-                    }
-#pragma unroll
-                    for (int u = 0; u < UM; ++u)   // t + u < LPE: UM divides LPE
-                        gat_bwd_edge<DT, D, EPW>(g, xf[u], ok[u], r, at, as, a.slope, ts,
-                                                 grec + (t + u) * RS);
+                // rolling prefetch over two buffers: the next edge's row is in
+                // flight while an edge is processed, and each load refills the
+                // buffer just consumed (no register copy that would wait for
+                // it). The loads are unconditional (a padded head's lanes read
+                // row 0; past the last edge the last one is read again), so
+                // each wait needs only the older of two loads.
+                auto fetch = [&](int t) {
+                    const int64_t j = __shfl(cj, lead + (t < nb ? t : nb - 1));
+                    return ldg<DT>(a.Xt, g.hvalid ? j * HD + g.col : 0);
+                };
+                Frag xa = fetch(0);
+                for (int t = 0; t < nb; t += 2) {
+                    const Frag xb = fetch(t + 1);
+                    gat_bwd_edge<DT, D, EPW>(g, xa, true, r, at, h1, h2, a.slope, ts,
+                                             grec + t * RS);
+                    xa = fetch(t + 2);
+                    if (t + 1 < nb)   // the same for the whole group
+                        gat_bwd_edge<DT, D, EPW>(g, xb, true, r, at, h1, h2, a.slope, ts,
+                                                 grec + (t + 1) * RS);
                 }
                 wave_lds_fence();
                 {

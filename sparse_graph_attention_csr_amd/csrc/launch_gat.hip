@@ -8,12 +8,14 @@
 namespace sgat {
 
 // Neighbour rows each wave gathers before their first use (compile-time
-// tunables; -DSGAT_UNROLL_FWD=... etc. override them).
+// tunables; -DSGAT_UNROLL_FWD=... etc. override them). The CSR backward pass
+// gathers SGAT_UNROLL_BWD rows per edge group into each of two register
+// buffers, one in flight while the other is used.
 #ifndef SGAT_UNROLL_FWD
 #define SGAT_UNROLL_FWD 8
 #endif
 #ifndef SGAT_UNROLL_BWD
-#define SGAT_UNROLL_BWD 4
+#define SGAT_UNROLL_BWD 2
 #endif
 #ifndef SGAT_UNROLL_ROWS
 #define SGAT_UNROLL_ROWS 8
@@ -26,9 +28,6 @@ namespace sgat {
 #endif
 #ifndef SGAT_UNROLL_MULTI
 #define SGAT_UNROLL_MULTI 4
-#endif
-#ifndef SGAT_UNROLL_MULTI_BWD
-#define SGAT_UNROLL_MULTI_BWD 1
 #endif
 // one source row per step and edge group in the transposed pass: with its
 // per-node da terms a second one costs occupancy
@@ -216,10 +215,10 @@ int launch_gat_bwd(const Plan& p, int H, int D, int dt, const int32_t* colidx, c
 #define X(DT_, D_, E_)                                                                        \
     if (dt == DT_ && D == D_ && dc.epw == E_) {                                               \
         fr = reinterpret_cast<const void*>(                                                   \
-            &gat_bwd_rows<DT_, D_, E_, unroll_bwd(E_), SGAT_UNROLL_MULTI_BWD, false>);        \
+            &gat_bwd_rows<DT_, D_, E_, unroll_bwd(E_), false>);                               \
         if constexpr (E_ > 1)                                                                 \
             frs = reinterpret_cast<const void*>(                                              \
-                &gat_bwd_rows<DT_, D_, E_, unroll_bwd(E_), SGAT_UNROLL_MULTI_BWD, true>);     \
+                &gat_bwd_rows<DT_, D_, E_, unroll_bwd(E_), true>);                            \
         fc = reinterpret_cast<const void*>(                                                   \
             &gat_bwd_cols<DT_, D_, E_, SGAT_UNROLL_COLS, SGAT_UNROLL_MULTI_COLS>);            \
     }
