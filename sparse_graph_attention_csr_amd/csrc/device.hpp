@@ -39,6 +39,18 @@ __device__ __forceinline__ Frag ldg(const void* base, int64_t elem)
     return Frag{{v.x, v.y, v.z, v.w}};
 }
 
+// A row read once per kernel (the item's own row): marked non-temporal so it
+// does not displace gathered rows that other waves will read again.
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+template <int DT>
+__device__ __forceinline__ Frag ldg_once(const void* base, int64_t elem)
+{
+    const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(
+        static_cast<const char*>(base) + elem * Elem<DT>::BYTES));
+    return Frag{{v.x, v.y, v.z, v.w}};
+}
+
 template <int DT>
 __device__ __forceinline__ void to_f32(const Frag& f, float (&x)[Elem<DT>::VEC])
 {
@@ -90,7 +102,9 @@ __device__ __forceinline__ void stg(void* base, int64_t elem, const float (&x)[E
         v = make_uint4(pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]), pack_bf16x2(x[4], x[5]),
                        pack_bf16x2(x[6], x[7]));
     }
-    *reinterpret_cast<uint4*>(static_cast<char*>(base) + elem * Elem<DT>::BYTES) = v;
+    const u32x4_t w = {v.x, v.y, v.z, v.w};
+    __builtin_nontemporal_store(w, reinterpret_cast<u32x4_t*>(static_cast<char*>(base) +
+                                                              elem * Elem<DT>::BYTES));
 }
 
 template <int N>

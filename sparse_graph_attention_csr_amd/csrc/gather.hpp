@@ -118,7 +118,7 @@ __global__ __launch_bounds__(kBlock) void gt_fwd_rows(GtFwdArgs a)
     const int64_t HD = static_cast<int64_t>(a.H) * D;
 
     Frag q = frag_zero();
-    if (g.hvalid) q = ldg<DT>(a.Q, static_cast<int64_t>(it.row) * HD + g.col);
+    if (g.hvalid) q = ldg_once<DT>(a.Q, static_cast<int64_t>(it.row) * HD + g.col);
     Online<VEC> st;
     const int32_t* ci = a.colidx + it.begin;
     for (int base = 0; base < it.len; base += kWave) {
@@ -244,7 +244,7 @@ __device__ __forceinline__ void gat_fwd_prologue(const GatFwdArgs& a, const Geo<
 #pragma unroll
     for (int k = 0; k < VEC; ++k) xs[k] = at[k] = 0.f;
     if (g.hvalid) {
-        if (has) to_f32<DT>(ldg<DT>(a.Xs, static_cast<int64_t>(it.row) * HD + g.col), xs);
+        if (has) to_f32<DT>(ldg_once<DT>(a.Xs, static_cast<int64_t>(it.row) * HD + g.col), xs);
         ld_f32<VEC>(a.att + g.col, at);
     }
     const float h1 = 0.5f * (1.f + a.slope) * kLog2e, h2 = 0.5f * (1.f - a.slope) * kLog2e;
@@ -528,7 +528,7 @@ __global__ __launch_bounds__(kBlock) void bwd_delta(DeltaArgs a)
     const int64_t HD = static_cast<int64_t>(a.H) * D;
     Frag of = frag_zero(), dof = frag_zero();
     if (ok) {
-        of = ldg<DT>(a.O, node * HD + g.col);
+        of = ldg_once<DT>(a.O, node * HD + g.col);
         dof = ldg<DT>(a.dO, node * HD + g.col);
     }
     const float delta = head_sum<G::SPH>(dot<DT>(dof, of));
@@ -582,7 +582,7 @@ __global__ __launch_bounds__(kBlock) void gt_bwd_rows(GtBwdRowArgs a)
                 d[u] = 0.f;
                 if (e < nb && g.hvalid) {
                     kf[u] = ldg<DT>(a.K, j * HD + g.col);
-                    d[u] = dsr[static_cast<int64_t>(base + e) * a.H];
+                    d[u] = __builtin_nontemporal_load(dsr + static_cast<int64_t>(base + e) * a.H);
                 }
             }
 #pragma unroll
@@ -651,9 +651,9 @@ __device__ __forceinline__ GatRowState<Elem<DT>::VEC> gat_row_state(const GatBwd
 #pragma unroll
     for (int k = 0; k < VEC; ++k) r.xs[k] = 0.f;
     if (load && g.hvalid) {
-        to_f32<DT>(ldg<DT>(a.Xs, ro), r.xs);
-        r.dof = ldg<DT>(a.dO, ro);
-        of = ldg<DT>(a.O, ro);
+        to_f32<DT>(ldg_once<DT>(a.Xs, ro), r.xs);
+        r.dof = ldg<DT>(a.dO, ro);   // gathered again by the transposed pass
+        of = ldg_once<DT>(a.O, ro);
         r.lse2 = a.lse[static_cast<int64_t>(it.row) * a.H + g.head] * kLog2e;
     }
     r.delta = head_sum<Geo<DT, D, EPW>::SPH>(dot<DT>(r.dof, of));
@@ -929,8 +929,8 @@ __global__ __launch_bounds__(kBlock) void gt_bwd_cols(GtBwdColArgs a)
 
     Frag kj = frag_zero(), vj = frag_zero();
     if (g.hvalid) {
-        kj = ldg<DT>(a.K, static_cast<int64_t>(it.row) * HD + g.col);
-        vj = ldg<DT>(a.V, static_cast<int64_t>(it.row) * HD + g.col);
+        kj = ldg_once<DT>(a.K, static_cast<int64_t>(it.row) * HD + g.col);
+        vj = ldg_once<DT>(a.V, static_cast<int64_t>(it.row) * HD + g.col);
     }
     float dk[VEC] = {}, dv[VEC] = {};
     const int32_t* ri = a.rowidx + it.begin;
@@ -1002,6 +1002,14 @@ struct GatBwdColArgs {
     float* part;
     float* da_part;             // [gridDim.x][H*D]
 };
+
+// (p, dE) of one head from an edge record, read once (non-temporal)
+__device__ __forceinline__ float2 rec_pd(const uint32_t* r)
+{
+    typedef float f32x2_t __attribute__((ext_vector_type(2)));
+    const f32x2_t v = __builtin_nontemporal_load(reinterpret_cast<const f32x2_t*>(r));
+    return make_float2(v.x, v.y);
+}
 
 // Adds U edges (ok == false: no edge) to pacc += p dO_i and uacc += dE s,
 // s from the sign bits of the edge record (1 for z > 0, the slope otherwise).
@@ -1075,8 +1083,8 @@ __global__ __launch_bounds__(kBlock) void gat_bwd_cols(GatBwdColArgs a)
                         if (e < nb && g.hvalid) {
                             const uint32_t* r = rbase + eid * RS;
                             df[u] = ldg<DT>(a.dO, i * HD + g.col);
-                            pd[u] = *reinterpret_cast<const float2*>(r + 2 * hl);
-                            zb[u] = r[zl] >> zsh;
+                            pd[u] = rec_pd(r + 2 * hl);
+                            zb[u] = __builtin_nontemporal_load(r + zl) >> zsh;
                         }
                     }
                     gat_col_step<DT, VEC, U>(pacc, uacc, df, pd, zb, a.slope);
@@ -1092,7 +1100,7 @@ __global__ __launch_bounds__(kBlock) void gat_bwd_cols(GatBwdColArgs a)
 #pragma unroll
                 for (int k = 0; k < VEC; ++k) dxt[k] = fmaf(at[k], uacc[k], pacc[k]);
                 grad_store<DT, VEC>(dxt, 1.f, it, HD, g.col, a.dXt, a.part);
-                to_f32<DT>(ldg<DT>(a.Xt, static_cast<int64_t>(it.row) * HD + g.col), xt);
+                to_f32<DT>(ldg_once<DT>(a.Xt, static_cast<int64_t>(it.row) * HD + g.col), xt);
                 da_add<VEC>(myda, xt, uacc);
             }
         } else if constexpr (EPW > 1) {
@@ -1123,8 +1131,8 @@ __global__ __launch_bounds__(kBlock) void gat_bwd_cols(GatBwdColArgs a)
                         if (t + u < nb && g.hvalid) {
                             const uint32_t* r = rbase + eid * RS;
                             df[u] = ldg<DT>(a.dO, i * HD + g.col);
-                            pd[u] = *reinterpret_cast<const float2*>(r + 2 * hl);
-                            zb[u] = r[zl] >> zsh;
+                            pd[u] = rec_pd(r + 2 * hl);
+                            zb[u] = __builtin_nontemporal_load(r + zl) >> zsh;
                         }
                     }
                     gat_col_step<DT, VEC, V>(pacc, uacc, df, pd, zb, a.slope);
@@ -1136,7 +1144,7 @@ __global__ __launch_bounds__(kBlock) void gat_bwd_cols(GatBwdColArgs a)
 #pragma unroll
                 for (int k = 0; k < VEC; ++k) dxt[k] = fmaf(at[k], uacc[k], pacc[k]);
                 grad_store<DT, VEC>(dxt, 1.f, it, HD, g.col, a.dXt, a.part);
-                to_f32<DT>(ldg<DT>(a.Xt, static_cast<int64_t>(it.row) * HD + g.col), xt);
+                to_f32<DT>(ldg_once<DT>(a.Xt, static_cast<int64_t>(it.row) * HD + g.col), xt);
                 da_add<VEC>(myda, xt, uacc);
             }
         }

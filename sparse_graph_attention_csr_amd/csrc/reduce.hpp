@@ -49,7 +49,9 @@ __device__ __forceinline__ void stg_exact(void* base, int64_t elem, const float 
             w[k] = (__float_as_uint(x[2 * k]) >> 16) | (__float_as_uint(x[2 * k + 1]) & 0xffff0000u);
         v = make_uint4(w[0], w[1], w[2], w[3]);
     }
-    *reinterpret_cast<uint4*>(static_cast<char*>(base) + elem * Elem<DT>::BYTES) = v;
+    const u32x4_t nv = {v.x, v.y, v.z, v.w};   // written once: non-temporal
+    __builtin_nontemporal_store(nv, reinterpret_cast<u32x4_t*>(static_cast<char*>(base) +
+                                                               elem * Elem<DT>::BYTES));
 }
 
 template <int N>
@@ -57,8 +59,11 @@ __device__ __forceinline__ void st_i32(int32_t* p, const int32_t (&x)[N])
 {
     static_assert(N % 4 == 0, "");
 #pragma unroll
-    for (int k = 0; k < N; k += 4)
-        *reinterpret_cast<int4*>(p + k) = make_int4(x[k], x[k + 1], x[k + 2], x[k + 3]);
+    for (int k = 0; k < N; k += 4) {   // written once: non-temporal
+        const u32x4_t v = {static_cast<uint32_t>(x[k]), static_cast<uint32_t>(x[k + 1]),
+                           static_cast<uint32_t>(x[k + 2]), static_cast<uint32_t>(x[k + 3])};
+        __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t*>(p + k));
+    }
 }
 
 template <int N>
