@@ -737,6 +737,14 @@ __device__ __forceinline__ void gat_bwd_edge(const Geo<DT, D, EPW>& g, const Fra
     }
 }
 
+// 8 bytes of an edge record, read once by the transposed pass (non-temporal)
+__device__ __forceinline__ void rec_store(uint2* dst, uint2 v)
+{
+    typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+    const u32x2_t w = {v.x, v.y};
+    __builtin_nontemporal_store(w, reinterpret_cast<u32x2_t*>(dst));
+}
+
 // SHORT = false: the items [0, n_single), one wave each; SHORT = true: the
 // items [n_single, n_items), EPW to a wave. Each launch writes one da
 // partial per workgroup into its own da_part.
@@ -820,7 +828,7 @@ void gat_bwd_rows(GatBwdRowArgs a)
                 {
                     uint2* dst = reinterpret_cast<uint2*>(rec + static_cast<int64_t>(base) * RS);
                     const uint2* src = reinterpret_cast<const uint2*>(lrec);
-                    for (int w = g.lane; w < nb * (RS / 2); w += kWave) dst[w] = src[w];
+                    for (int w = g.lane; w < nb * (RS / 2); w += kWave) rec_store(dst + w, src[w]);
                 }
                 wave_lds_fence();
             }
@@ -873,7 +881,7 @@ void gat_bwd_rows(GatBwdRowArgs a)
                 {
                     uint2* dst = reinterpret_cast<uint2*>(rec + static_cast<int64_t>(base) * RS);
                     const uint2* src = reinterpret_cast<const uint2*>(grec);
-                    for (int w = g.pos; w < nb * (RS / 2); w += G::LPE) dst[w] = src[w];
+                    for (int w = g.pos; w < nb * (RS / 2); w += G::LPE) rec_store(dst + w, src[w]);
                 }
                 wave_lds_fence();
             }
@@ -965,7 +973,8 @@ __global__ __launch_bounds__(kBlock) void gt_bwd_cols(GtBwdColArgs a)
                 const float dp = head_sum<G::SPH>(dot<DT>(df[u], vj));
                 const float p = ok[u] ? fast_exp2(s2 - rs[u].lse2) : 0.f;
                 const float ds = p * (dp - rs[u].delta);
-                if (ok[u] && g.hvalid && g.leader) a.ds[eid[u] * a.H + g.head] = ds;
+                if (ok[u] && g.hvalid && g.leader)
+                    __builtin_nontemporal_store(ds, a.ds + eid[u] * a.H + g.head);
                 float qx[VEC], dx[VEC];
                 to_f32<DT>(qf[u], qx);
                 to_f32<DT>(df[u], dx);
