@@ -227,28 +227,36 @@ def cpu_baseline(w, seconds: float):
     rp, ci = w["rowptr"], w["colidx"]
     n = rp.size - 1
 
+    split = [0.0, 0.0]   # forward and backward seconds of the runs that count
+
     def run(r):
         sub = rp.copy()
         sub[r + 1:] = rp[r]
         e = int(sub[-1])
+        bwd = spec.passes == "fwd+bwd"
         t0 = time.perf_counter()
         if spec.op == "reduce":
             _, arg = oracle.reduce_fwd(sub, ci[:e], w["x"], "min", rows=np.arange(r))
-            if spec.passes == "fwd+bwd":
+            t1 = time.perf_counter()
+            if bwd:
                 full = np.full((n, spec.dim), -1, dtype=np.int64)
                 full[:r] = arg
                 oracle.reduce_bwd(sub, ci[:e], full, w["dout"])
         elif spec.op == "gt":
             oracle.gt_fwd(sub, ci[:e], w["q"], w["k"], w["v"], rows=np.arange(r))
-            if spec.passes == "fwd+bwd":
+            t1 = time.perf_counter()
+            if bwd:
                 oracle.gt_bwd(sub, ci[:e], w["q"], w["k"], w["v"], w["dout"],
                               dst_rows=np.arange(r), src_rows=np.unique(ci[:e]))
         else:
             oracle.gat_fwd(sub, ci[:e], w["xs"], w["xt"], w["a"], 0.2, rows=np.arange(r))
-            if spec.passes == "fwd+bwd":
+            t1 = time.perf_counter()
+            if bwd:
                 oracle.gat_bwd(sub, ci[:e], w["xs"], w["xt"], w["a"], w["dout"], 0.2,
                                dst_rows=np.arange(r), src_rows=np.unique(ci[:e]))
-        return e, time.perf_counter() - t0
+        t2 = time.perf_counter()
+        split[0], split[1] = t1 - t0, t2 - t1
+        return e, t2 - t0
 
 
     r = min(n, 2000)
@@ -261,12 +269,17 @@ def cpu_baseline(w, seconds: float):
         r = int(min(n, np.searchsorted(rp, target)))
         e, t = run(r)
     reps = 1
+    tf, tb = split
     if r == n and t < seconds / 2:          # the whole workload is quick: repeat it
         reps = int(np.ceil(seconds / max(t, 1e-9)))
-        t = sum(run(r)[1] for _ in range(reps))
+        t = tf = tb = 0.0
+        for _ in range(reps):
+            t += run(r)[1]
+            tf, tb = tf + split[0], tb + split[1]
     rate = reps * e * spec.heads / t / 1e9
     return {"value": rate, "unit": "GEdge\u00b7head/s", "cores": oracle.num_threads(),
-            "cpu": cpu_model(), "kind": "oracle",
+            "cpu": cpu_model(), "fwd_seconds": round(tf, 3), "bwd_seconds": round(tb, 3),
+            "kind": "oracle",
             "sample": f"destination rows 0..{r - 1} of {n} ({e} of {int(rp[-1])} edges), "
                       f"{spec.passes}, fp64, {reps} run(s), {t:.1f} s"}
 
