@@ -137,6 +137,45 @@ def test_gat_da_many_partials(dt, H, D):
     assert np.array_equal(host(da), host(da2))
 
 
+@pytest.mark.parametrize("slope", [0.0, 0.01, 1.0, -0.5, 3.0])
+@pytest.mark.parametrize("dt,H,D", [("bf16", 2, 64), ("f32", 4, 32), ("bf16", 8, 64)])
+def test_gat_slopes_and_exact_zeros(dt, H, D, slope):
+    """Any LeakyReLU slope (ReLU, identity, negative, steeper than 1), on
+    inputs that are multiples of 1/2 in [-2, 2], so that z = Xs_i + Xt_j is
+    exactly 0 on about one channel in nine: there the derivative is the slope
+    (the z > 0 convention), in both backward passes' signs and in da.
+
+    With slope 1 the score is a.Xs_i + a.Xt_j, the softmax cancels the first
+    term and dXs is exactly 0 (the oracle, which applies the softmax Jacobian
+    in full, returns 0 to fp64 rounding). The library forms Delta from the
+    output as the caller stores it (bf16 here), so its dXs is then the rounding
+    residue of that output; dXs is therefore measured against the larger of
+    the dXs and dXt scales (both are sums of a dE terms)."""
+    note(f"gat slopes dt={dt} H={H} D={D} slope={slope}")
+    rng = np.random.default_rng(61 + H + D)
+    rp, ci = I.random_csr(400, 24, rng, empty_frac=0.05, heavy_rows=2, heavy_deg=400)
+    n = rp.size - 1
+
+    def halves(shape):
+        x = (rng.integers(-4, 5, size=shape) * 0.5).astype(np.float32)
+        return I.f32_to_bf16_bits(x) if dt == "bf16" else x
+    xs_h, xt_h, do_h = halves((n, H, D)), halves((n, H, D)), halves((n, H, D))
+    a = (rng.standard_normal((H, D)) / np.sqrt(D)).astype(np.float32)
+    zeros = np.mean(widen(xs_h)[np.repeat(np.arange(n), np.diff(rp))] + widen(xt_h)[ci] == 0)
+    assert zeros > 0.05
+    r = Runner(rp, ci, chunk=64)
+    xs, xt, do, ad = dev(xs_h), dev(xt_h), dev(do_h), dev(a)
+    out, lse = r.gat_fwd(xs, xt, ad, slope=slope)
+    dxs, dxt, da = r.gat_bwd(xs, xt, ad, out, lse, do, slope=slope)
+    ro, rl = oracle.gat_fwd(rp, ci, xs_h, xt_h, a, slope)
+    rs, rt, ra = oracle.gat_bwd(rp, ci, xs_h, xt_h, a, do_h, slope)
+    for name, got, ref in (("out", out, ro), ("lse", lse, rl), ("dXt", dxt, rt), ("da", da, ra)):
+        assert rel_err(host(got), ref) <= TOL[dt], name
+    scale = max(np.abs(rs).max(), np.abs(rt).max())
+    assert np.isfinite(host(dxs)).all()
+    assert np.abs(host(dxs) - rs).max() <= TOL[dt] * scale, "dXs"
+
+
 def test_er_workload_forward_full():
     """The fp32 Erdos-Renyi workload (N=1000, H=4, D=32), every output element."""
     note("gt_er1k_h4d32_f32 forward")
