@@ -6,7 +6,7 @@
 // Heavy-tailed degree distributions let a few high-degree nodes dominate the
 // run time and starve the GPU of parallelism (Yandex Research blog "On
 // efficient scaling of GNNs via IO-aware layer implementations", paragraph on
-// aggregation layers; the "super nodes" of the DF-GNN paper, Abstract). The
+// aggregation layers; the super nodes of the DF-GNN paper, Abstract). The
 // work list answers that by cutting every row longer than `chunk` edges into
 // chunks of `chunk` edges, each its own wavefront, and by ordering the rest by
 // a coarse degree bin so the longest work is dispatched first while rows of
