@@ -92,7 +92,7 @@ typedef struct sgat_plan_opts {
     int64_t chunk;        /* A row (or, in the transposed CSR, a source) with more
                              than `chunk` edges is split into chunks of `chunk`
                              edges, each processed by its own wavefront and merged
-                             afterwards in fixed order. Default 512. */
+                             afterwards in fixed order. Default 1024. */
     int32_t tile_min_nnz; /* A 16x16 block of the adjacency with at least this many
                              distinct edges becomes a dense tile. Default 32. */
     int32_t block_sparse; /* 1: also build the 16x16 tile layout and residual CSR. */

@@ -9,7 +9,7 @@
 
 namespace sgat {
 
-constexpr int64_t kDefaultChunk = 512;
+constexpr int64_t kDefaultChunk = 1024;
 constexpr int32_t kDefaultTileMinNnz = 32;
 constexpr int kTile = 16;
 constexpr size_t kAlign = 256;
