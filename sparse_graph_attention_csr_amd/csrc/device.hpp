@@ -41,6 +41,25 @@ __device__ __forceinline__ Frag ldg(const void* base, int64_t elem)
 
 // A row read once per kernel (the item's own row): marked non-temporal so it
 // does not displace gathered rows that other waves will read again.
+// A lane's 16 bytes of row `row` of a row-major [N][H*D] array: lane_base is
+// the array plus the lane's column offset, row_bytes the row pitch. One
+// 32 x 32 + 64-bit multiply-add forms the address (rows and pitches fit 32
+// bits) instead of 64-bit index arithmetic.
+__device__ __forceinline__ Frag ldg_row(const char* lane_base, uint32_t row, uint32_t row_bytes)
+{
+    const uint4 v = *reinterpret_cast<const uint4*>(
+        lane_base + static_cast<uint64_t>(row) * row_bytes);
+    return Frag{{v.x, v.y, v.z, v.w}};
+}
+
+// ldg_row for element `col` of row `row` of an [N][H*D] array of DT
+template <int DT>
+__device__ __forceinline__ Frag ldg_nbr(const void* base, uint32_t row, int col, int64_t HD)
+{
+    return ldg_row(static_cast<const char*>(base) + col * Elem<DT>::BYTES, row,
+                   static_cast<uint32_t>(HD) * Elem<DT>::BYTES);
+}
+
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 template <int DT>

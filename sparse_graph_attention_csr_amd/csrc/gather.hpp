@@ -135,8 +135,8 @@ __global__ __launch_bounds__(kBlock) void gt_fwd_rows(GtFwdArgs a)
                 kf[u] = frag_zero();
                 vf[u] = frag_zero();
                 if (ok[u] && g.hvalid) {
-                    kf[u] = ldg<DT>(a.K, j * HD + g.col);
-                    vf[u] = ldg<DT>(a.V, j * HD + g.col);
+                    kf[u] = ldg_nbr<DT>(a.K, static_cast<uint32_t>(j), g.col, HD);
+                    vf[u] = ldg_nbr<DT>(a.V, static_cast<uint32_t>(j), g.col, HD);
                 }
             }
             float s[U];
@@ -279,7 +279,7 @@ __device__ __forceinline__ void gat_fwd_one(const GatFwdArgs& a, int64_t ii, int
                 ok[u] = e < nb;
                 const int64_t j = bcast<EPW>(cj, e);
                 xf[u] = frag_zero();
-                if (ok[u] && g.hvalid) xf[u] = ldg<DT>(a.Xt, j * HD + g.col);
+                if (ok[u] && g.hvalid) xf[u] = ldg_nbr<DT>(a.Xt, static_cast<uint32_t>(j), g.col, HD);
             }
             gat_online_step<DT, VEC, G::SPH, U>(st, xf, ok, xs, c1, c2);
         }
@@ -320,7 +320,7 @@ __device__ __forceinline__ void gat_fwd_multi(const GatFwdArgs& a, int64_t first
                 ok[u] = t + u < nb;
                 const int64_t j = __shfl(cj, lead + t + u);
                 xf[u] = frag_zero();
-                if (ok[u] && g.hvalid) xf[u] = ldg<DT>(a.Xt, j * HD + g.col);
+                if (ok[u] && g.hvalid) xf[u] = ldg_nbr<DT>(a.Xt, static_cast<uint32_t>(j), g.col, HD);
             }
             gat_online_step<DT, VEC, G::SPH, U>(st, xf, ok, xs, c1, c2);
         }
@@ -581,7 +581,7 @@ __global__ __launch_bounds__(kBlock) void gt_bwd_rows(GtBwdRowArgs a)
                 kf[u] = frag_zero();
                 d[u] = 0.f;
                 if (e < nb && g.hvalid) {
-                    kf[u] = ldg<DT>(a.K, j * HD + g.col);
+                    kf[u] = ldg_nbr<DT>(a.K, static_cast<uint32_t>(j), g.col, HD);
                     d[u] = __builtin_nontemporal_load(dsr + static_cast<int64_t>(base + e) * a.H);
                 }
             }
@@ -782,6 +782,10 @@ void gat_bwd_rows(GatBwdRowArgs a)
     float at[VEC] = {};
     if (g.hvalid) ld_f32<VEC>(a.att + g.col, at);
     const float h1 = 0.5f * (1.f + a.slope) * kLog2e, h2 = 0.5f * (1.f - a.slope) * kLog2e;
+    // neighbour rows: a padded head's lanes read row 0, column 0
+    const char* const xt_lane =
+        static_cast<const char*>(a.Xt) + (g.hvalid ? g.col * Elem<DT>::BYTES : 0);
+    const uint32_t row_bytes = static_cast<uint32_t>(HD * Elem<DT>::BYTES);
 
     const int64_t n_wunits = SHORT ? (a.n_items - a.n_single + EPW - 1) / EPW : a.n_single;
     const int64_t stride = static_cast<int64_t>(gridDim.x) * kWavesPerBlock;
@@ -804,8 +808,8 @@ void gat_bwd_rows(GatBwdRowArgs a)
 #pragma unroll
                     for (int u = 0; u < U; ++u) {
                         const int e = t + u * EPW + g.sub;
-                        const int64_t j = bcast<EPW>(cj, e < nb ? e : nb - 1);
-                        xf[u] = ldg<DT>(a.Xt, g.hvalid ? j * HD + g.col : 0);
+                        const uint32_t j = bcast<EPW>(cj, e < nb ? e : nb - 1);
+                        xf[u] = ldg_row(xt_lane, g.hvalid ? j : 0u, row_bytes);
                     }
                 };
                 auto step = [&](int t, const Frag (&xf)[U]) {
@@ -864,8 +868,8 @@ void gat_bwd_rows(GatBwdRowArgs a)
                 // row 0; past the last edge the last one is read again), so
                 // each wait needs only the older of two loads.
                 auto fetch = [&](int t) {
-                    const int64_t j = __shfl(cj, lead + (t < nb ? t : nb - 1));
-                    return ldg<DT>(a.Xt, g.hvalid ? j * HD + g.col : 0);
+                    const uint32_t j = __shfl(cj, lead + (t < nb ? t : nb - 1));
+                    return ldg_row(xt_lane, g.hvalid ? j : 0u, row_bytes);
                 };
                 Frag xa = fetch(0);
                 for (int t = 0; t < nb; t += 2) {
@@ -962,8 +966,8 @@ __global__ __launch_bounds__(kBlock) void gt_bwd_cols(GtBwdColArgs a)
                 df[u] = frag_zero();
                 rs[u] = RowStat{0.f, 0.f};
                 if (ok[u] && g.hvalid) {
-                    qf[u] = ldg<DT>(a.Q, i * HD + g.col);
-                    df[u] = ldg<DT>(a.dO, i * HD + g.col);
+                    qf[u] = ldg_nbr<DT>(a.Q, static_cast<uint32_t>(i), g.col, HD);
+                    df[u] = ldg_nbr<DT>(a.dO, static_cast<uint32_t>(i), g.col, HD);
                     rs[u] = a.stats[i * a.H + g.head];
                 }
             }
@@ -1091,7 +1095,7 @@ __global__ __launch_bounds__(kBlock) void gat_bwd_cols(GatBwdColArgs a)
                         zb[u] = 0;
                         if (e < nb && g.hvalid) {
                             const uint32_t* r = rbase + eid * RS;
-                            df[u] = ldg<DT>(a.dO, i * HD + g.col);
+                            df[u] = ldg<DT>(a.dO, i * HD + g.col);   // keeps 7 waves per SIMD
                             pd[u] = rec_pd(r + 2 * hl);
                             zb[u] = __builtin_nontemporal_load(r + zl) >> zsh;
                         }
@@ -1139,7 +1143,7 @@ __global__ __launch_bounds__(kBlock) void gat_bwd_cols(GatBwdColArgs a)
                         zb[u] = 0;
                         if (t + u < nb && g.hvalid) {
                             const uint32_t* r = rbase + eid * RS;
-                            df[u] = ldg<DT>(a.dO, i * HD + g.col);
+                            df[u] = ldg<DT>(a.dO, i * HD + g.col);   // keeps 7 waves per SIMD
                             pd[u] = rec_pd(r + 2 * hl);
                             zb[u] = __builtin_nontemporal_load(r + zl) >> zsh;
                         }
