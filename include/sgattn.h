@@ -242,10 +242,12 @@ int gat_fwd(const sgat_plan* plan, int64_t n, int64_t nnz,
 
 /* Backward of L = sum(out * dout): dx_dst, dx_nbr (input dtype, [n,H,D]) and
  * da (fp32 [H,D]), all overwritten. The CSR pass recomputes alpha_ij from lse,
- * accumulates dx_dst and per-workgroup da partials, and leaves per edge the
- * weight, dE_ij = alpha_ij (dout_i . x_nbr[j] - Delta_i) and the signs of z in
- * the workspace; the transposed-CSR pass reads them and gathers only dout_i
- * for dx_nbr. da is reduced from the partials in fixed order. */
+ * accumulates dx_dst, and leaves per edge the weight, dE_ij = alpha_ij
+ * (dout_i . x_nbr[j] - Delta_i) and the signs of z in the workspace; the
+ * transposed-CSR pass reads them and gathers only dout_i for dx_nbr. da splits
+ * into per-node terms (sum_i x_dst[i] . T_i + sum_j x_nbr[j] . U_j, T and U the
+ * sums of dE times LeakyReLU'(z) the two passes form anyway); both passes write
+ * them as per-workgroup partials, reduced in fixed order. */
 int gat_bwd(const sgat_plan* plan, int64_t n, int64_t nnz,
             const int64_t* rowptr, const int32_t* colidx,
             int H, int D, int dtype, const void* x_dst, const void* x_nbr,
