@@ -33,8 +33,13 @@ struct RowStat { float lse2; float delta; };   // lse * log2(e), Delta
 // forward: online softmax over one row (or chunk)
 // ---------------------------------------------------------------------------
 
-// Online-softmax state of one lane: running max m (base 2), sum l and the
-// weighted accumulator of this lane's VEC channels.
+// a running maximum moves only when passed by more than 2^kLazyLog2 (the
+// weights then stay below 2^8: no overflow risk in fp32 sums)
+constexpr float kLazyLog2 = 8.f;
+
+// Online-softmax state of one lane: reference maximum m (base 2; the running
+// maximum, or in the GATv2 step within 2^kLazyLog2 below it), sum l of
+// exp2(s - m) and the weighted accumulator of this lane's VEC channels.
 template <int VEC>
 struct Online {
     float m = kNegInf, l = 0.f;
@@ -216,21 +221,27 @@ __device__ __forceinline__ void gat_online_step(Online<VEC>& st, const Frag (&xf
         s[u] = ok[u] ? hs : kNegInf;
         mb = fmaxf(mb, s[u]);
     }
-    const float mn = fmaxf(st.m, mb);
-    const float corr = mn == kNegInf ? 1.f : fast_exp2(st.m - mn);
-    st.l *= corr;
+    // Lazy rescaling: m is a reference maximum, moved (and l, acc rescaled)
+    // only when a score passes it by more than 2^kLazyLog2, so the weights
+    // exp2(s - m) stay below 2^kLazyLog2 and most steps skip the rescale;
+    // out = acc / l and lse = m + log2(l) hold for any reference m (while m
+    // is -inf, l and acc are 0 and the factor exp2(-inf) = 0 keeps them so).
+    if (mb > st.m + kLazyLog2) {
+        const float corr = fast_exp2(st.m - mb);
+        st.l *= corr;
 #pragma unroll
-    for (int k = 0; k < VEC; ++k) st.acc[k] *= corr;
+        for (int k = 0; k < VEC; ++k) st.acc[k] *= corr;
+        st.m = mb;
+    }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-        const float p = ok[u] ? fast_exp2(s[u] - mn) : 0.f;
+        const float p = ok[u] ? fast_exp2(s[u] - st.m) : 0.f;
         st.l += p;
         float x[VEC];
         to_f32<DT>(xf[u], x);
 #pragma unroll
         for (int k = 0; k < VEC; ++k) st.acc[k] = fmaf(p, x[k], st.acc[k]);
     }
-    st.m = mn;
 }
 
 template <int DT, int D, int EPW>
