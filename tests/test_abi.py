@@ -194,3 +194,32 @@ def test_binding_refuses_host_tensors_before_any_call(plan):
         B.reduce_fwd(plan, rp, ci, torch.zeros(n, 64), "min", torch.zeros(n, 64), None, None)
     with pytest.raises(ValueError, match="rows"):
         B.gt_fwd(plan, rp, ci, torch.zeros(n + 1, H, D), q, q, q, lse, None)
+
+
+def test_missing_library_raises_without_fallback(tmp_path):
+    """With no built library every entry point raises: there is no CPU path.
+    Run in a child interpreter whose binding points at an empty directory."""
+    import subprocess
+    import sys
+    code = (
+        "import sparse_graph_attention_csr_amd.binding as B\n"
+        f"B._LIB_PATH = {str(tmp_path / 'libsgattn.so')!r}\n"
+        "import numpy as np\n"
+        "for call in (lambda: B.lib(), lambda: B.Plan(np.array([0, 1]), np.array([0], np.int32)),\n"
+        "             lambda: B.gt_fwd(None, None, None, None, None, None, None, None, None)):\n"
+        "    try:\n"
+        "        call()\n"
+        "    except (RuntimeError, ValueError, AttributeError, TypeError):\n"
+        "        pass\n"
+        "    else:\n"
+        "        raise SystemExit('a call succeeded without the library')\n"
+        "try:\n"
+        "    B.lib()\n"
+        "except RuntimeError as e:\n"
+        "    assert 'no fallback' in str(e)\n"
+        "    print('raised')\n")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, "-c", code], cwd=root, capture_output=True, text=True,
+                       timeout=120)
+    assert r.returncode == 0, r.stderr[-2000:]
+    assert r.stdout.strip().endswith("raised")
