@@ -1,4 +1,4 @@
-"""Seeded randomized parity sweep: small graphs of random size and degree mix
+"""Seeded randomized parity sweeps. The gather path: small graphs of random size and degree mix
 (empty rows, single-edge rows, rows just under and over the short-item bound
 and the chunk size, repeated edges), random layouts among those compiled,
 random chunk sizes and GATv2 slopes; the Graph Transformer and GATv2 forward
@@ -6,7 +6,8 @@ and backward of each against the fp64 oracle, every output element.
 
 Bar: the same as the fixed parity cases (max |gpu - oracle| / max |oracle|
 <= 1e-4 for fp32 inputs, <= 2e-2 for bf16), with dXs measured against the
-larger of the dXs and dXt scales (it vanishes for slope 1)."""
+larger of the dXs and dXt scales (it vanishes for slope 1). The tile path:
+random 16x16-block structures with random tile thresholds and layouts."""
 import numpy as np
 import pytest
 
@@ -66,3 +67,55 @@ def test_random_graphs(case):
         assert rel_err(host(got), ref) <= TOL[dt], name
     scale = max(np.abs(gs).max(initial=0.0), np.abs(gt).max(initial=0.0))
     assert np.abs(host(dxs) - gs).max(initial=0.0) <= TOL[dt] * max(scale, 1e-30), "gat.dxs"
+
+
+def random_block_graph(rng):
+    """Random 16x16-block structure: a few blocks dense at random densities
+    (they become tiles above the threshold), scattered edges elsewhere, a
+    ragged node count, some empty rows and repeated edges."""
+    n = int(rng.integers(17, 600))
+    nb = (n + 15) // 16
+    dst, src = [], []
+    for _ in range(int(rng.integers(1, 3 * nb + 2))):
+        br, bc = int(rng.integers(nb)), int(rng.integers(nb))
+        dens = float(rng.choice([0.05, 0.2, 0.5, 0.9, 1.0]))
+        m = rng.random((16, 16)) < dens
+        r_, c_ = np.nonzero(m)
+        r_, c_ = r_ + 16 * br, c_ + 16 * bc
+        ok = (r_ < n) & (c_ < n)
+        dst.append(r_[ok]), src.append(c_[ok])
+    k = int(rng.integers(0, 4 * n))
+    dst.append(rng.integers(0, n, size=k)), src.append(rng.integers(0, n, size=k))
+    dst, src = np.concatenate(dst), np.concatenate(src)
+    rp, ci = I.csr_from_edges(n, dst, src, self_loops=bool(rng.integers(2)), dedup=bool(rng.integers(2)))
+    return rp, ci
+
+
+@pytest.mark.parametrize("case", range(32))
+def test_random_tile_graphs(case):
+    """The 16x16 tile path (bf16 MFMA) on random block structures, random
+    tile thresholds and layouts: forward and backward against the oracle."""
+    import torch
+    rng = np.random.default_rng(7000 + case)
+    rp, ci = random_block_graph(rng)
+    n = rp.size - 1
+    H = int(rng.choice([1, 2, 4, 5, 8]))
+    D = int(rng.choice([32, 64, 128]))
+    tau = int(rng.choice([1, 8, 32, 100]))
+    note(f"random tile case {case}: n={n} nnz={rp[-1]} H={H} D={D} tau={tau}")
+    t = {nm: I.normal_tensor(rng, (n, H, D), I.BF16) for nm in ("q", "k", "v", "dout")}
+    r = Runner(rp, ci, block_sparse=True, tile_min_nnz=tau)
+    B, g = r.B, r.g
+    q, k, v, do = (dev(t[x]) for x in ("q", "k", "v", "dout"))
+    out = torch.empty_like(q)
+    lse = torch.empty((n, H), dtype=torch.float32, device=q.device)
+    B.gt_fwd(g.plan, g.rowptr, g.colidx, q, k, v, out, lse, g.workspace(B.OP_GT_FWD, H, D, B.BF16),
+             use_tiles=True)
+    dq, dk, dv = (torch.empty_like(q) for _ in range(3))
+    B.gt_bwd(g.plan, g.rowptr, g.colidx, q, k, v, out, lse, do, dq, dk, dv,
+             g.workspace(B.OP_GT_BWD, H, D, B.BF16), use_tiles=True)
+    ro, rl = oracle.gt_fwd(rp, ci, t["q"], t["k"], t["v"])
+    rq, rk, rv = oracle.gt_bwd(rp, ci, t["q"], t["k"], t["v"], t["dout"])
+    for name, got, ref in (("out", out, ro), ("lse", lse, rl), ("dq", dq, rq), ("dk", dk, rk),
+                           ("dv", dv, rv)):
+        assert rel_err(host(got), ref) <= TOL["bf16"], name
