@@ -7,7 +7,8 @@ and backward of each against the fp64 oracle, every output element.
 Bar: the same as the fixed parity cases (max |gpu - oracle| / max |oracle|
 <= 1e-4 for fp32 inputs, <= 2e-2 for bf16), with dXs measured against the
 larger of the dXs and dXt scales (it vanishes for slope 1). The tile path:
-random 16x16-block structures with random tile thresholds and layouts."""
+random 16x16-block structures with random tile thresholds and layouts. Min/max
+aggregation: random graphs, widths, dtypes, operations and chunk sizes."""
 import numpy as np
 import pytest
 
@@ -119,3 +120,29 @@ def test_random_tile_graphs(case):
     for name, got, ref in (("out", out, ro), ("lse", lse, rl), ("dq", dq, rq), ("dk", dk, rk),
                            ("dv", dv, rv)):
         assert rel_err(host(got), ref) <= TOL["bf16"], name
+
+
+@pytest.mark.parametrize("case", range(32))
+def test_random_minmax(case):
+    """Min/max aggregation on random graphs, feature widths (any multiple of
+    the fragment up to 2048), dtypes, chunk sizes and tie-heavy or continuous
+    values: values and winners bit-exact, dX to the bar of the fixed cases."""
+    from tests.test_gpu_reduce import run_case
+    rng = np.random.default_rng(5000 + case)
+    rp, ci = random_graph(rng)
+    n = rp.size - 1
+    dt = str(rng.choice(["f32", "bf16"]))
+    vec = 4 if dt == "f32" else 8
+    F = vec * int(rng.integers(1, 2048 // vec + 1))
+    op = str(rng.choice(["min", "max"]))
+    chunk = int(rng.choice([0, 1, 5, 64, 300]))
+    ties = bool(rng.integers(2))
+    note(f"random min/max case {case}: n={n} nnz={rp[-1]} dt={dt} F={F} op={op} chunk={chunk} ties={ties}")
+    x = (rng.integers(-4, 5, size=(n, F)) / 4.0) if ties else rng.standard_normal((n, F))
+    x = x.astype(np.float32)
+    if dt == "bf16":
+        x = I.f32_to_bf16_bits(x)
+    dout = rng.standard_normal((n, F)).astype(np.float32)
+    if dt == "bf16":
+        dout = I.f32_to_bf16_bits(dout)
+    run_case(rp, ci, x, dout, dt, op, chunk)
