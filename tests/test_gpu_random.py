@@ -5,8 +5,10 @@ random chunk sizes and GATv2 slopes; the Graph Transformer and GATv2 forward
 and backward of each against the fp64 oracle, every output element.
 
 Bar: the same as the fixed parity cases (max |gpu - oracle| / max |oracle|
-<= 1e-4 for fp32 inputs, <= 2e-2 for bf16), with dXs measured against the
-larger of the dXs and dXt scales (it vanishes for slope 1). The tile path:
+<= 1e-4 for fp32 inputs, <= 2e-2 for bf16), with GATv2's dXs measured against
+the larger of the dXs and dXt scales (it vanishes for slope 1), and on graphs
+whose rows each have one distinct in-neighbour (where dQ, dK, dXs and da vanish
+exactly) those against the dV or dXt scale. The tile path:
 random 16x16-block structures with random tile thresholds and layouts. Min/max
 aggregation: random graphs, widths, dtypes, operations and chunk sizes."""
 import numpy as np
@@ -54,20 +56,36 @@ def test_random_graphs(case):
     dq, dk, dv = r.gt_bwd(q, k, v, out, lse, do)
     ro, rl = oracle.gt_fwd(rp, ci, t["q"], t["k"], t["v"])
     rq, rk, rv = oracle.gt_bwd(rp, ci, t["q"], t["k"], t["v"], t["dout"])
-    for name, got, ref in (("gt.out", out, ro), ("gt.lse", lse, rl), ("gt.dq", dq, rq),
-                           ("gt.dk", dk, rk), ("gt.dv", dv, rv)):
-        assert rel_err(host(got), ref) <= TOL[dt], name
+    # A graph whose every non-empty row has one distinct in-neighbour gives
+    # equal scores in each row, out = that neighbour's row and dS = dE = 0
+    # exactly: dQ, dK, dXs and da vanish (the oracle returns 0 to fp64
+    # rounding, the library the rounding residue of Delta from its stored
+    # output). There they are checked against the dV / dXt scale instead.
+    degenerate = all(np.unique(ci[rp[i]:rp[i + 1]]).size <= 1 for i in range(n))
+
+    def check(name, got, ref, scale_ref=None):
+        g = host(got)
+        if scale_ref is None:
+            assert rel_err(g, ref) <= TOL[dt], name
+        else:
+            assert np.isfinite(g).all(), name
+            scale = max(np.abs(ref).max(initial=0.0), np.abs(scale_ref).max(initial=0.0), 1e-30)
+            assert np.abs(g - ref).max(initial=0.0) <= TOL[dt] * scale, name
+
+    for name, got, ref in (("gt.out", out, ro), ("gt.lse", lse, rl), ("gt.dv", dv, rv)):
+        check(name, got, ref)
+    check("gt.dq", dq, rq, rv if degenerate else None)
+    check("gt.dk", dk, rk, rv if degenerate else None)
 
     ad = dev(a)
     gout, glse = r.gat_fwd(q, k, ad, slope=slope)
     dxs, dxt, da = r.gat_bwd(q, k, ad, gout, glse, do, slope=slope)
     go, gl = oracle.gat_fwd(rp, ci, t["q"], t["k"], a, slope)
     gs, gt, ga = oracle.gat_bwd(rp, ci, t["q"], t["k"], a, t["dout"], slope)
-    for name, got, ref in (("gat.out", gout, go), ("gat.lse", glse, gl), ("gat.dxt", dxt, gt),
-                           ("gat.da", da, ga)):
-        assert rel_err(host(got), ref) <= TOL[dt], name
-    scale = max(np.abs(gs).max(initial=0.0), np.abs(gt).max(initial=0.0))
-    assert np.abs(host(dxs) - gs).max(initial=0.0) <= TOL[dt] * max(scale, 1e-30), "gat.dxs"
+    for name, got, ref in (("gat.out", gout, go), ("gat.lse", glse, gl), ("gat.dxt", dxt, gt)):
+        check(name, got, ref)
+    check("gat.da", da, ga, gt if degenerate else None)
+    check("gat.dxs", dxs, gs, gt)   # the dXt scale always: dXs vanishes for slope 1 too
 
 
 def random_block_graph(rng):
