@@ -45,8 +45,9 @@ namespace {
 constexpr int unroll_fwd(int epw) { return epw >= 4 ? (SGAT_UNROLL_FWD + 3) / 4 : SGAT_UNROLL_FWD; }
 constexpr int unroll_bwd(int epw) { return epw >= 4 ? (SGAT_UNROLL_BWD + 1) / 2 : SGAT_UNROLL_BWD; }
 // The backward passes take one work unit per wave up to this grid and
-// stride beyond it; every workgroup writes one row of da partials.
-constexpr int kGatBwdMaxBlocks = 1 << 20;
+// stride beyond it; every workgroup writes one row of da partials, so the
+// cap also bounds that workspace (3 * 2^16 rows of H*D floats at most).
+constexpr int kGatBwdMaxBlocks = 1 << 16;
 // da partials summed per run of this many by the first reduction level
 constexpr int kDaRun = 64;
 // above this many partials the reduction takes two levels
