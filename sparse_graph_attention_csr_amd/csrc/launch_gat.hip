@@ -42,7 +42,7 @@ namespace {
 // With several edges per wave side by side, each unrolled step already holds
 // EPW neighbour rows, so fewer steps keep the same bytes in flight with fewer
 // registers.
-constexpr int unroll_fwd(int epw) { return epw >= 4 ? (SGAT_UNROLL_FWD + 3) / 4 : SGAT_UNROLL_FWD; }
+constexpr int unroll_fwd(int epw) { return epw >= 4 ? (SGAT_UNROLL_FWD + 1) / 2 : SGAT_UNROLL_FWD; }
 constexpr int unroll_bwd(int epw) { return epw >= 4 ? (SGAT_UNROLL_BWD + 1) / 2 : SGAT_UNROLL_BWD; }
 // The backward passes take one work unit per wave up to this grid and
 // stride beyond it; every workgroup writes one row of da partials, so the
