@@ -303,6 +303,21 @@ int sgat_trace_clear(void);
 int sgat_trace_count(void);
 int sgat_trace_get(int index, char* name, size_t name_len, float* ms);
 
+/* Bandwidth probes (measurement only; they compute nothing of the layers).
+ * sgat_probe_read streams `bytes` (a multiple of 16, src 16-byte aligned) of
+ * device memory with `blocks` workgroups of 256 lanes, each lane reading 16
+ * bytes per access. sgat_probe_gather reads whole rows of a row-major table of
+ * `rows` rows of `row_bytes` bytes (256, 512 or 1024; table 16-byte aligned) at
+ * the n_idx row indices idx (device int32; indices outside [0, rows) read
+ * nothing), 16 KiB in flight per wave like the attention forward's neighbour
+ * gathers. `sink` is a device uint32 that the probes leave unwritten in
+ * practice (a data-dependent store keeps the loads from being removed). Both
+ * launch through the timing trace as "probe_read" / "probe_gather", so the
+ * achieved rate is bytes / traced time. */
+int sgat_probe_read(const void* src, size_t bytes, uint32_t* sink, int blocks, void* stream);
+int sgat_probe_gather(const void* table, int64_t rows, int row_bytes, const int32_t* idx,
+                      int64_t n_idx, uint32_t* sink, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -92,6 +92,8 @@ _SIGS = {
                           _vp]),
     "reduce_bwd": (_i32, [_vp, _i64, _i64, _vp, _vp, _i32, _i32, _vp, _vp, _vp, _vp, _sz, _vp]),
     "sgat_status_string": (ctypes.c_char_p, [_i32]),
+    "sgat_probe_read": (_i32, [_vp, _sz, _vp, _i32, _vp]),
+    "sgat_probe_gather": (_i32, [_vp, _i64, _i32, _vp, _i64, _vp, _vp]),
     "sgat_trace_enable": (_i32, [_i32]),
     "sgat_trace_only": (_i32, [ctypes.c_char_p]),
     "sgat_trace_clear": (_i32, []),
@@ -396,6 +398,20 @@ def trace_read() -> list:
         _check("sgat_trace_get", lib().sgat_trace_get(i, name, 64, ctypes.byref(ms)))
         out.append((name.value.decode(), float(ms.value)))
     return out
+
+
+def probe_read(buf, sink, blocks: int = 2048, stream=None):
+    """Stream the bytes of a device tensor (sgat_probe_read)."""
+    _check("sgat_probe_read", lib().sgat_probe_read(
+        _ptr(buf), buf.numel() * buf.element_size(), _ptr(sink), int(blocks), _stream(stream)))
+
+
+def probe_gather(table, idx, sink, stream=None):
+    """Gather rows of a 2-D device tensor at device int32 indices (sgat_probe_gather)."""
+    row_bytes = table.shape[1] * table.element_size()
+    _check("sgat_probe_gather", lib().sgat_probe_gather(
+        _ptr(table), table.shape[0], row_bytes, _ptr(idx), idx.numel(), _ptr(sink),
+        _stream(stream)))
 
 
 # ---------------------------------------------------------------------------

@@ -22,7 +22,7 @@ LIB = os.path.join(PKG, "libsgattn.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 SOURCES = ["plan.cpp", "api.cpp", "launch_gt.hip", "launch_gat.hip", "launch_bs.hip",
-           "launch_reduce.hip"]
+           "launch_reduce.hip", "probe.hip"]
 
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++20", "-fPIC", "-Wall", "-Wno-unused-result",
