@@ -71,7 +71,9 @@ typedef enum sgat_status {
     SGAT_HIP_ERROR = 5,           /* a HIP call or kernel launch failed */
     SGAT_NOT_UPLOADED = 6,        /* plan used before sgat_plan_upload */
     SGAT_OUT_OF_HOST_MEMORY = 7,  /* host allocation inside sgat_plan_create failed */
-    SGAT_UNSUPPORTED = 8          /* option not available for this plan (e.g. no tiles built) */
+    SGAT_UNSUPPORTED = 8,         /* option not available for this plan (e.g. no tiles built) */
+    SGAT_SCRATCH_LIMIT = 9        /* gt_fwd_noalloc: the call needs more scratch than the
+                                     library's static array holds */
 } sgat_status;
 
 typedef enum sgat_dtype { SGAT_F32 = 0, SGAT_BF16 = 1 } sgat_dtype;
@@ -213,6 +215,26 @@ int gt_fwd(const sgat_plan* plan, int64_t n, int64_t nnz,
            const int64_t* rowptr, const int32_t* colidx,
            int H, int D, int dtype, const void* Q, const void* K, const void* V,
            void* out, float* lse, void* ws, size_t ws_bytes, int use_tiles, void* stream);
+
+/* gt_fwd without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc). It runs the same kernels as gt_fwd, with the
+ * partial results of split rows in a static device array of
+ * SGAT_NOALLOC_SCRATCH_BYTES that the library owns; each GPU the library runs
+ * on holds one such array until the process ends. The first call on a device
+ * looks the array's address up there (hipGetSymbolAddress, no allocation);
+ * no call allocates or frees anything. Every call on one GPU shares that GPU's
+ * array, so calls that overlap in time on one GPU (on different streams, or
+ * from several threads) race on it and must be serialised by the caller. No
+ * region of it needs to start at zero (each chunk writes its own slot before
+ * the merge reads it). Arguments and results are those of gt_fwd; a call
+ * whose gt_fwd workspace (sgat_workspace_bytes, SGAT_OP_GT_FWD) would exceed
+ * SGAT_NOALLOC_SCRATCH_BYTES returns SGAT_SCRATCH_LIMIT and enqueues nothing. */
+#define SGAT_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+int gt_fwd_noalloc(const sgat_plan* plan, int64_t n, int64_t nnz,
+                   const int64_t* rowptr, const int32_t* colidx,
+                   int H, int D, int dtype, const void* Q, const void* K, const void* V,
+                   void* out, float* lse, int use_tiles, void* stream);
 
 /* Backward of L = sum(out * dout): dQ, dK, dV. Recomputes alpha_ij from lse
  * (the forward's output); nothing per edge is kept from the forward.

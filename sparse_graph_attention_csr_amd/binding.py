@@ -29,7 +29,10 @@ REDUCE_OPS = {"min": REDUCE_MIN, "max": REDUCE_MAX}
 
 STATUS = {0: "OK", 1: "INVALID_ARGUMENT", 2: "INVALID_CSR", 3: "WORKSPACE_TOO_SMALL",
           4: "PLAN_MISMATCH", 5: "HIP_ERROR", 6: "NOT_UPLOADED", 7: "OUT_OF_HOST_MEMORY",
-          8: "UNSUPPORTED"}
+          8: "UNSUPPORTED", 9: "SCRATCH_LIMIT"}
+
+# bytes of the static device scratch gt_fwd_noalloc uses (SGAT_NOALLOC_SCRATCH_BYTES)
+NOALLOC_SCRATCH_BYTES = 32 << 20
 
 WORK_ITEM_DTYPE = np.dtype([("begin", "<i8"), ("len", "<i4"), ("row", "<i4"),
                             ("slot", "<i4"), ("flags", "<i4")])
@@ -82,6 +85,8 @@ _SIGS = {
     "sgat_workspace_bytes": (_i32, [_vp, _i32, _i32, _i32, _i32, ctypes.POINTER(_sz)]),
     "gt_fwd": (_i32, [_vp, _i64, _i64, _vp, _vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp,
                       _vp, _sz, _i32, _vp]),
+    "gt_fwd_noalloc": (_i32, [_vp, _i64, _i64, _vp, _vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp,
+                              _vp, _i32, _vp]),
     "gt_bwd": (_i32, [_vp, _i64, _i64, _vp, _vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp,
                       _vp, _vp, _vp, _vp, _sz, _i32, _vp]),
     "gat_fwd": (_i32, [_vp, _i64, _i64, _vp, _vp, _i32, _i32, _i32, _vp, _vp, _vp, _f, _vp, _vp,
@@ -290,6 +295,20 @@ def gt_fwd(plan: Plan, rowptr, colidx, q, k, v, out, lse, ws, use_tiles=False, s
         plan.handle, plan.n, plan.nnz, _ptr(rowptr), _ptr(colidx), H, D, _dtype_code(q),
         _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),
         _ptr(ws), _ws_bytes(ws), int(bool(use_tiles)), _stream(stream)))
+
+
+def gt_fwd_noalloc(plan: Plan, rowptr, colidx, q, k, v, out, lse, use_tiles=False, stream=None):
+    """gt_fwd with the library's static scratch instead of a workspace (for
+    callers that cannot allocate; calls on one GPU must not overlap)."""
+    import torch
+    n, H, D = _shape(q)
+    dev = _check_call(plan, rowptr, colidx, None, q)
+    for nm, t in (("q", q), ("k", k), ("v", v), ("out", out)):
+        _expect(nm, t, q.shape, q.dtype, dev)
+    _expect("lse", lse, (n, H), torch.float32, dev)
+    _check("gt_fwd_noalloc", lib().gt_fwd_noalloc(
+        plan.handle, plan.n, plan.nnz, _ptr(rowptr), _ptr(colidx), H, D, _dtype_code(q),
+        _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), int(bool(use_tiles)), _stream(stream)))
 
 
 def gt_bwd(plan: Plan, rowptr, colidx, q, k, v, out, lse, dout, dq, dk, dv, ws,

@@ -4,6 +4,7 @@
 
 #include <algorithm>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -180,6 +181,73 @@ int check_ws(const Plan& p, int op, int H, int D, int dt, const void* ws, size_t
 }  // namespace
 }  // namespace sgat
 
+// Static scratch of gt_fwd_noalloc: one copy per GPU, held until the process
+// ends. In host code `scratch` is only a handle for the symbol lookup below;
+// kernels receive the per-device address that hipGetSymbolAddress returns.
+static __device__ __align__(256) unsigned char scratch[SGAT_NOALLOC_SCRATCH_BYTES];
+
+namespace sgat {
+namespace {
+
+constexpr int kMaxDevices = 256;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Address of the scratch array on the device that `s` launches on, looked up
+// once per device with that device current (the caller's current device is
+// restored).
+int scratch_address(hipStream_t s, void** out)
+{
+    int dev = -1;
+    if (hipStreamGetDevice(s, &dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+        return SGAT_HIP_ERROR;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        int cur = -1;
+        if (hipGetDevice(&cur) != hipSuccess) return SGAT_HIP_ERROR;
+        if (cur != dev && hipSetDevice(dev) != hipSuccess) return SGAT_HIP_ERROR;
+        void* p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (cur != dev && hipSetDevice(cur) != hipSuccess) return SGAT_HIP_ERROR;
+        if (e != hipSuccess || !p) return SGAT_HIP_ERROR;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return SGAT_OK;
+}
+
+// gt_fwd with the workspace given as a pointer and size (a caller's buffer,
+// or the static scratch; `noalloc` selects the error for a short one).
+int gt_fwd_impl(const sgat_plan* plan, int64_t n, int64_t nnz, const int64_t* rowptr,
+                const int32_t* colidx, int H, int D, int dtype, const void* Q, const void* K,
+                const void* V, void* out, float* lse, void* ws, size_t ws_bytes, bool noalloc,
+                int use_tiles, hipStream_t stream)
+{
+    int rc = check_common(plan, n, nnz, rowptr, colidx, H, D, dtype);
+    if (rc) return rc;
+    for (const void* t : {Q, K, V, static_cast<const void*>(out)})
+        if ((rc = check_tensor(t, n))) return rc;
+    if (n > 0 && (!lse || !aligned(lse, 4))) return SGAT_INVALID_ARGUMENT;
+    if (use_tiles != 0 && use_tiles != 1) return SGAT_INVALID_ARGUMENT;
+    if (use_tiles && (!plan->p.block_sparse || dtype != SGAT_BF16)) return SGAT_UNSUPPORTED;
+    Layout L;
+    if (noalloc) {
+        L = ws_layout(plan->p, SGAT_OP_GT_FWD, H, D, dtype);
+        if (L.total > SGAT_NOALLOC_SCRATCH_BYTES) return SGAT_SCRATCH_LIMIT;
+        if (n == 0 || use_tiles || L.total == 0) ws = nullptr;   // nothing to look up
+        else if ((rc = scratch_address(stream, &ws))) return rc;
+    } else if ((rc = check_ws(plan->p, SGAT_OP_GT_FWD, H, D, dtype, ws, ws_bytes, L))) {
+        return rc;
+    }
+    if (n == 0) return SGAT_OK;
+    if (use_tiles) return launch_gt_bs_fwd(plan->p, H, D, Q, K, V, out, lse, stream);
+    FwdWs w{at<float>(ws, L.off[0]), at<float>(ws, L.off[1])};
+    return launch_gt_fwd(plan->p, H, D, dtype, colidx, Q, K, V, out, lse, w, stream);
+}
+
+}  // namespace
+}  // namespace sgat
+
 using namespace sgat;
 
 extern "C" {
@@ -196,6 +264,7 @@ const char* sgat_status_string(int st)
     case SGAT_NOT_UPLOADED: return "plan not uploaded";
     case SGAT_OUT_OF_HOST_MEMORY: return "out of host memory";
     case SGAT_UNSUPPORTED: return "unsupported for this plan";
+    case SGAT_SCRATCH_LIMIT: return "needs more than the static scratch (SGAT_NOALLOC_SCRATCH_BYTES)";
     default: return "unknown status";
     }
 }
@@ -238,21 +307,16 @@ int gt_fwd(const sgat_plan* plan, int64_t n, int64_t nnz, const int64_t* rowptr,
            const void* V, void* out, float* lse, void* ws, size_t ws_bytes, int use_tiles,
            void* stream)
 {
-    int rc = check_common(plan, n, nnz, rowptr, colidx, H, D, dtype);
-    if (rc) return rc;
-    for (const void* t : {Q, K, V, static_cast<const void*>(out)})
-        if ((rc = check_tensor(t, n))) return rc;
-    if (n > 0 && (!lse || !aligned(lse, 4))) return SGAT_INVALID_ARGUMENT;
-    if (use_tiles != 0 && use_tiles != 1) return SGAT_INVALID_ARGUMENT;
-    if (use_tiles && (!plan->p.block_sparse || dtype != SGAT_BF16)) return SGAT_UNSUPPORTED;
-    Layout L;
-    if ((rc = check_ws(plan->p, SGAT_OP_GT_FWD, H, D, dtype, ws, ws_bytes, L))) return rc;
-    if (n == 0) return SGAT_OK;
-    if (use_tiles)
-        return launch_gt_bs_fwd(plan->p, H, D, Q, K, V, out, lse, static_cast<hipStream_t>(stream));
-    FwdWs w{at<float>(ws, L.off[0]), at<float>(ws, L.off[1])};
-    return launch_gt_fwd(plan->p, H, D, dtype, colidx, Q, K, V, out, lse, w,
-                         static_cast<hipStream_t>(stream));
+    return gt_fwd_impl(plan, n, nnz, rowptr, colidx, H, D, dtype, Q, K, V, out, lse, ws,
+                       ws_bytes, false, use_tiles, static_cast<hipStream_t>(stream));
+}
+
+int gt_fwd_noalloc(const sgat_plan* plan, int64_t n, int64_t nnz, const int64_t* rowptr,
+                   const int32_t* colidx, int H, int D, int dtype, const void* Q, const void* K,
+                   const void* V, void* out, float* lse, int use_tiles, void* stream)
+{
+    return gt_fwd_impl(plan, n, nnz, rowptr, colidx, H, D, dtype, Q, K, V, out, lse, nullptr,
+                       0, true, use_tiles, static_cast<hipStream_t>(stream));
 }
 
 int gt_bwd(const sgat_plan* plan, int64_t n, int64_t nnz, const int64_t* rowptr,

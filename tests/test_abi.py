@@ -30,7 +30,7 @@ def test_library_exports_every_declared_function():
 
 
 def test_status_strings():
-    for st in range(9):
+    for st in range(10):
         assert B.status_string(st) != "unknown status"
     assert B.status_string(99) == "unknown status"
 
@@ -63,6 +63,24 @@ def test_gt_fwd_argument_checks(plan):
     assert call_gt_fwd(plan, n=5) == 4
     assert call_gt_fwd(plan, nnz=4) == 4
     assert call_gt_fwd(plan) == 6            # not uploaded
+
+
+def test_gt_fwd_noalloc_argument_checks(plan):
+    """The static-scratch variant checks its arguments like gt_fwd, before it
+    looks up the scratch or launches anything."""
+    L = B.lib()
+
+    def call(p=plan, H=2, D=32, dt=0, lse=FAKE, tiles=0):
+        return L.gt_fwd_noalloc(p.handle if p is not None else None, plan.n, plan.nnz,
+                                FAKE, FAKE, H, D, dt, FAKE, FAKE, FAKE, FAKE, lse, tiles, None)
+    assert call(p=None) == 1
+    assert call(H=0) == 1
+    assert call(D=48) == 1
+    assert call(dt=2) == 1
+    assert call() == 6                       # plan not uploaded
+    assert B.NOALLOC_SCRATCH_BYTES == 32 << 20
+    hdr = open(os.path.join(ROOT, "include", "sgattn.h")).read()
+    assert "#define SGAT_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)" in hdr
 
 
 def test_workspace_bytes(plan):

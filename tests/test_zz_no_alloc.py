@@ -1,0 +1,73 @@
+"""gt_fwd_noalloc (the Graph Transformer forward on the library's static
+scratch, for callers that cannot allocate) against gt_fwd with a caller
+workspace, through the C ABI: two calls in a row, the second on a smaller
+graph, so the second reuses the scratch the first left behind. Both run the
+same kernels, so out and lse must agree bit for bit; each is also held to the
+oracle at the fp32 / bf16 bar. A call whose workspace would exceed the
+scratch is refused with SGAT_SCRATCH_LIMIT before any launch."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from sparse_graph_attention_csr_amd import binding as B
+from sparse_graph_attention_csr_amd import inputs as I
+from tests.gpu_util import TOL, dev, host, note, rel_err
+
+pytestmark = pytest.mark.gpu
+
+
+def run_both(rp, ci, dt, H, D, chunk, seed):
+    n = rp.size - 1
+    rng = np.random.default_rng(seed)
+    q, k, v = (I.normal_tensor(rng, (n, H, D), dt) for _ in range(3))
+    g = B.DeviceGraph(rp, ci, chunk=chunk)
+    Q, K, V = dev(q), dev(k), dev(v)
+    ws_bytes = g.plan.workspace_bytes(B.OP_GT_FWD, H, D, B._dtype_code(Q))
+    assert 0 < ws_bytes <= B.NOALLOC_SCRATCH_BYTES, ws_bytes   # the scratch is really used
+    out_a, out_b = torch.empty_like(Q), torch.empty_like(Q)
+    lse_a = torch.empty(n, H, dtype=torch.float32, device=Q.device)
+    lse_b = torch.empty_like(lse_a)
+    B.gt_fwd(g.plan, g.rowptr, g.colidx, Q, K, V, out_a, lse_a,
+             g.workspace(B.OP_GT_FWD, H, D, B._dtype_code(Q)))
+    B.gt_fwd_noalloc(g.plan, g.rowptr, g.colidx, Q, K, V, out_b, lse_b)
+    torch.cuda.synchronize()
+    assert torch.equal(out_a.view(torch.int16) if dt == I.BF16 else out_a.view(torch.int32),
+                       out_b.view(torch.int16) if dt == I.BF16 else out_b.view(torch.int32))
+    assert torch.equal(lse_a.view(torch.int32), lse_b.view(torch.int32))
+    ro, rl = oracle.gt_fwd(rp, ci, q, k, v)
+    assert rel_err(host(out_b), ro) <= TOL[dt]
+    assert rel_err(host(lse_b), rl) <= TOL[dt]
+    return ws_bytes
+
+
+@pytest.mark.parametrize("dt,H,D", [("f32", 4, 32), ("bf16", 8, 64), ("bf16", 4, 128)])
+def test_noalloc_matches_gt_fwd_twice(dt, H, D):
+    note(f"gt_fwd_noalloc dt={dt} H={H} D={D}")
+    rng = np.random.default_rng(11)
+    big = I.random_csr(3000, 24, rng, empty_frac=0.05, dup_frac=0.05, heavy_rows=6,
+                       heavy_deg=2500)
+    small = I.random_csr(200, 10, rng, empty_frac=0.1, heavy_rows=2, heavy_deg=300)
+    first = run_both(*big, dt, H, D, 64, 1)
+    second = run_both(*small, dt, H, D, 64, 2)
+    assert second < first
+
+
+def test_noalloc_refuses_beyond_scratch():
+    note("gt_fwd_noalloc scratch limit")
+    # one row of 5,000 edges split into single-edge chunks: 5,000 slots of
+    # 16 x 128 fp32 accumulators, about 41 MB of workspace
+    deg = 5000
+    rp = np.array([0, deg] + [deg] * 3, dtype=np.int64)
+    ci = (np.arange(deg) % 4).astype(np.int32)
+    n, H, D = 4, 16, 128
+    g = B.DeviceGraph(rp, ci, chunk=1)
+    assert g.plan.workspace_bytes(B.OP_GT_FWD, H, D, B.F32) > B.NOALLOC_SCRATCH_BYTES
+    Q = torch.zeros(n, H, D, dtype=torch.float32, device="cuda")
+    out = torch.full_like(Q, 7.0)
+    lse = torch.empty(n, H, dtype=torch.float32, device="cuda")
+    with pytest.raises(B.SgatError) as e:
+        B.gt_fwd_noalloc(g.plan, g.rowptr, g.colidx, Q, Q, Q, out, lse)
+    assert e.value.status == 9
+    torch.cuda.synchronize()
+    assert bool((out == 7.0).all())          # nothing was launched
