@@ -4,17 +4,26 @@
 
 A step is one forward and one backward pass of the whole fused layer over the
 workload's graph, inputs already resident in device memory. The default
-workload is the Graph Transformer on a Chung-Lu power-law graph
-(N = 200,000, exponent 2.1, mean in-degree 15, in-degree cap 20,000, plus
-self-loops; H = 4, D = 128; bf16 inputs, fp32 accumulation).
+workload is the largest of the five: the super-node stress graph (N =
+2,000,000, Erdos-Renyi background of mean in-degree 10 plus 64 hubs with
+200,000 in-edges and 50,000 out-edges each, self-loops; Graph Transformer,
+H = 8, D = 64; bf16 inputs, fp32 accumulation).
 
 Prints one JSON line. ``value`` is E*H / step time in GEdge.head/s (E counts
-self-loops). ``roofline`` is for the kernel with the largest share of the step:
-algorithmic bytes per launch (the per-edge and per-node traffic model of that
-kernel) over its mean launch time, timed with HIP events recorded by the
-library on the launch stream during the timed steps. ``cpu_baseline`` times
-the fp64 CPU oracle on a bounded sample of the same workload (rows 0..r-1 of
-the CSR, the rest emptied) on this host's cores.
+self-loops), the step timed with a cold cache: 1 GiB is written between
+steps, outside the timing, so no input survives in the Infinity Cache;
+``warm`` holds the same steps run back to back. ``roofline`` is for the
+kernel with the largest share of the step: algorithmic bytes per launch (the
+per-edge and per-node traffic model of that kernel) over its mean launch
+time, timed with HIP events recorded by the library on the launch stream
+during the timed steps, against the 8 TB/s specification and against the
+ceiling this GPU measured in the same run (``hbm_ceiling``: a read-only
+stream and a random gather of rows of the workload's row size, both over
+4 GiB). ``configs`` holds the cold and warm step times of the power-law Graph
+Transformer and GATv2 workloads and of the community workload on the tile
+path, measured in the same run. ``cpu_baseline`` times the fp64 CPU oracle on
+a bounded sample of the headline workload (rows 0..r-1 of the CSR, the rest
+emptied) on this host's cores.
 """
 from __future__ import annotations
 
@@ -31,7 +40,10 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK = 2.5e15   # dense bf16 matrix-core flop/s
-DEFAULT_WORKLOAD = "gt_powerlaw200k_h4d128_bf16"
+DEFAULT_WORKLOAD = "gt_hubs2m_h8d64_bf16"
+# timed beside the default workload in the same run: (workload, tile path)
+EXTRA_CONFIGS = [("gt_powerlaw200k_h4d128_bf16", False), ("gatv2_powerlaw500k_h2d64_bf16", False),
+                 ("gt_community262k_h4d128_bf16", True)]
 _CSRC = "sparse_graph_attention_csr_amd/csrc/"
 # the sources each kernel family is compiled from (a counter summary is valid
 # only for the sources it was taken on)
@@ -138,8 +150,24 @@ def row_item_split(plan) -> dict:
             "short_items": int(ln.size - first_short), "short_edges": int(ln[first_short:].sum())}
 
 
+# sgat_plan_opts.edge_order 0: the Graph Transformer backward hands dS over
+# in transposed order when it takes more than this many bytes
+DS_TRANSPOSED_BYTES = 128 << 20
+
+
+def gt_ds_transposed(plan, H: int) -> bool:
+    """Whether the library's Graph Transformer backward keeps dS in
+    transposed order for this plan and H (the rule documented with
+    sgat_plan_opts.edge_order)."""
+    from sparse_graph_attention_csr_amd import binding as B
+    if plan.edge_order == 1 or plan.export(B.ARR_ROW_TPOS).size == 0:
+        return False
+    return plan.edge_order == 2 or plan.nnz * H * 4 > DS_TRANSPOSED_BYTES
+
+
 def algorithmic_bytes(kernel: str, n: int, e: int, H: int, D: int, b: int,
-                      tw: dict | None = None, split: dict | None = None) -> int | None:
+                      tw: dict | None = None, split: dict | None = None,
+                      tpos: bool = False) -> int | None:
     """Bytes a kernel must move: neighbour-row gathers per edge plus the
     per-node reads and writes of its own rows (R = H*D*b bytes per node row).
     The GATv2 CSR backward pass runs as two kernels when a wavefront holds
@@ -147,7 +175,9 @@ def algorithmic_bytes(kernel: str, n: int, e: int, H: int, D: int, b: int,
     is charged its own edges and items (an item reads and writes its
     destination's row data like a node). The per-workgroup da partials of
     the GATv2 backward (H*D*4 bytes each, under 1% of either pass) are not
-    counted."""
+    counted. With `tpos` the Graph Transformer backward hands dS over in
+    transposed order: its transposed pass reads no CSR edge ids and its CSR
+    pass reads each edge's transposed position instead."""
     R = H * D * b
     if kernel in ("gat_bwd_rows", "gat_bwd_rows_short") and split is not None:
         which = "short" if kernel.endswith("_short") else "long"
@@ -176,9 +206,9 @@ def algorithmic_bytes(kernel: str, n: int, e: int, H: int, D: int, b: int,
         "gt_bwd_delta": (0, 2 * R + 12 * H),
         # Q_i, dO_i, (lse_i, Delta_i), rowidx, edge id read and dS written per edge;
         # K_j, V_j read, dK_j, dV_j written per node
-        "gt_bwd_cols": (2 * R + 12 * H + 8, 4 * R + 8),
-        # K_j, colidx, dS per edge; dQ_i written per node
-        "gt_bwd_rows": (R + 4 + 4 * H, R + 8),
+        "gt_bwd_cols": (2 * R + 12 * H + (4 if tpos else 8), 4 * R + 8),
+        # K_j, colidx, dS (and with tpos its position) per edge; dQ_i written per node
+        "gt_bwd_rows": (R + (8 if tpos else 4) + 4 * H, R + 8),
         # Xt_j and colidx per edge; Xs_i read, out_i, lse_i written
         "gat_fwd_rows": (R + 4, 2 * R + 4 * H + 8),
         # Xt_j, colidx read and the edge record written per edge; Xs_i, dO_i,
@@ -409,6 +439,306 @@ def compare_unfused(spec, g, fused_step, fused_owned, inputs, fused_out, bwd, fu
             "output_max_rel_diff": diff}
 
 
+def hbm_ceiling(dev, row_bytes: int, gib: float) -> dict:
+    """What this GPU's memory delivers, measured with the library's probes:
+    a read-only stream over `gib` GiB (the best of three grid sizes) and a
+    gather of whole rows of `row_bytes` bytes at uniform random indices over a
+    `gib` GiB table (a footprint no cache holds, like the hub workload's K and
+    V), each the best of 5 launches after one warm-up."""
+    import torch
+
+    from sparse_graph_attention_csr_amd import binding as B
+
+    def best(fn):
+        B.trace_clear()
+        B.trace_enable(True)
+        for _ in range(6):
+            fn()
+        torch.cuda.synchronize()
+        B.trace_enable(False)
+        ms = [t for _, t in B.trace_read()][1:]
+        B.trace_clear()
+        return min(ms)
+
+    sink = torch.zeros(4, dtype=torch.int32, device=dev)
+    nb = int(gib * (1 << 30)) // 16 * 16
+    buf = torch.ones(nb // 4, dtype=torch.int32, device=dev)
+    read = {blocks: nb / (best(lambda: B.probe_read(buf, sink, blocks)) * 1e-3) / 1e9
+            for blocks in (16384, 32768, 65536)}
+    del buf
+    rb = row_bytes if row_bytes in (256, 512, 1024) else 1024
+    rows = nb // rb
+    table = torch.ones(rows, rb // 4, dtype=torch.int32, device=dev)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(0)
+    n_idx = 64 << 20
+    idx = torch.randint(0, rows, (n_idx,), dtype=torch.int32, device=dev, generator=gen)
+    gather = n_idx * rb / (best(lambda: B.probe_gather(table, idx, sink)) * 1e-3) / 1e9
+    del table, idx
+    torch.cuda.empty_cache()
+    top = max(read, key=read.get)
+    return {"stream_read_gbs": round(read[top], 1), "stream_read_blocks": top,
+            "gather_gbs": round(gather, 1), "gather_row_bytes": rb,
+            "footprint_gib": gib, "spec_gbs": HBM_PEAK_GBS}
+
+
+def edge_handoff_bytes(spec, n_e: int, H: int, D: int, b: int, tw: dict | None) -> int:
+    """Bytes of the per-edge values the first backward pass leaves in the
+    workspace for the second: dS per (edge, head) for the Graph Transformer
+    gather path, the (p, dE, signs) record per edge for GATv2, P and dS per
+    (tile, head) and per (residual edge, head) on the tile path."""
+    if spec.op == "reduce" or spec.passes != "fwd+bwd":
+        return 0
+    if tw:
+        return tw["tiles"] * H * 1024 + tw["residual_edges"] * H * 4
+    if spec.op == "gt":
+        return n_e * H * 4
+    return n_e * gat_record_bytes(H, D, b)
+
+
+class Bench:
+    """One workload set up on the device: its plan, resident inputs, outputs,
+    workspaces and the step closure."""
+
+    def __init__(self, name: str, dev, chunk: int = 0, tiles: bool = False, reorder: str = "none",
+                 locality: int = 0, cache_dir: str = ""):
+        import numpy as np
+        import torch
+
+        from sparse_graph_attention_csr_amd import binding as B
+        from sparse_graph_attention_csr_amd import inputs as I
+
+        self.name = name
+        self.spec = spec = I.WORKLOADS[name]
+        w = load_workload(name, cache_dir)
+        if reorder != "none":
+            w = I.relabel(w, I.node_order(w["rowptr"], w["colidx"], reorder))
+        self.w = w
+        rp, ci = w["rowptr"], w["colidx"]
+        self.n, self.e = n, e = rp.size - 1, int(rp[-1])
+        self.H, self.D = H, D = spec.heads, spec.dim
+        self.dt = dt = B.BF16 if spec.dtype == I.BF16 else B.F32
+        self.nbytes = 2 if dt == B.BF16 else 4
+        self.tiles = tiles
+
+        t0 = time.perf_counter()
+        g = self.g = B.DeviceGraph(rp, ci, device=dev, chunk=chunk, block_sparse=tiles,
+                                   locality=bool(locality))
+        self.tw = tile_work(g.plan) if tiles else None
+        self.split = (row_item_split(g.plan)
+                      if spec.op == "gat" and edge_groups(H, D, self.nbytes) > 1 else None)
+        self.tpos = spec.op == "gt" and not tiles and gt_ds_transposed(g.plan, H)
+        torch.cuda.synchronize()
+        self.plan_ms = (time.perf_counter() - t0) * 1e3
+
+        def todev(a):
+            if a.dtype == np.uint16:
+                return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+            return torch.from_numpy(a).to(dev)
+
+        bwd = self.bwd = spec.passes == "fwd+bwd"
+        lse = torch.empty(n, H, dtype=torch.float32, device=dev) if spec.op != "reduce" else None
+        if spec.op == "reduce":
+            X = todev(w["x"])
+            out = torch.empty_like(X)
+            arg = torch.empty((n, D), dtype=torch.int32, device=dev) if bwd else None
+            wsf = g.workspace(B.OP_REDUCE_FWD, 1, D, dt)
+            if bwd:
+                dO = todev(w["dout"])
+                dX = torch.empty_like(X)
+                wsb = g.workspace(B.OP_REDUCE_BWD, 1, D, dt)
+            outs = [out] + ([arg, dX] if bwd else [])
+            inputs = [X] + ([dO] if bwd else [])
+
+            def step():
+                B.reduce_fwd(g.plan, g.rowptr, g.colidx, X, "min", out, arg, wsf)
+                if bwd:
+                    B.reduce_bwd(g.plan, g.rowptr, g.colidx, arg, dO, dX, wsb)
+        elif spec.op == "gt":
+            Q, K, V = todev(w["q"]), todev(w["k"]), todev(w["v"])
+            out = torch.empty_like(Q)
+            wsf = g.workspace(B.OP_GT_FWD, H, D, dt)
+            if bwd:
+                dO = todev(w["dout"])
+                dQ, dK, dV = (torch.empty_like(Q) for _ in range(3))
+                wsb = g.workspace(B.OP_GT_BWD, H, D, dt)
+            outs = [out, lse] + ([dQ, dK, dV] if bwd else [])
+            inputs = [Q, K, V] + ([dO] if bwd else [])
+
+            def step():
+                B.gt_fwd(g.plan, g.rowptr, g.colidx, Q, K, V, out, lse, wsf, use_tiles=tiles)
+                if bwd:
+                    B.gt_bwd(g.plan, g.rowptr, g.colidx, Q, K, V, out, lse, dO, dQ, dK, dV, wsb,
+                             use_tiles=tiles)
+        else:
+            Xs, Xt = todev(w["xs"]), todev(w["xt"])
+            A = torch.from_numpy(w["a"]).to(dev)
+            out = torch.empty_like(Xs)
+            wsf = g.workspace(B.OP_GAT_FWD, H, D, dt)
+            if bwd:
+                dO = todev(w["dout"])
+                dXs, dXt = torch.empty_like(Xs), torch.empty_like(Xs)
+                dA = torch.empty(H, D, dtype=torch.float32, device=dev)
+                wsb = g.workspace(B.OP_GAT_BWD, H, D, dt)
+            outs = [out, lse] + ([dXs, dXt, dA] if bwd else [])
+            inputs = [Xs, Xt, A] + ([dO] if bwd else [])
+
+            def step():
+                B.gat_fwd(g.plan, g.rowptr, g.colidx, Xs, Xt, A, 0.2, out, lse, wsf)
+                if bwd:
+                    B.gat_bwd(g.plan, g.rowptr, g.colidx, Xs, Xt, A, 0.2, out, lse, dO, dXs, dXt,
+                              dA, wsb)
+        self.step, self.out, self.inputs = step, out, inputs
+        self.ws = [wsf] + ([wsb] if bwd else [])
+        self.owned = outs + self.ws
+
+        def nb_(t):
+            return t.numel() * t.element_size()
+        self.memory = {
+            "inputs_bytes": sum(nb_(t) for t in inputs),
+            "outputs_bytes": sum(nb_(t) for t in outs),
+            "plan_bytes": nb_(g.plan_buf),
+            "workspace_bytes": {"fwd": g.plan.workspace_bytes(
+                                    B.OP_REDUCE_FWD if spec.op == "reduce" else
+                                    B.OP_GT_FWD if spec.op == "gt" else B.OP_GAT_FWD,
+                                    1 if spec.op == "reduce" else H, D, dt)},
+            "edge_handoff_bytes": edge_handoff_bytes(spec, e, H, D, self.nbytes, self.tw),
+        }
+        if bwd:
+            self.memory["workspace_bytes"]["bwd"] = g.plan.workspace_bytes(
+                B.OP_REDUCE_BWD if spec.op == "reduce" else
+                B.OP_GT_BWD if spec.op == "gt" else B.OP_GAT_BWD,
+                1 if spec.op == "reduce" else H, D, dt)
+
+    def kernel_table(self, steps: int) -> dict:
+        """Every kernel timed with events over `steps` untimed steps."""
+        import torch
+
+        from sparse_graph_attention_csr_amd import binding as B
+        B.trace_clear()
+        B.trace_enable(True)
+        for _ in range(steps):
+            self.step()
+        torch.cuda.synchronize()
+        B.trace_enable(False)
+        recs = B.trace_read()
+        B.trace_clear()
+        per = {}
+        for name, ms in recs:
+            d = per.setdefault(name, [0.0, 0])
+            d[0] += ms
+            d[1] += 1
+        total = max(sum(v[0] for v in per.values()), 1e-12)
+        kernels = {}
+        for name, (tot, cnt) in per.items():
+            avg = tot / cnt
+            ab = algorithmic_bytes(name, self.n, self.e, self.H, self.D, self.nbytes, self.tw,
+                                   self.split, self.tpos)
+            k = kernels[name] = {"ms": round(avg, 4), "launches_per_step": cnt / steps,
+                                 "share": round(tot / total, 4)}
+            if ab is not None:
+                k["algorithmic_bytes"] = ab
+                k["achieved_gbs"] = round(ab / (avg * 1e-3) / 1e9, 1)
+            fl = mfma_flops(name, self.H, self.D, self.tw)
+            if fl is not None:
+                k["mfma_tflops"] = round(fl / (avg * 1e-3) / 1e12, 2)
+                k["mfma_utilisation"] = round(fl / (avg * 1e-3) / MFMA_BF16_PEAK, 5)
+        return kernels
+
+    def timed(self, steps: int, dom: str, flush_buf) -> dict:
+        """The timed regions. Cold: K steps, each bracketed by events on the
+        launch stream, with `flush_buf` (1 GiB) written before each step
+        outside its events; warm: K steps back to back between two
+        synchronisations. The dominant kernel's launches carry events in both
+        (the library's trace restricted to that kernel)."""
+        import torch
+
+        from sparse_graph_attention_csr_amd import binding as B
+        B.trace_clear()
+        B.trace_only(dom)
+        B.trace_enable(True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        evs = []
+        for _ in range(steps):
+            flush_buf.fill_(1.0)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            self.step()
+            b.record()
+            evs.append((a, b))
+        torch.cuda.synchronize()
+        cold_wall = time.perf_counter() - t0
+        cold = [a.elapsed_time(b) for a, b in evs]
+        n_cold = B.trace_read()
+        B.trace_clear()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            self.step()
+        torch.cuda.synchronize()
+        warm_ms = (time.perf_counter() - t0) * 1e3 / steps
+        n_warm = B.trace_read()
+        B.trace_enable(False)
+        B.trace_only(None)
+        B.trace_clear()
+        dom_cold = [ms for name, ms in n_cold if name == dom]
+        dom_warm = [ms for name, ms in n_warm if name == dom]
+        return {"cold_ms": sum(cold) / steps, "cold_wall_s": cold_wall,
+                "cold_median_ms": sorted(cold)[len(cold) // 2], "warm_ms": warm_ms,
+                "dom_ms": sum(dom_cold + dom_warm) / len(dom_cold + dom_warm),
+                "dom_cold_ms": sum(dom_cold) / len(dom_cold),
+                "dom_warm_ms": sum(dom_warm) / len(dom_warm)}
+
+    def rate(self, ms: float) -> float:
+        return self.e * self.H / (ms * 1e-3) / 1e9
+
+    def run(self, steps: int, warmup: int, flush_buf, ceiling: dict | None) -> dict:
+        import torch
+        for _ in range(warmup):
+            self.step()
+        torch.cuda.synchronize()
+        kernels = self.kernel_table(steps)
+        dom = max((k for k in kernels if "algorithmic_bytes" in kernels[k]),
+                  key=lambda k: kernels[k]["ms"] * kernels[k]["launches_per_step"])
+        t = self.timed(steps, dom, flush_buf)
+        dk = kernels[dom]
+        achieved = dk["algorithmic_bytes"] / (t["dom_ms"] * 1e-3) / 1e9
+        roof = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1),
+                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": read_traffic(dom, self.name),
+                "algorithmic_bytes": dk["algorithmic_bytes"], "kernel_ms": round(t["dom_ms"], 4),
+                "kernel_ms_cold": round(t["dom_cold_ms"], 4),
+                "kernel_ms_warm": round(t["dom_warm_ms"], 4),
+                # algorithmic bytes over time above the specification can only
+                # mean that caches served part of the modelled gathers
+                "cache_served": achieved > HBM_PEAK_GBS}
+        if ceiling:
+            roof["ceiling_gbs"] = ceiling["gather_gbs"]
+            roof["frac_of_ceiling"] = round(achieved / ceiling["gather_gbs"], 4)
+        if roof["traffic"] is not None:
+            # the counter-measured bytes (L2 misses, Infinity Cache hits included) over the
+            # same kernel's time: what the kernel actually pulled through the fabric
+            tr = roof["traffic"] / (t["dom_ms"] * 1e-3) / 1e9
+            roof["traffic_gbs"] = round(tr, 1)
+            roof["traffic_frac"] = round(tr / HBM_PEAK_GBS, 4)
+        step_bytes = sum(k["algorithmic_bytes"] * k["launches_per_step"]
+                         for k in kernels.values() if "algorithmic_bytes" in k)
+        step_gbs = step_bytes / (t["cold_ms"] * 1e-3) / 1e9
+        return {"ms_per_step": t["cold_ms"], "cold_median_ms": t["cold_median_ms"],
+                "cold_wall_s": t["cold_wall_s"], "warm_ms": t["warm_ms"], "roofline": roof,
+                "kernels": kernels,
+                "step_model": {"bytes": step_bytes, "gbs": round(step_gbs, 1),
+                               "frac": round(step_gbs / HBM_PEAK_GBS, 4),
+                               "cache_served": step_gbs > HBM_PEAK_GBS}}
+
+    def release(self):
+        import torch
+        for a in ("g", "step", "out", "inputs", "ws", "owned"):
+            setattr(self, a, None)
+        torch.cuda.empty_cache()
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -428,9 +758,15 @@ def main():
                     help="also time the unfused PyTorch formulation (bench_unfused.py) and "
                          "report latency and peak-memory ratios")
     ap.add_argument("--step-times", action="store_true",
-                    help="also time each step alone, warm and with the Infinity Cache flushed "
-                         "between steps (median, min); off by default so that a profile of the "
-                         "default command holds warm launches only")
+                    help="also time each step alone, warm and cold, and report median and "
+                         "minimum over the steps")
+    ap.add_argument("--extra", default="auto",
+                    help="workloads timed beside the headline in the same run: 'auto' (the "
+                         "power-law GT and GATv2 workloads and the community workload on tiles "
+                         "when the headline is the default), 'none', or a comma list of names "
+                         "(a name ending in ':tiles' runs on the tile path)")
+    ap.add_argument("--probe-gib", type=float, default=4.0,
+                    help="footprint of the memory-ceiling probes (0: skip them)")
     ap.add_argument("--cache-dir", default="",
                     help="keep the generated workload arrays here (.npz) and reuse them on the "
                          "next run (inputs only; the timed work is unchanged)")
@@ -443,11 +779,9 @@ def main():
               "(run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
 
-    import numpy as np
     import torch
 
     from sparse_graph_attention_csr_amd import binding as B
-    from sparse_graph_attention_csr_amd import inputs as I
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -461,171 +795,20 @@ def main():
         print(json.dumps({"copy_probe_bytes_read": nb, "copy_probe_bytes_written": nb,
                           "launches": 3}), flush=True)
         return
+    from sparse_graph_attention_csr_amd import inputs as I
     spec = I.WORKLOADS[args.workload]
-    w = load_workload(args.workload, args.cache_dir)
-    if args.reorder != "none":
-        w = I.relabel(w, I.node_order(w["rowptr"], w["colidx"], args.reorder))
-    rp, ci = w["rowptr"], w["colidx"]
-    n, e = rp.size - 1, int(rp[-1])
-    H, D = spec.heads, spec.dim
-    dt = B.BF16 if spec.dtype == I.BF16 else B.F32
-    nbytes = 2 if dt == B.BF16 else 4
+    row_bytes = spec.heads * spec.dim * (2 if spec.dtype == I.BF16 else 4)
+    ceiling = hbm_ceiling(dev, row_bytes, args.probe_gib) if args.probe_gib > 0 else None
+    # 1 GiB written between cold steps (outside their timing)
+    flush_buf = torch.empty(1 << 28, dtype=torch.float32, device=dev)
 
-    t0 = time.perf_counter()
-    g = B.DeviceGraph(rp, ci, device=dev, chunk=args.chunk, block_sparse=args.tiles,
-                      locality=bool(args.locality))
-    tw = tile_work(g.plan) if args.tiles else None
-    split = (row_item_split(g.plan)
-             if spec.op == "gat" and edge_groups(H, D, nbytes) > 1 else None)
-    torch.cuda.synchronize()
-    plan_ms = (time.perf_counter() - t0) * 1e3
-
-    def todev(a):
-        if a.dtype == np.uint16:
-            return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
-        return torch.from_numpy(a).to(dev)
-
-    lse = torch.empty(n, H, dtype=torch.float32, device=dev) if spec.op != "reduce" else None
-    if spec.op == "reduce":
-        X = todev(w["x"])
-        out = torch.empty_like(X)
-        bwd = spec.passes == "fwd+bwd"
-        arg = torch.empty((n, D), dtype=torch.int32, device=dev) if bwd else None
-        wsf = g.workspace(B.OP_REDUCE_FWD, 1, D, dt)
-        if bwd:
-            dO = todev(w["dout"])
-            dX = torch.empty_like(X)
-            wsb = g.workspace(B.OP_REDUCE_BWD, 1, D, dt)
-        owned = [out, wsf] + ([arg, dX, wsb] if bwd else [])
-        inputs = [X] + ([dO] if bwd else [])
-
-        def step():
-            B.reduce_fwd(g.plan, g.rowptr, g.colidx, X, "min", out, arg, wsf)
-            if bwd:
-                B.reduce_bwd(g.plan, g.rowptr, g.colidx, arg, dO, dX, wsb)
-    elif spec.op == "gt":
-        Q, K, V = todev(w["q"]), todev(w["k"]), todev(w["v"])
-        out = torch.empty_like(Q)
-        wsf = g.workspace(B.OP_GT_FWD, H, D, dt)
-        bwd = spec.passes == "fwd+bwd"
-        if bwd:
-            dO = todev(w["dout"])
-            dQ, dK, dV = (torch.empty_like(Q) for _ in range(3))
-            wsb = g.workspace(B.OP_GT_BWD, H, D, dt)
-
-        owned = [out, lse, wsf] + ([dQ, dK, dV, wsb] if bwd else [])
-        inputs = [Q, K, V] + ([dO] if bwd else [])
-
-        def step():
-            B.gt_fwd(g.plan, g.rowptr, g.colidx, Q, K, V, out, lse, wsf, use_tiles=args.tiles)
-            if bwd:
-                B.gt_bwd(g.plan, g.rowptr, g.colidx, Q, K, V, out, lse, dO, dQ, dK, dV, wsb,
-                         use_tiles=args.tiles)
-    else:
-        Xs, Xt = todev(w["xs"]), todev(w["xt"])
-        A = torch.from_numpy(w["a"]).to(dev)
-        out = torch.empty_like(Xs)
-        wsf = g.workspace(B.OP_GAT_FWD, H, D, dt)
-        bwd = spec.passes == "fwd+bwd"
-        if bwd:
-            dO = todev(w["dout"])
-            dXs, dXt = torch.empty_like(Xs), torch.empty_like(Xs)
-            dA = torch.empty(H, D, dtype=torch.float32, device=dev)
-            wsb = g.workspace(B.OP_GAT_BWD, H, D, dt)
-
-        owned = [out, lse, wsf] + ([dXs, dXt, dA, wsb] if bwd else [])
-        inputs = [Xs, Xt, A] + ([dO] if bwd else [])
-
-        def step():
-            B.gat_fwd(g.plan, g.rowptr, g.colidx, Xs, Xt, A, 0.2, out, lse, wsf)
-            if bwd:
-                B.gat_bwd(g.plan, g.rowptr, g.colidx, Xs, Xt, A, 0.2, out, lse, dO, dXs, dXt,
-                          dA, wsb)
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-
-    # Every kernel timed with events over K untimed steps: the per-kernel
-    # table and the dominant kernel. An event pair around each of a step's
-    # 7-9 launches costs a few microseconds apiece, so the timed steps below
-    # bracket only the dominant kernel.
-    B.trace_clear()
-    B.trace_enable(True)
-    for _ in range(args.steps):
-        step()
-    torch.cuda.synchronize()
-    B.trace_enable(False)
-    recs = B.trace_read()
-    B.trace_clear()
-
-    steps_ms = None
-    if args.step_times:
-        # the same steps timed one by one, warm and then cold: 1 GiB written
-        # between steps (outside the timing) leaves none of the inputs in the
-        # Infinity Cache
-        steps_ms = {"warm": per_step_ms(step, args.steps)}
-        flush_buf = torch.empty(1 << 28, dtype=torch.float32, device=dev)
-        steps_ms["cold"] = per_step_ms(step, args.steps, flush=lambda: flush_buf.fill_(1.0))
-        del flush_buf
-        for v in steps_ms.values():
-            v["value"] = round(e * H / (v["median"] / 1e3) / 1e9, 4)
-
-    per = {}
-    for name, ms in recs:
-        d = per.setdefault(name, [0.0, 0])
-        d[0] += ms
-        d[1] += 1
-    kernels = {}
-    for name, (tot, cnt) in per.items():
-        avg = tot / cnt
-        ab = algorithmic_bytes(name, n, e, H, D, nbytes, tw, split)
-        kernels[name] = {"ms": round(avg, 4), "launches_per_step": cnt / args.steps,
-                         "share": round(tot / max(sum(v[0] for v in per.values()), 1e-12), 4)}
-        if ab is not None:
-            kernels[name]["algorithmic_bytes"] = ab
-            kernels[name]["achieved_gbs"] = round(ab / (avg * 1e-3) / 1e9, 1)
-        fl = mfma_flops(name, H, D, tw)
-        if fl is not None:
-            kernels[name]["mfma_tflops"] = round(fl / (avg * 1e-3) / 1e12, 2)
-            kernels[name]["mfma_utilisation"] = round(fl / (avg * 1e-3) / MFMA_BF16_PEAK, 5)
-    dom = max((k for k in kernels if "algorithmic_bytes" in kernels[k]),
-              key=lambda k: kernels[k]["ms"] * kernels[k]["launches_per_step"])
-    dk = kernels[dom]
-
-    # the timed region: K steps between two synchronisations, with events
-    # around the dominant kernel's launches only
-    B.trace_only(dom)
-    B.trace_enable(True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-    B.trace_enable(False)
-    B.trace_only(None)
-    live = [ms for name, ms in B.trace_read() if name == dom]
-    B.trace_clear()
-    ms_per_step = elapsed * 1e3 / args.steps
-    value = e * H / (ms_per_step / 1e3) / 1e9
-    dom_ms = sum(live) / len(live)
-
-    achieved = round(dk["algorithmic_bytes"] / (dom_ms * 1e-3) / 1e9, 1)
-    traffic = read_traffic(dom, args.workload)
-    roofline = {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                "algorithmic_bytes": dk["algorithmic_bytes"], "kernel_ms": round(dom_ms, 4)}
-    if traffic is not None:
-        # the counter-measured bytes (L2 misses, Infinity Cache hits included) over the
-        # same kernel's time: what the kernel actually pulled through the fabric
-        tr = traffic / (dom_ms * 1e-3) / 1e9
-        roofline["traffic_gbs"] = round(tr, 1)
-        roofline["traffic_frac"] = round(tr / HBM_PEAK_GBS, 4)
-
+    hb = Bench(args.workload, dev, chunk=args.chunk, tiles=args.tiles, reorder=args.reorder,
+               locality=args.locality, cache_dir=args.cache_dir)
+    r = hb.run(args.steps, args.warmup, flush_buf, ceiling)
+    ms_per_step = r["ms_per_step"]
     line = {
         "metric": "fused graph-attn fwd+bwd GEdge\u00b7head/s; achieved HBM GB/s vs MI355X peak",
-        "value": round(value, 4),
+        "value": round(hb.rate(ms_per_step), 4),
         "unit": "GEdge\u00b7head/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -634,23 +817,62 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if dt == B.BF16 else "f32",
+        "dtype": "bf16" if hb.dt == B.BF16 else "f32",
         "data": "synthetic (seeded generator, seed 0)",
-        "config": {"workload": args.workload, "graph": spec.graph, "nodes": n, "edges": e,
-                   "heads": H, "head_dim": D, "passes": spec.passes,
-                   "chunk": g.plan.stats()["chunk"], "tiles": bool(args.tiles),
-                   "reorder": args.reorder, "locality": args.locality},
-        "roofline": roofline,
-        "kernels": kernels,
-        "plan_ms": round(plan_ms, 1),
+        "config": {"workload": args.workload, "graph": spec.graph, "nodes": hb.n,
+                   "edges": hb.e, "heads": hb.H, "head_dim": hb.D, "passes": spec.passes,
+                   "chunk": hb.g.plan.stats()["chunk"], "tiles": bool(args.tiles),
+                   "reorder": args.reorder, "locality": args.locality,
+                   "ds_order": "transposed" if hb.tpos else "csr",
+                   "timing": "cold: 1 GiB written between steps, outside the timing"},
+        "warm": {"ms_per_step": round(r["warm_ms"], 4), "value": round(hb.rate(r["warm_ms"]), 4)},
+        "roofline": r["roofline"],
+        "hbm_ceiling": ceiling,
+        "step_model": r["step_model"],
+        "memory": hb.memory,
+        "kernels": r["kernels"],
+        "plan_ms": round(hb.plan_ms, 1),
     }
-    if steps_ms is not None:
-        line["steps_ms"] = steps_ms
+    if args.step_times:
+        line["steps_ms"] = {"warm": per_step_ms(hb.step, args.steps),
+                            "cold": per_step_ms(hb.step, args.steps,
+                                                flush=lambda: flush_buf.fill_(1.0))}
+        for v in line["steps_ms"].values():
+            v["value"] = round(hb.rate(v["median"]), 4)
     if args.compare_unfused:
-        line["unfused"] = compare_unfused(spec, g, step, owned + [g.plan_buf], inputs, out,
-                                          bwd, ms_per_step, args.steps, args.warmup)
+        line["unfused"] = compare_unfused(spec, hb.g, hb.step, hb.owned + [hb.g.plan_buf],
+                                          hb.inputs, hb.out, hb.bwd, r["warm_ms"], args.steps,
+                                          args.warmup)
+    w_head = hb.w
+    hb.release()
+
+    extra = args.extra
+    if extra == "auto":
+        extra = EXTRA_CONFIGS if (args.workload == DEFAULT_WORKLOAD and not args.tiles) else []
+    elif extra == "none":
+        extra = []
+    else:
+        extra = [(x.split(":")[0], x.endswith(":tiles")) for x in extra.split(",") if x]
+    if extra:
+        line["configs"] = {}
+    for name, tiles in extra:
+        eb = Bench(name, dev, tiles=tiles, cache_dir=args.cache_dir)
+        er = eb.run(args.steps, args.warmup, flush_buf, None)
+        key = name + (":tiles" if tiles else "")
+        roof = er["roofline"]
+        c = {"ms_per_step": round(er["ms_per_step"], 4), "value": round(eb.rate(er["ms_per_step"]), 4),
+             "warm_ms_per_step": round(er["warm_ms"], 4), "warm_value": round(eb.rate(er["warm_ms"]), 4),
+             "edges": eb.e, "dominant": {k: roof[k] for k in ("kernel", "kernel_ms", "achieved",
+                                                                "frac", "cache_served")},
+             "step_model": er["step_model"], "memory": eb.memory,
+             "kernels": {k: {f: v[f] for f in ("ms", "achieved_gbs", "mfma_utilisation") if f in v}
+                         for k, v in er["kernels"].items()}}
+        line["configs"][key] = c
+        eb.release()
+        del eb
+
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+        line["cpu_baseline"] = cpu_baseline(w_head, args.cpu_seconds)
     print(json.dumps(line), flush=True)
 
 

@@ -102,7 +102,16 @@ typedef struct sgat_plan_opts {
                              order of the undirected graph, so rows that share
                              neighbours run close together in time (more L2 reuse
                              of gathered rows). Results are the same up to rounding. */
-    int32_t reserved;     /* must be 0 */
+    int32_t edge_order;   /* Where the Graph Transformer backward (gather path) keeps the
+                             dS values its transposed-CSR pass hands to its CSR pass:
+                             1 = CSR edge order (each edge's H floats written at its CSR
+                             position: scattered small writes, contiguous reads);
+                             2 = transposed order (written contiguously, read through
+                             SGAT_ARR_ROW_TPOS); 0 = automatic: transposed when
+                             nnz * H * 4 bytes exceed 128 MiB, about half the 256 MB
+                             Infinity Cache, beyond which the scattered partial-line
+                             writes reach HBM; CSR order otherwise. Results are bitwise
+                             the same either way. */
 } sgat_plan_opts;
 
 /* Summary of a plan (all counts are exact). */
@@ -138,7 +147,10 @@ typedef enum sgat_array {
     SGAT_ARR_COL_EDGE = 16,   /* int32 [nnz]: CSR edge id of each transposed-CSR entry  */
     SGAT_ARR_RES_COL_EDGE = 17,/* int32 [residual_edges]: residual-CSR edge id of each
                                  transposed residual entry                              */
-    SGAT_ARR_COUNT = 18
+    SGAT_ARR_ROW_TPOS = 18,   /* int32 [nnz]: transposed-CSR position of each CSR edge
+                                 (the inverse of SGAT_ARR_COL_EDGE); built for
+                                 edge_order 2, and for 0 when nnz > 2^21; else empty     */
+    SGAT_ARR_COUNT = 19
 } sgat_array;
 
 /* One unit of work of the gather kernels: `len` consecutive edges starting at

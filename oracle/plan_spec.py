@@ -144,6 +144,15 @@ def transpose(rowptr: np.ndarray, colidx: np.ndarray, edge_ids: bool = False):
     return colptr, dst[order].astype(np.int32)
 
 
+def transposed_positions(col_edge: np.ndarray) -> np.ndarray:
+    """Position in the transposed CSR of every CSR edge: entry q of the
+    transposed CSR is CSR edge col_edge[q], so edge col_edge[q] sits at q."""
+    col_edge = np.asarray(col_edge, dtype=np.int64)
+    out = np.empty(col_edge.size, dtype=np.int32)
+    out[col_edge] = np.arange(col_edge.size, dtype=np.int32)
+    return out
+
+
 def tiles(rowptr: np.ndarray, colidx: np.ndarray, min_nnz: int):
     rowptr = np.asarray(rowptr, dtype=np.int64)
     src = np.asarray(colidx, dtype=np.int64)

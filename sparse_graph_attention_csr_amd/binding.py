@@ -25,7 +25,7 @@ REDUCE_OPS = {"min": REDUCE_MIN, "max": REDUCE_MAX}
 (ARR_ROW_ITEMS, ARR_ROW_SPLITS, ARR_COLPTR, ARR_ROWIDX, ARR_COL_ITEMS, ARR_COL_SPLITS,
  ARR_TILE_ROWPTR, ARR_TILE_COL, ARR_TILE_MASK, ARR_RES_ROWPTR, ARR_RES_COLIDX,
  ARR_TILE_ROW, ARR_TILE_COLPTR, ARR_TILE_BYCOL, ARR_RES_COLPTR, ARR_RES_ROWIDX,
- ARR_COL_EDGE, ARR_RES_COL_EDGE) = range(18)
+ ARR_COL_EDGE, ARR_RES_COL_EDGE, ARR_ROW_TPOS) = range(19)
 
 STATUS = {0: "OK", 1: "INVALID_ARGUMENT", 2: "INVALID_CSR", 3: "WORKSPACE_TOO_SMALL",
           4: "PLAN_MISMATCH", 5: "HIP_ERROR", 6: "NOT_UPLOADED", 7: "OUT_OF_HOST_MEMORY",
@@ -48,6 +48,7 @@ ARRAY_DTYPES = {
     ARR_TILE_COLPTR: np.dtype("<i8"), ARR_TILE_BYCOL: np.dtype("<i4"),
     ARR_RES_COLPTR: np.dtype("<i8"), ARR_RES_ROWIDX: np.dtype("<i4"),
     ARR_COL_EDGE: np.dtype("<i4"), ARR_RES_COL_EDGE: np.dtype("<i4"),
+    ARR_ROW_TPOS: np.dtype("<i4"),
 }
 
 
@@ -60,7 +61,7 @@ class SgatError(RuntimeError):
 class PlanOpts(ctypes.Structure):
     _fields_ = [("chunk", ctypes.c_int64), ("tile_min_nnz", ctypes.c_int32),
                 ("block_sparse", ctypes.c_int32), ("locality", ctypes.c_int32),
-                ("reserved", ctypes.c_int32)]
+                ("edge_order", ctypes.c_int32)]
 
 
 class PlanStats(ctypes.Structure):
@@ -216,13 +217,14 @@ class Plan:
     """Host plan of one CSR graph (sgat_plan_create / _upload / _destroy)."""
 
     def __init__(self, rowptr, colidx, chunk: int = 0, tile_min_nnz: int = 0,
-                 block_sparse: bool = False, locality: bool = False):
+                 block_sparse: bool = False, locality: bool = False, edge_order: int = 0):
         rowptr = np.ascontiguousarray(rowptr, dtype=np.int64)
         colidx = np.ascontiguousarray(colidx, dtype=np.int32)
         self.n = int(rowptr.size - 1)
         self.nnz = int(colidx.size)
+        self.edge_order = int(edge_order)
         opts = PlanOpts(int(chunk), int(tile_min_nnz), int(bool(block_sparse)),
-                        int(bool(locality)), 0)
+                        int(bool(locality)), int(edge_order))
         h = ctypes.c_void_p()
         _check("sgat_plan_create",
                lib().sgat_plan_create(self.n, self.nnz, rowptr.ctypes.data, colidx.ctypes.data,
@@ -445,10 +447,11 @@ class DeviceGraph:
     """
 
     def __init__(self, rowptr, colidx, device="cuda", chunk: int = 0, tile_min_nnz: int = 0,
-                 block_sparse: bool = False, locality: bool = False, stream=None):
+                 block_sparse: bool = False, locality: bool = False, edge_order: int = 0,
+                 stream=None):
         import torch
         self.plan = Plan(rowptr, colidx, chunk=chunk, tile_min_nnz=tile_min_nnz,
-                         block_sparse=block_sparse, locality=locality)
+                         block_sparse=block_sparse, locality=locality, edge_order=edge_order)
         self.n, self.nnz = self.plan.n, self.plan.nnz
         self.device = torch.device(device)
         self.rowptr = torch.from_numpy(np.ascontiguousarray(rowptr, dtype=np.int64)).to(self.device)

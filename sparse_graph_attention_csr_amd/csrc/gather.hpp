@@ -556,6 +556,7 @@ struct GtBwdRowArgs {
     int64_t n_units;
     int n_hg, H;
     const int32_t* colidx;
+    const int32_t* tpos;   // TPOS: transposed position of each CSR edge (where its dS is)
     const void* K;
     const float* ds;
     void* dQ;
@@ -563,7 +564,9 @@ struct GtBwdRowArgs {
     float oscale;   // 1 / sqrt(D)
 };
 
-template <int DT, int D, int EPW, int U>
+// TPOS = false: dS is in CSR edge order, read contiguously; true: it is in
+// transposed order and each edge's H floats are found through tpos.
+template <int DT, int D, int EPW, int U, bool TPOS>
 __global__ __launch_bounds__(kBlock) void gt_bwd_rows(GtBwdRowArgs a)
 {
     using G = Geo<DT, D, EPW>;
@@ -578,10 +581,11 @@ __global__ __launch_bounds__(kBlock) void gt_bwd_rows(GtBwdRowArgs a)
 
     float dq[VEC] = {};
     const int32_t* ci = a.colidx + it.begin;
-    const float* dsr = a.ds + it.begin * a.H + g.head;
+    const float* dsr = a.ds + (TPOS ? 0 : it.begin * a.H) + g.head;
     for (int base = 0; base < it.len; base += kWave) {
         const int nb = min(kWave, it.len - base);
         const int cj = g.lane < nb ? ci[base + g.lane] : 0;
+        const int tq = TPOS && g.lane < nb ? a.tpos[it.begin + base + g.lane] : 0;
         for (int t = 0; t < nb; t += EPW * U) {
             Frag kf[U];
             float d[U];
@@ -589,11 +593,12 @@ __global__ __launch_bounds__(kBlock) void gt_bwd_rows(GtBwdRowArgs a)
             for (int u = 0; u < U; ++u) {
                 const int e = t + u * EPW + g.sub;
                 const int64_t j = bcast<EPW>(cj, e);
+                const int64_t q = TPOS ? static_cast<int64_t>(bcast<EPW>(tq, e)) : base + e;
                 kf[u] = frag_zero();
                 d[u] = 0.f;
                 if (e < nb && g.hvalid) {
                     kf[u] = ldg_nbr<DT>(a.K, static_cast<uint32_t>(j), g.col, HD);
-                    d[u] = __builtin_nontemporal_load(dsr + static_cast<int64_t>(base + e) * a.H);
+                    d[u] = __builtin_nontemporal_load(dsr + q * a.H);
                 }
             }
 #pragma unroll
@@ -937,13 +942,22 @@ struct GtBwdColArgs {
     float scale2, oscale;
 };
 
-template <int DT, int D, int EPW, int U>
+// dS of a block of 64 edges is collected in LDS (one float per edge and head
+// of the group) and written once the block's gathers are done: loads and
+// stores share one outstanding-memory counter, so a store issued inside the
+// gather loop would make every later wait for gathered rows wait for it too.
+// TPOS = false: each edge's H floats go to its CSR position (col_edge), a
+// scattered partial-line write per edge; true: to its transposed position,
+// so a block's values are one contiguous span.
+template <int DT, int D, int EPW, int U, bool TPOS>
 __global__ __launch_bounds__(kBlock) void gt_bwd_cols(GtBwdColArgs a)
 {
     using G = Geo<DT, D, EPW>;
     constexpr int VEC = G::VEC;
+    __shared__ float dsl[kWavesPerBlock][kWave * G::HG];
     const int64_t unit = logical_block() * kWavesPerBlock + wave_id();
     if (unit >= a.n_units) return;
+    float* my_ds = dsl[wave_id()];
     const int64_t ii = unit / a.n_hg;
     const int hg = static_cast<int>(unit - ii * a.n_hg);
     const sgat_work_item it = a.items[ii];
@@ -961,18 +975,16 @@ __global__ __launch_bounds__(kBlock) void gt_bwd_cols(GtBwdColArgs a)
     for (int base = 0; base < it.len; base += kWave) {
         const int nb = min(kWave, it.len - base);
         const int ci = g.lane < nb ? ri[base + g.lane] : 0;
-        const int ce = g.lane < nb ? re[base + g.lane] : 0;
+        const int ce = !TPOS && g.lane < nb ? re[base + g.lane] : 0;
         for (int t = 0; t < nb; t += EPW * U) {
             Frag qf[U], df[U];
             RowStat rs[U];
             bool ok[U];
-            int64_t eid[U];
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const int e = t + u * EPW + g.sub;
                 ok[u] = e < nb;
                 const int64_t i = bcast<EPW>(ci, e);
-                eid[u] = bcast<EPW>(ce, e);
                 qf[u] = frag_zero();
                 df[u] = frag_zero();
                 rs[u] = RowStat{0.f, 0.f};
@@ -988,8 +1000,7 @@ __global__ __launch_bounds__(kBlock) void gt_bwd_cols(GtBwdColArgs a)
                 const float dp = head_sum<G::SPH>(dot<DT>(df[u], vj));
                 const float p = ok[u] ? fast_exp2(s2 - rs[u].lse2) : 0.f;
                 const float ds = p * (dp - rs[u].delta);
-                if (ok[u] && g.hvalid && g.leader)
-                    __builtin_nontemporal_store(ds, a.ds + eid[u] * a.H + g.head);
+                if (ok[u] && g.leader) my_ds[(t + u * EPW + g.sub) * G::HG + g.pos / G::SPH] = ds;
                 float qx[VEC], dx[VEC];
                 to_f32<DT>(qf[u], qx);
                 to_f32<DT>(df[u], dx);
@@ -1000,6 +1011,20 @@ __global__ __launch_bounds__(kBlock) void gt_bwd_cols(GtBwdColArgs a)
                 }
             }
         }
+        // the block's dS: value k*64 + lane is edge (k*64 + lane) / HG, head
+        // (k*64 + lane) % HG of the group, so HG consecutive lanes write one
+        // edge's HG floats
+        wave_lds_fence();
+#pragma unroll 1
+        for (int k = 0; k < G::HG; ++k) {
+            const int v = k * kWave + g.lane;
+            const int e = v / G::HG;
+            const int head = hg * G::HG + v % G::HG;
+            const int64_t eid = TPOS ? it.begin + base + e : __shfl(ce, e);
+            if (e < nb && head < a.H)
+                __builtin_nontemporal_store(my_ds[v], a.ds + eid * a.H + head);
+        }
+        wave_lds_fence();
     }
     if constexpr (EPW > 1) {
         sum_groups<VEC, G::LPE>(dk);

@@ -126,6 +126,8 @@ int launch_gt_bwd(const Plan& p, int H, int D, int dt, const int32_t* colidx, co
     r.n_hg = dc.n_hg;
     r.H = H;
     r.colidx = colidx;
+    const bool tpos = p.ds_transposed(H);
+    r.tpos = tpos ? p.dptr<int32_t>(SGAT_ARR_ROW_TPOS) : nullptr;
     r.K = K;
     r.ds = ws.ds;
     r.dQ = dQ;
@@ -133,11 +135,13 @@ int launch_gt_bwd(const Plan& p, int H, int D, int dt, const int32_t* colidx, co
     r.oscale = oscale;
 
     const void *fd = nullptr, *fr = nullptr, *fc = nullptr;
-#define X(DT_, D_, E_)                                                                 \
-    if (dt == DT_ && D == D_ && dc.epw == E_) {                                        \
-        fd = reinterpret_cast<const void*>(&bwd_delta<DT_, D_, E_>);                   \
-        fr = reinterpret_cast<const void*>(&gt_bwd_rows<DT_, D_, E_, unroll_rows(E_)>);     \
-        fc = reinterpret_cast<const void*>(&gt_bwd_cols<DT_, D_, E_, unroll_bwd(E_)>);     \
+#define X(DT_, D_, E_)                                                                      \
+    if (dt == DT_ && D == D_ && dc.epw == E_) {                                             \
+        fd = reinterpret_cast<const void*>(&bwd_delta<DT_, D_, E_>);                        \
+        fr = tpos ? reinterpret_cast<const void*>(&gt_bwd_rows<DT_, D_, E_, unroll_rows(E_), true>)  \
+                  : reinterpret_cast<const void*>(&gt_bwd_rows<DT_, D_, E_, unroll_rows(E_), false>); \
+        fc = tpos ? reinterpret_cast<const void*>(&gt_bwd_cols<DT_, D_, E_, unroll_bwd(E_), true>)   \
+                  : reinterpret_cast<const void*>(&gt_bwd_cols<DT_, D_, E_, unroll_bwd(E_), false>);  \
     }
     SGAT_GATHER_CONFIGS(X)
 #undef X

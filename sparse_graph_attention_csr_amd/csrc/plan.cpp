@@ -280,8 +280,15 @@ const void* Plan::host_array(int id) const
     case SGAT_ARR_RES_ROWIDX: return res_rowidx.data();
     case SGAT_ARR_RES_COL_EDGE: return res_col_edge.data();
     case SGAT_ARR_COL_EDGE: return col_edge.data();
+    case SGAT_ARR_ROW_TPOS: return row_tpos.data();
     default: return nullptr;
     }
+}
+
+bool Plan::ds_transposed(int H) const
+{
+    if (edge_order == 1 || row_tpos.empty()) return false;
+    return edge_order == 2 || nnz * static_cast<int64_t>(H) * 4 > kDsTransposedBytes;
 }
 
 void Plan::layout()
@@ -304,6 +311,7 @@ void Plan::layout()
     bytes[SGAT_ARR_RES_ROWIDX] = res_rowidx.size() * sizeof(int32_t);
     bytes[SGAT_ARR_RES_COL_EDGE] = res_col_edge.size() * sizeof(int32_t);
     bytes[SGAT_ARR_COL_EDGE] = col_edge.size() * sizeof(int32_t);
+    bytes[SGAT_ARR_ROW_TPOS] = row_tpos.size() * sizeof(int32_t);
     size_t off = 0;
     for (int a = 0; a < SGAT_ARR_COUNT; ++a) {
         offset[a] = off;
@@ -328,16 +336,18 @@ int sgat_plan_create(int64_t n, int64_t nnz, const int64_t* rowptr, const int32_
     int64_t chunk = sgat::kDefaultChunk;
     int32_t tmin = sgat::kDefaultTileMinNnz;
     bool bs = false, loc = false;
+    int32_t order = 0;
     if (opts) {
         if (opts->chunk < 0 || opts->chunk > INT32_MAX) return SGAT_INVALID_ARGUMENT;
         if (opts->tile_min_nnz < 0 || opts->tile_min_nnz > 256) return SGAT_INVALID_ARGUMENT;
         if (opts->block_sparse != 0 && opts->block_sparse != 1) return SGAT_INVALID_ARGUMENT;
         if (opts->locality != 0 && opts->locality != 1) return SGAT_INVALID_ARGUMENT;
-        if (opts->reserved != 0) return SGAT_INVALID_ARGUMENT;
+        if (opts->edge_order < 0 || opts->edge_order > 2) return SGAT_INVALID_ARGUMENT;
         if (opts->chunk > 0) chunk = opts->chunk;
         if (opts->tile_min_nnz > 0) tmin = opts->tile_min_nnz;
         bs = opts->block_sparse == 1;
         loc = opts->locality == 1;
+        order = opts->edge_order;
     }
     sgat_plan* h = new (std::nothrow) sgat_plan;
     if (!h) return SGAT_OUT_OF_HOST_MEMORY;
@@ -349,9 +359,16 @@ int sgat_plan_create(int64_t n, int64_t nnz, const int64_t* rowptr, const int32_
         p.tile_min_nnz = tmin;
         p.block_sparse = bs;
         p.locality = loc;
+        p.edge_order = order;
         for (int64_t i = 0; i < n; ++i)
             p.max_in_degree = std::max(p.max_in_degree, rowptr[i + 1] - rowptr[i]);
         sgat::build_transpose(n, rowptr, colidx, p.colptr, p.rowidx, &p.col_edge);
+        if (order == 2 || (order == 0 && nnz > sgat::kTposMinEdges)) {
+            p.row_tpos.assign(static_cast<size_t>(nnz), 0);
+            for (int64_t q = 0; q < nnz; ++q)
+                p.row_tpos[static_cast<size_t>(p.col_edge[static_cast<size_t>(q)])] =
+                    static_cast<int32_t>(q);
+        }
         for (int64_t j = 0; j < n; ++j)
             p.max_out_degree = std::max(p.max_out_degree, p.colptr[j + 1] - p.colptr[j]);
         std::vector<int32_t> rank;

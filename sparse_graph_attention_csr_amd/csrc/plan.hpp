@@ -13,6 +13,10 @@ constexpr int64_t kDefaultChunk = 1024;
 constexpr int32_t kDefaultTileMinNnz = 32;
 constexpr int kTile = 16;
 constexpr size_t kAlign = 256;
+// edge_order 0: dS goes in transposed order above this many bytes, and the
+// inverse map is built when some H <= 16 could get there
+constexpr int64_t kDsTransposedBytes = int64_t(128) << 20;
+constexpr int64_t kTposMinEdges = int64_t(1) << 21;
 
 inline size_t align_up(size_t x, size_t a = kAlign) { return (x + a - 1) / a * a; }
 
@@ -22,6 +26,7 @@ struct Plan {
     int32_t tile_min_nnz = kDefaultTileMinNnz;
     bool block_sparse = false;
     bool locality = false;
+    int32_t edge_order = 0;             // sgat_plan_opts.edge_order
     int64_t max_in_degree = 0, max_out_degree = 0;
 
     std::vector<sgat_work_item> row_items;
@@ -34,6 +39,7 @@ struct Plan {
     std::vector<int64_t> colptr;
     std::vector<int32_t> rowidx;
     std::vector<int32_t> col_edge;      // CSR edge id of each transposed entry
+    std::vector<int32_t> row_tpos;      // transposed position of each CSR edge (may be empty)
     std::vector<sgat_work_item> col_items;
     std::vector<sgat_split> col_splits;
     int64_t col_slots = 0;
@@ -59,6 +65,8 @@ struct Plan {
     bool uploaded = false;
 
     const void* host_array(int id) const;
+    // Graph Transformer backward: dS in transposed order for H heads?
+    bool ds_transposed(int H) const;
     void layout();
     template <class T>
     const T* dptr(int id) const { return reinterpret_cast<const T*>(dev + offset[id]); }

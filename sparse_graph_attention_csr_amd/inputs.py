@@ -333,20 +333,23 @@ def make_tensors(name: str, seed: int = 0, with_grad: bool = True) -> dict:
     w = WORKLOADS[name]
     st = _streams(seed)
     shape = (w.n, w.heads, w.dim) if w.op != "reduce" else (w.n, w.dim)
-    t = {}
+    # (name, stream, shape, dtype, std): each tensor has a stream of its own,
+    # so drawing them on parallel threads gives the same bytes as in turn
+    jobs = []
     if w.op == "reduce":
-        t["x"] = normal_tensor(st["q"], shape, w.dtype)
+        jobs.append(("x", "q", shape, w.dtype, 1.0))
     elif w.op == "gt":
-        t["q"] = normal_tensor(st["q"], shape, w.dtype)
-        t["k"] = normal_tensor(st["k"], shape, w.dtype)
-        t["v"] = normal_tensor(st["v"], shape, w.dtype)
+        jobs += [("q", "q", shape, w.dtype, 1.0), ("k", "k", shape, w.dtype, 1.0),
+                 ("v", "v", shape, w.dtype, 1.0)]
     else:
-        t["xs"] = normal_tensor(st["q"], shape, w.dtype)
-        t["xt"] = normal_tensor(st["k"], shape, w.dtype)
-        t["a"] = normal_tensor(st["a"], (w.heads, w.dim), F32, std=w.dim ** -0.5)
+        jobs += [("xs", "q", shape, w.dtype, 1.0), ("xt", "k", shape, w.dtype, 1.0),
+                 ("a", "a", (w.heads, w.dim), F32, w.dim ** -0.5)]
     if with_grad and w.passes == "fwd+bwd":
-        t["dout"] = normal_tensor(st["dout"], shape, w.dtype)
-    return t
+        jobs.append(("dout", "dout", shape, w.dtype, 1.0))
+    from concurrent.futures import ThreadPoolExecutor
+    with ThreadPoolExecutor(len(jobs)) as ex:
+        arrs = list(ex.map(lambda j: normal_tensor(st[j[1]], j[2], j[3], std=j[4]), jobs))
+    return {j[0]: a for j, a in zip(jobs, arrs)}
 
 
 def make_workload(name: str, seed: int = 0, with_grad: bool = True) -> dict:

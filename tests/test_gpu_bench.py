@@ -18,7 +18,8 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 def test_bench_json_line():
     note("bench.py on gt_er1k_h4d32_f32")
     r = subprocess.run([sys.executable, "bench.py", "--workload", "gt_er1k_h4d32_f32",
-                        "--steps", "3", "--warmup", "1", "--cpu-seconds", "1", "--step-times"],
+                        "--steps", "3", "--warmup", "1", "--cpu-seconds", "1", "--step-times",
+                        "--probe-gib", "0.5", "--extra", "gt_er1k_h4d32_f32"],
                        cwd=ROOT, capture_output=True, text=True, timeout=240)
     assert r.returncode == 0, r.stderr[-2000:]
     lines = [l for l in r.stdout.splitlines() if l.startswith("{")]
@@ -42,6 +43,21 @@ def test_bench_json_line():
         assert k in roof, k
     assert roof["bound"] == "hbm" and roof["unit"] == "GB/s" and roof["peak"] == 8000.0
     assert abs(roof["frac"] - roof["achieved"] / roof["peak"]) < 1e-3
+    # a fraction above 1 is only possible if caches served modelled gathers,
+    # and the line must say so
+    assert (roof["frac"] > 1) == roof["cache_served"]
+    assert (d["step_model"]["frac"] > 1) == d["step_model"]["cache_served"]
+    assert abs(d["step_model"]["gbs"] - d["step_model"]["bytes"] / (ms * 1e-3) / 1e9) \
+        <= 1e-3 * d["step_model"]["gbs"] + 0.1
+    hc = d["hbm_ceiling"]
+    assert 0 < hc["stream_read_gbs"] and 0 < hc["gather_gbs"] and hc["spec_gbs"] == 8000.0
+    assert roof["frac_of_ceiling"] > 0
+    assert d["warm"]["ms_per_step"] > 0 and d["warm"]["value"] > 0
+    mem = d["memory"]
+    assert mem["inputs_bytes"] == 3 * 1000 * 4 * 32 * 4      # Q, K, V fp32
+    assert mem["workspace_bytes"]["fwd"] >= 0 and mem["plan_bytes"] > 0
+    cf = d["configs"]["gt_er1k_h4d32_f32"]
+    assert cf["ms_per_step"] > 0 and cf["value"] > 0 and cf["edges"] == c["edges"]
     for kind in ("warm", "cold"):          # each step timed alone, median and minimum
         st = d["steps_ms"][kind]
         assert 0 < st["min"] <= st["median"] and st["reps"] == 3 and st["value"] > 0
@@ -98,3 +114,21 @@ def test_trace_only_brackets_one_kernel():
     one = traced("gt_bwd_cols")
     assert [n for n, _ in one] == ["gt_bwd_cols"] * names.count("gt_bwd_cols")
     assert traced("no_such_kernel") == []
+
+
+def test_probes_load_and_leave_the_sink_alone():
+    """The bandwidth probes run on ones-filled buffers (every folded word is
+    0, never the sink constant) and skip row indices outside the table."""
+    import torch
+
+    from sparse_graph_attention_csr_amd import binding as B
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+    buf = torch.ones(1 << 20, dtype=torch.int32, device="cuda")
+    B.probe_read(buf, sink, 64)
+    table = torch.ones(1000, 256, dtype=torch.int32, device="cuda")    # 1 KiB rows
+    idx = torch.tensor([0, 999, 1000, 5000, -1, 3] * 50, dtype=torch.int32, device="cuda")
+    B.probe_gather(table, idx, sink)
+    torch.cuda.synchronize()
+    assert int(sink.abs().sum()) == 0
+    with pytest.raises(B.SgatError):
+        B.probe_gather(torch.ones(10, 3, dtype=torch.int32, device="cuda"), idx, sink)  # 12-byte rows

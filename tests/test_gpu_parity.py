@@ -34,12 +34,13 @@ def tensors(seed, n, H, D, dt, names):
 
 @pytest.mark.parametrize("chunk", [0, 5])
 @pytest.mark.parametrize("dt,H,D", LAYOUTS)
-def test_gt_parity(dt, H, D, chunk):
-    note(f"gt parity dt={dt} H={H} D={D} chunk={chunk}")
+@pytest.mark.parametrize("order", [1, 2])
+def test_gt_parity(dt, H, D, chunk, order):
+    note(f"gt parity dt={dt} H={H} D={D} chunk={chunk} edge_order={order}")
     rp, ci = graph(100 + H + D)
     n = rp.size - 1
     t = tensors(7, n, H, D, dt, ["q", "k", "v", "dout"])
-    r = Runner(rp, ci, chunk=chunk)
+    r = Runner(rp, ci, chunk=chunk, edge_order=order)
     q, k, v, do = (dev(t[x]) for x in ("q", "k", "v", "dout"))
     out, lse = r.gt_fwd(q, k, v)
     ro, rl = oracle.gt_fwd(rp, ci, t["q"], t["k"], t["v"])
@@ -250,6 +251,24 @@ def test_bitwise_determinism():
         out, lse = r.gat_fwd(xs, xt, a)
         g = r.gat_bwd(xs, xt, a, out, lse, do)
         res.append([host(x) for x in (out, lse, *g)])
+    for x, y in zip(*res):
+        assert np.array_equal(x, y)
+
+
+@pytest.mark.parametrize("dt,H,D", [("bf16", 8, 64), ("f32", 4, 32), ("bf16", 2, 64)])
+def test_gt_edge_orders_bitwise_equal(dt, H, D):
+    """dS handed over in CSR order or in transposed order: the same values,
+    summed in the same order, so every gradient is bitwise the same."""
+    note(f"gt edge orders dt={dt} H={H} D={D}")
+    rp, ci = graph(31, n=500)
+    n = rp.size - 1
+    t = tensors(32, n, H, D, dt, ["q", "k", "v", "dout"])
+    q, k, v, do = (dev(t[x]) for x in ("q", "k", "v", "dout"))
+    res = []
+    for order in (1, 2):
+        r = Runner(rp, ci, chunk=64, edge_order=order)
+        out, lse = r.gt_fwd(q, k, v)
+        res.append([host(x) for x in (out, lse, *r.gt_bwd(q, k, v, out, lse, do))])
     for x, y in zip(*res):
         assert np.array_equal(x, y)
 

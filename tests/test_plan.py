@@ -10,8 +10,9 @@ from sparse_graph_attention_csr_amd import binding as B
 from sparse_graph_attention_csr_amd import inputs as I
 
 
-def check_plan(rowptr, colidx, chunk, tmin=0, bs=False, loc=False):
-    p = B.Plan(rowptr, colidx, chunk=chunk, tile_min_nnz=tmin, block_sparse=bs, locality=loc)
+def check_plan(rowptr, colidx, chunk, tmin=0, bs=False, loc=False, order=2):
+    p = B.Plan(rowptr, colidx, chunk=chunk, tile_min_nnz=tmin, block_sparse=bs, locality=loc,
+               edge_order=order)
     C = p.stats()["chunk"]
     rank = S.cuthill_mckee_rank(rowptr, colidx) if loc else None
     items, splits, nslots = S.work_list(rowptr, C, rank)
@@ -21,6 +22,12 @@ def check_plan(rowptr, colidx, chunk, tmin=0, bs=False, loc=False):
     assert np.array_equal(p.export(B.ARR_COLPTR), colptr)
     assert np.array_equal(p.export(B.ARR_ROWIDX), rowidx)
     assert np.array_equal(p.export(B.ARR_COL_EDGE), col_edge)
+    # the inverse map is built for edge order 2 (and for 0 above 2^21 edges)
+    tpos = p.export(B.ARR_ROW_TPOS)
+    if order == 2:
+        assert np.array_equal(tpos, S.transposed_positions(col_edge))
+    else:
+        assert tpos.size == 0
     citems, csplits, cslots = S.work_list(colptr, C, rank)
     assert p.export(B.ARR_COL_ITEMS).tobytes() == citems.tobytes()
     assert p.export(B.ARR_COL_SPLITS).tobytes() == csplits.tobytes()
@@ -87,8 +94,24 @@ GRAPHS = {
 @pytest.mark.parametrize("loc", [False, True])
 def test_plan_matches_spec(name, chunk, loc):
     rp, ci = I.random_csr(rng=np.random.default_rng(sum(map(ord, name))), **GRAPHS[name])
-    p = check_plan(rp, ci, chunk, tmin=3, bs=True, loc=loc)
+    p = check_plan(rp, ci, chunk, tmin=3, bs=True, loc=loc, order=2 if chunk else 1)
     invariants(p, rp, ci)
+
+
+def test_transposed_positions_invert_the_transpose():
+    """Every CSR edge p sits at position tpos[p] of the transposed CSR: same
+    source and destination there, and tpos is a permutation."""
+    rp, ci = I.random_csr(200, 15, np.random.default_rng(5), empty_frac=0.1, dup_frac=0.2)
+    p = B.Plan(rp, ci, edge_order=2)
+    tpos = p.export(B.ARR_ROW_TPOS).astype(np.int64)
+    n, E = rp.size - 1, ci.size
+    assert np.array_equal(np.sort(tpos), np.arange(E))
+    colptr, rowidx = p.export(B.ARR_COLPTR), p.export(B.ARR_ROWIDX)
+    src_of_pos = np.repeat(np.arange(n), np.diff(colptr))
+    assert np.array_equal(src_of_pos[tpos], ci)
+    assert np.array_equal(rowidx[tpos], np.repeat(np.arange(n), np.diff(rp)))
+    # automatic order: no map for a small graph
+    assert B.Plan(rp, ci).export(B.ARR_ROW_TPOS).size == 0
 
 
 def test_cuthill_mckee_visits_components_breadth_first():
@@ -172,7 +195,8 @@ def test_invalid_csr_rejected(case):
 def test_invalid_options_rejected():
     rp = np.array([0, 1], dtype=np.int64)
     ci = np.array([0], dtype=np.int32)
-    for kw in (dict(chunk=-1), dict(tile_min_nnz=-2), dict(tile_min_nnz=257)):
+    for kw in (dict(chunk=-1), dict(tile_min_nnz=-2), dict(tile_min_nnz=257),
+               dict(edge_order=3), dict(edge_order=-1)):
         with pytest.raises(B.SgatError) as e:
             B.Plan(rp, ci, **kw)
         assert e.value.status == 1
