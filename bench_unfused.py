@@ -3,9 +3,11 @@ and min/max aggregation.
 
 This is the baseline that ``bench.py --compare-unfused`` times and measures
 the peak memory of, beside the fused library. It is the message-passing form
-an unfused GNN layer takes (DF-GNN, Introduction and Evaluation: the
-unfused pipeline runs SDDMM, edge softmax and SpMM as separate kernels and keeps
-every per-edge score and weight in device memory): gather the endpoint rows
+an unfused GNN layer takes (DF-GNN, Abstract: without kernel fusion the
+layer's operations run as separate kernels with heavy data movement between
+them; IO-aware layers paper, Abstract: message-passing frameworks materialise
+edge-wise intermediates, so every per-edge score and weight sits in device
+memory): gather the endpoint rows
 per edge, score each edge, take the softmax over each destination's in-edges
 with scatter reductions, weight the gathered value rows and scatter-add them
 into the destinations. torch.autograd supplies the backward, which keeps the

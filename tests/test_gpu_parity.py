@@ -10,7 +10,7 @@ import pytest
 
 import oracle
 from sparse_graph_attention_csr_amd import inputs as I
-from tests.gpu_util import TOL, Runner, dev, host, note, rel_err, widen
+from tests.gpu_util import TOL, TOL_LSE, Runner, dev, host, note, rel_err, widen
 
 pytestmark = pytest.mark.gpu
 
@@ -45,7 +45,7 @@ def test_gt_parity(dt, H, D, chunk, order):
     out, lse = r.gt_fwd(q, k, v)
     ro, rl = oracle.gt_fwd(rp, ci, t["q"], t["k"], t["v"])
     assert rel_err(host(out), ro) <= TOL[dt]
-    assert rel_err(host(lse), rl) <= TOL[dt]
+    assert rel_err(host(lse), rl) <= TOL_LSE
     dq, dk, dv = r.gt_bwd(q, k, v, out, lse, do)
     # the backward consumes the GPU's stored output, as a caller's would
     rq, rk, rv = oracle.gt_bwd(rp, ci, t["q"], t["k"], t["v"], t["dout"])
@@ -70,7 +70,7 @@ def test_gat_parity(dt, H, D, chunk):
     out, lse = r.gat_fwd(xs, xt, ad)
     ro, rl = oracle.gat_fwd(rp, ci, t["xs"], t["xt"], a)
     assert rel_err(host(out), ro) <= TOL[dt]
-    assert rel_err(host(lse), rl) <= TOL[dt]
+    assert rel_err(host(lse), rl) <= TOL_LSE
     dxs, dxt, da = r.gat_bwd(xs, xt, ad, out, lse, do)
     rs, rt, ra = oracle.gat_bwd(rp, ci, t["xs"], t["xt"], a, t["dout"])
     assert rel_err(host(dxs), rs) <= TOL[dt]
@@ -103,7 +103,7 @@ def test_gat_short_and_long_items(dt, H, D):
         ad = dev(a)
         out, lse = r.gat_fwd(xs, xt, ad)
         assert rel_err(host(out), ro) <= TOL[dt]
-        assert rel_err(host(lse), rl) <= TOL[dt]
+        assert rel_err(host(lse), rl) <= TOL_LSE
         dxs, dxt, da = r.gat_bwd(xs, xt, ad, out, lse, do)
         assert rel_err(host(dxs), rs) <= TOL[dt]
         assert rel_err(host(dxt), rt) <= TOL[dt]
@@ -171,7 +171,7 @@ def test_gat_slopes_and_exact_zeros(dt, H, D, slope):
     ro, rl = oracle.gat_fwd(rp, ci, xs_h, xt_h, a, slope)
     rs, rt, ra = oracle.gat_bwd(rp, ci, xs_h, xt_h, a, do_h, slope)
     for name, got, ref in (("out", out, ro), ("lse", lse, rl), ("dXt", dxt, rt), ("da", da, ra)):
-        assert rel_err(host(got), ref) <= TOL[dt], name
+        assert rel_err(host(got), ref) <= (TOL_LSE if name == "lse" else TOL[dt]), name
     scale = max(np.abs(rs).max(), np.abs(rt).max())
     assert np.isfinite(host(dxs)).all()
     assert np.abs(host(dxs) - rs).max() <= TOL[dt] * scale, "dXs"

@@ -16,7 +16,7 @@ import pytest
 
 import oracle
 from sparse_graph_attention_csr_amd import inputs as I
-from tests.gpu_util import TOL, Runner, dev, host, note, rel_err
+from tests.gpu_util import TOL, TOL_LSE, Runner, dev, host, note, rel_err
 
 pytestmark = pytest.mark.gpu
 
@@ -68,7 +68,7 @@ def test_random_graphs(case):
     def check(name, got, ref, scale_ref=None):
         g = host(got)
         if scale_ref is None:
-            assert rel_err(g, ref) <= TOL[dt], name
+            assert rel_err(g, ref) <= (TOL_LSE if name.endswith("lse") else TOL[dt]), name
         else:
             assert np.isfinite(g).all(), name
             scale = max(np.abs(ref).max(initial=0.0), np.abs(scale_ref).max(initial=0.0), 1e-30)
@@ -142,7 +142,7 @@ def test_random_tile_graphs(case):
     rq, rk, rv = oracle.gt_bwd(rp, ci, t["q"], t["k"], t["v"], t["dout"])
     for name, got, ref in (("out", out, ro), ("lse", lse, rl), ("dq", dq, rq), ("dk", dk, rk),
                            ("dv", dv, rv)):
-        assert rel_err(host(got), ref) <= TOL["bf16"], name
+        assert rel_err(host(got), ref) <= (TOL_LSE if name == "lse" else TOL["bf16"]), name
 
 
 @pytest.mark.parametrize("case", range(32))
