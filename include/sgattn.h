@@ -150,7 +150,12 @@ typedef enum sgat_array {
     SGAT_ARR_ROW_TPOS = 18,   /* int32 [nnz]: transposed-CSR position of each CSR edge
                                  (the inverse of SGAT_ARR_COL_EDGE); built for
                                  edge_order 2, and for 0 when nnz > 2^21; else empty     */
-    SGAT_ARR_COUNT = 19
+    SGAT_ARR_RES_ROW = 19,    /* int32 [residual_edges]: destination of each residual edge */
+    SGAT_ARR_RES_COLSRC = 20, /* int32 [residual_edges]: source of each transposed
+                                 residual entry                                         */
+    SGAT_ARR_TILE_ROW_BYCOL = 21,/* int32 [tiles]: block row of the tiles in
+                                 SGAT_ARR_TILE_BYCOL order                              */
+    SGAT_ARR_COUNT = 22
 } sgat_array;
 
 /* One unit of work of the gather kernels: `len` consecutive edges starting at

@@ -144,6 +144,12 @@ def transpose(rowptr: np.ndarray, colidx: np.ndarray, edge_ids: bool = False):
     return colptr, dst[order].astype(np.int32)
 
 
+def expand_pointer(ptr: np.ndarray) -> np.ndarray:
+    """The row of every entry of a CSR-like pointer array."""
+    ptr = np.asarray(ptr, dtype=np.int64)
+    return np.repeat(np.arange(ptr.size - 1, dtype=np.int64), np.diff(ptr)).astype(np.int32)
+
+
 def transposed_positions(col_edge: np.ndarray) -> np.ndarray:
     """Position in the transposed CSR of every CSR edge: entry q of the
     transposed CSR is CSR edge col_edge[q], so edge col_edge[q] sits at q."""

@@ -25,7 +25,8 @@ REDUCE_OPS = {"min": REDUCE_MIN, "max": REDUCE_MAX}
 (ARR_ROW_ITEMS, ARR_ROW_SPLITS, ARR_COLPTR, ARR_ROWIDX, ARR_COL_ITEMS, ARR_COL_SPLITS,
  ARR_TILE_ROWPTR, ARR_TILE_COL, ARR_TILE_MASK, ARR_RES_ROWPTR, ARR_RES_COLIDX,
  ARR_TILE_ROW, ARR_TILE_COLPTR, ARR_TILE_BYCOL, ARR_RES_COLPTR, ARR_RES_ROWIDX,
- ARR_COL_EDGE, ARR_RES_COL_EDGE, ARR_ROW_TPOS) = range(19)
+ ARR_COL_EDGE, ARR_RES_COL_EDGE, ARR_ROW_TPOS, ARR_RES_ROW, ARR_RES_COLSRC,
+ ARR_TILE_ROW_BYCOL) = range(22)
 
 STATUS = {0: "OK", 1: "INVALID_ARGUMENT", 2: "INVALID_CSR", 3: "WORKSPACE_TOO_SMALL",
           4: "PLAN_MISMATCH", 5: "HIP_ERROR", 6: "NOT_UPLOADED", 7: "OUT_OF_HOST_MEMORY",
@@ -48,7 +49,8 @@ ARRAY_DTYPES = {
     ARR_TILE_COLPTR: np.dtype("<i8"), ARR_TILE_BYCOL: np.dtype("<i4"),
     ARR_RES_COLPTR: np.dtype("<i8"), ARR_RES_ROWIDX: np.dtype("<i4"),
     ARR_COL_EDGE: np.dtype("<i4"), ARR_RES_COL_EDGE: np.dtype("<i4"),
-    ARR_ROW_TPOS: np.dtype("<i4"),
+    ARR_ROW_TPOS: np.dtype("<i4"), ARR_RES_ROW: np.dtype("<i4"), ARR_RES_COLSRC: np.dtype("<i4"),
+    ARR_TILE_ROW_BYCOL: np.dtype("<i4"),
 }
 
 

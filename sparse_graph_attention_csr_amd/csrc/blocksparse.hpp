@@ -55,6 +55,7 @@ struct BsFwdArgs {
     const uint16_t* tile_mask;
     const int64_t* res_rowptr;
     const int32_t* res_colidx;
+    const int32_t* res_row;      // destination of each residual edge
     const void *Q, *K, *V;
     void* out;
     float* lse;
@@ -83,141 +84,162 @@ __device__ __forceinline__ s16x4_t lds_read_tr16(const uint16_t* p)
         (__attribute__((address_space(3))) s16x4_t*)(p));
 }
 
-// V tile lanes: lane l loads and stores row vrow(l) = l % 8 + 8 * (l / 32),
-// 16-byte chunk vchunk(l) = (l / 8) % 4 of each 32-channel slab (the V tile
-// goes only through LDS, so any assignment of its chunks to lanes works; this
-// one has every 16 lanes store 8 rows x 2 chunks).
-__device__ __forceinline__ int vrow(int l) { return (l & 7) + 8 * (l >> 5); }
-__device__ __forceinline__ int vchunk(int l) { return (l >> 3) & 3; }
-
-// Tiles whose lanes are fixed by the MFMA operand layout (lane (i, g) holds
-// row i, 16-byte chunk 4s + g of every 32-channel slab s) are stored at row
-// stride LDV with the chunks of rows 8..15 swapped in pairs (chunk ^ 1), so
-// that rows i and i + 8, stored by the same instruction, start on different
-// banks.
+// Base of lane (i, g)'s transposed reads of a row-major LDS tile: block s
+// (channels 16s..16s+15 of rows 4g..4g+3) is at + 16 s; lane i of the group
+// addresses row 4g + i/4, channels 4(i%4)..+3.
 template <int D>
-__device__ __forceinline__ void store_operand_tile(uint16_t* t, const Frag (&f)[Shape<D>::KS],
-                                                   int i, int g)
+__device__ __forceinline__ const uint16_t* tr_base(const uint16_t* t, int i, int g)
 {
-    uint16_t* row = t + i * Shape<D>::LDV + 8 * (g ^ ((i >> 3) & 1));
-#pragma unroll
-    for (int s = 0; s < Shape<D>::KS; ++s) *reinterpret_cast<Frag*>(row + 32 * s) = f[s];
+    return t + (4 * g + (i >> 2)) * Shape<D>::LDV + 4 * (i & 3);
 }
 
-// Base address of lane (i, g)'s transposed reads of such a tile: block s
-// (channels 16s..16s+15, rows 4g..4g+3 into the MFMA A operand) is at + 16 s.
-// Lane i of the group addresses row 4g + i/4, channels 16s + 4(i%4).
-template <int D>
-__device__ __forceinline__ const uint16_t* operand_tr_base(const uint16_t* t, int i, int g)
-{
-    return t + (4 * g + (i >> 2)) * Shape<D>::LDV + 8 * (((i >> 1) & 1) ^ (g >> 1)) + 4 * (i & 1);
-}
+// ---------------------------------------------------------------------------
+// the tiles of one 16-node block
+// ---------------------------------------------------------------------------
 
-// Start offsets of rows 1..15 of a 16-row (or 16-source) block in a pointer
-// array, loaded once per block (rows past the end start at ptr[hi]).
-struct BlockStarts {
-    int64_t v[kTileDim];
-    __device__ __forceinline__ void load(const int64_t* ptr, int64_t lo, int64_t hi)
+// A workgroup owns one block of 16 nodes (a tile row, or a tile column in the
+// column pass): its dense tiles [tb, tb + nd) of the tile list, then its
+// residual entries [rb, re) in pseudo-tiles of 16; lo is its first node.
+// (Walking several consecutive blocks per workgroup, with the tile pipeline
+// running on across block boundaries, was measured slower: 1, 2, 4 and 8
+// blocks per workgroup gave 1.67, 1.72, 1.84 and 1.88 ms per community-graph
+// step, as the fewer, longer workgroups leave more of the chip idle at the end.)
+struct Blk {
+    int64_t tb, nd, rb, re, lo;
+
+    __device__ __forceinline__ void load(const int64_t* tile_ptr, const int64_t* res_ptr,
+                                         int64_t b, int64_t n)
     {
-#pragma unroll
-        for (int q = 1; q < kTileDim; ++q) v[q] = ptr[lo + q < hi ? lo + q : hi];
+        lo = b * kTileDim;
+        const int64_t hi = lo + kTileDim < n ? lo + kTileDim : n;
+        tb = tile_ptr[b];
+        nd = tile_ptr[b + 1] - tb;
+        rb = res_ptr[lo];
+        re = res_ptr[hi];
     }
-    // position of edge e among the block's rows
-    __device__ __forceinline__ int row_of(int64_t e) const
-    {
-        int r = 0;
-#pragma unroll
-        for (int q = 1; q < kTileDim; ++q) r += v[q] <= e ? 1 : 0;
-        return r;
-    }
+    __device__ __forceinline__ int64_t count() const { return nd + (re - rb + 15) / 16; }
 };
 
-// Tiles of one 16-row block, in order: its dense tiles, then its residual
-// edges in pseudo-tiles of 16. Tile k is described by a RowRef: the node of
-// column l%16 and this lane's 4 edge bits (row l%16, columns 4g..4g+3).
-// fetch() issues the raw loads of a description, decode() builds it; k is
-// uniform across the wave.
+// What a lane needs of a tile of a row block, loaded two tiles ahead. Dense
+// tile: its block column and the lane's row mask word (row i; bit c = edge
+// from column c). Pseudo-tile: the source of its column i (residual entry i
+// of the tile) and that edge's row within the block (-1 past the block's
+// residual entries).
+struct RowDesc {
+    int32_t col, aux;
+};
+
+template <class A>
+__device__ __forceinline__ RowDesc row_fetch(const A& a, const Blk& B, int64_t k, int i)
+{
+    RowDesc d;
+    if (k < B.nd) {
+        const int64_t t = B.tb + k;
+        d.col = a.tile_col[t];
+        d.aux = a.tile_mask[t * kTileDim + i];
+    } else {
+        const int64_t e = B.rb + (k - B.nd) * kTileDim + i;
+        d.col = e < B.re ? a.res_colidx[e] : 0;
+        d.aux = e < B.re ? a.res_row[e] - static_cast<int32_t>(B.lo) : -1;
+    }
+    return d;
+}
+
+// The source node of the lane's operand row i and its four edge bits (row i,
+// columns 4g..4g+3).
 struct RowRef {
     int64_t src;
     uint32_t valid;
 };
 
-struct RowTiles {
-    int64_t n, tb, nd, rb, re;
-    const int32_t* tile_col;
-    const uint16_t* tile_mask;
-    const int32_t* res_colidx;
-    BlockStarts starts;
+__device__ __forceinline__ RowRef row_decode(const Blk& B, int64_t k, const RowDesc& d, int i,
+                                             int g, int64_t n)
+{
+    RowRef r;
+    if (k < B.nd) {
+        r.src = min(static_cast<int64_t>(d.col) * kTileDim + i, n - 1);
+        r.valid = (static_cast<uint32_t>(d.aux) >> (4 * g)) & 0xFu;
+    } else {
+        r.src = d.col;
+        r.valid = 0;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) r.valid |= (__shfl(d.aux, 4 * g + q) == i ? 1u : 0u) << q;
+    }
+    return r;
+}
 
-    __device__ __forceinline__ int64_t count() const { return nd + (re - rb + 15) / 16; }
+// Whole-line tile loads. In the MFMA operand layout one load instruction
+// reads 64 bytes of each of 16 rows (lane l: row l % 16), so it touches 16
+// cache lines and uses half of each, and the L1 keeps twice the outstanding
+// lines per byte; the TA then waits on the L1 for a large share of the time.
+// Instead, instruction j reads rows [j*RPI, (j+1)*RPI) whole: the LPR lanes of
+// a row read its 2D-byte head slice contiguously (4 rows x 256 bytes, 8 full
+// lines, at D = 128). The rows go to LDS, and the MFMA operands are read
+// back from there.
+template <int D>
+struct TileRows {
+    static constexpr int LPR = 2 * D / 16;          // lanes per row
+    static constexpr int RPI = kWave / LPR;         // rows per load instruction
+    static constexpr int NI = kTileDim / RPI;       // load instructions per tile
+    static_assert(NI * RPI == kTileDim, "");
+    Frag r[NI];
 
-    __device__ __forceinline__ void fetch(int64_t k, int i, int32_t& col, uint32_t& word) const
+    // src: this lane's tile row node (row l % 16, in lanes 0..15 of each group)
+    __device__ __forceinline__ void load(const void* X, int64_t src, int64_t HD, int64_t hoff,
+                                         int l)
     {
-        if (k < nd) {
-            const int64_t t = tb + k;
-            col = tile_col[t];
-            word = tile_mask[t * kTileDim + i];
-        } else {
-            const int64_t e = rb + (k - nd) * 16 + i;
-            col = e < re ? res_colidx[e] : 0;
-            word = 0;
+#pragma unroll
+        for (int j = 0; j < NI; ++j) {
+            const int64_t node = __shfl(src, j * RPI + l / LPR);
+            r[j] = ldg<SGAT_BF16>(X, node * HD + hoff + 8 * (l % LPR));
         }
     }
-
-    __device__ __forceinline__ RowRef decode(int64_t k, int i, int g, int32_t col, uint32_t word) const
+    // into an LDS tile of 16 rows at stride Shape<D>::LDV
+    __device__ __forceinline__ void store(uint16_t* t, int l) const
     {
-        RowRef r;
-        if (k < nd) {
-            r.src = min(static_cast<int64_t>(col) * kTileDim + i, n - 1);
-            r.valid = (word >> (4 * g)) & 0xFu;
-        } else {
-            const int64_t e = rb + (k - nd) * 16 + i;   // column i is residual edge e
-            const int rr = e < re ? starts.row_of(e) : -1;
-            r.src = col;
-            r.valid = 0;
 #pragma unroll
-            for (int q = 0; q < 4; ++q) r.valid |= (__shfl(rr, 4 * g + q) == i ? 1u : 0u) << q;
-        }
-        return r;
+        for (int j = 0; j < NI; ++j)
+            *reinterpret_cast<Frag*>(t + (j * RPI + l / LPR) * Shape<D>::LDV + 8 * (l % LPR)) = r[j];
     }
 };
 
+// The MFMA A operand of an LDS tile for k-step s: lane (i, g) holds row i,
+// channels 32s + 8g .. +7.
+template <int D>
+__device__ __forceinline__ bf16x8_t lds_operand(const uint16_t* t, int s, int i, int g)
+{
+    return *reinterpret_cast<const bf16x8_t*>(t + i * Shape<D>::LDV + 32 * s + 8 * g);
+}
+
 template <int D>
 struct FwdTile {
-    Frag kf[Shape<D>::KS];
-    uint4 vr[Shape<D>::SPL];
-    // kbase: row l%16's node row (K, MFMA operand layout); vbase: row
-    // vrow(l)'s node row (V, staged through LDS)
-    __device__ __forceinline__ void load(const void* K, const void* V, int64_t kbase,
-                                         int64_t vbase, int g, int l)
+    TileRows<D> k, v;
+    __device__ __forceinline__ void load(const void* K, const void* V, int64_t src, int64_t HD,
+                                         int64_t hoff, int l)
     {
-#pragma unroll
-        for (int s = 0; s < Shape<D>::KS; ++s) kf[s] = ldg<SGAT_BF16>(K, kbase + 32 * s + 8 * g);
-#pragma unroll
-        for (int q = 0; q < Shape<D>::SPL; ++q)
-            vr[q] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(V) + vbase +
-                                                    32 * q + 8 * vchunk(l));
+        k.load(K, src, HD, hoff, l);
+        v.load(V, src, HD, hoff, l);
     }
 };
 
 // One forward tile for one head, in two phases. Phase A consumes the tile's
-// registers (S^T = K Q^T, V into LDS), so the next tile's loads can refill
-// them before phase B: the masked online-softmax update of (m, lsum) and
-// O^T += V^T P^T from LDS.
+// registers (K and V rows into LDS, S^T = K Q^T with K read back in operand
+// layout), so the next tile's loads can refill them before phase B: the
+// masked online-softmax update of (m, lsum) and O^T += V^T P^T from LDS.
 template <int D>
 __device__ __forceinline__ f32x4_t fwd_phase_a(const FwdTile<D>& tl,
-                                               const bf16x8_t (&qf)[Shape<D>::KS], uint16_t* vs,
-                                               int l)
+                                               const bf16x8_t (&qf)[Shape<D>::KS], uint16_t* ks,
+                                               uint16_t* vs, int l, int i, int g)
 {
     using S = Shape<D>;
+    tl.k.store(ks, l);
+    tl.v.store(vs, l);
+    __builtin_amdgcn_wave_barrier();
     f32x4_t st = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < S::KS; ++s)
-        st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, tl.kf[s]), qf[s],
-                                                     st, 0, 0, 0);
-#pragma unroll
-    for (int q = 0; q < S::SPL; ++q)
-        *reinterpret_cast<uint4*>(vs + vrow(l) * S::LDV + 32 * q + 8 * vchunk(l)) = tl.vr[q];
+        st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lds_operand<D>(ks, s, i, g), qf[s], st, 0, 0, 0);
+    __builtin_amdgcn_wave_barrier();
     return st;
 }
 
@@ -262,7 +284,7 @@ __device__ __forceinline__ void fwd_phase_b(const f32x4_t& st, uint32_t valid, f
     __builtin_amdgcn_wave_barrier();
     // A operand of block s: V[4g + kk][16s + i] for kk = 0..3, one transposed
     // read (lane 4k + j/4 of the group addresses row 4g + k, channels 16s + 4(j%4))
-    const uint16_t* vt = vs + (4 * g + (i >> 2)) * S::LDV + 4 * (i & 3);
+    const uint16_t* vt = tr_base<D>(vs, i, g);
 #pragma unroll
     for (int s = 0; s < S::NB; ++s) {
         const s16x4_t va = lds_read_tr16(vt + 16 * s);
@@ -279,6 +301,38 @@ __device__ __forceinline__ void store_tile_rows(void* dst, int64_t off, const f3
     *reinterpret_cast<uint2*>(static_cast<uint16_t*>(dst) + off) = w;
 }
 
+// Rows of a finished row block, head h: out = O / lsum and lse (rows without
+// edges: 0 and -inf).
+template <int D>
+__device__ __forceinline__ void fwd_finish(const BsFwdArgs& a, int64_t lo, int h, int64_t HD,
+                                           float m, float lsum, const f32x4_t (&acc)[Shape<D>::NB],
+                                           int i, int g)
+{
+    const int64_t row = lo + i;
+    if (row >= a.n) return;
+    const int64_t hoff = static_cast<int64_t>(h) * D;
+    const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+#pragma unroll
+    for (int s = 0; s < Shape<D>::NB; ++s)
+        store_tile_rows(a.out, row * HD + hoff + 16 * s + 4 * g, acc[s], inv);
+    if (g == 0) a.lse[row * a.H + h] = lsum > 0.f ? (m + __log2f(lsum)) * kLn2 : kNegInf;
+}
+
+// Q rows of a row block for head h (A operand of S^T = K Q^T): lane (i, g)
+// holds row lo + i, chunk 8g of each 32-channel slab.
+template <int D>
+__device__ __forceinline__ void load_block_rows(const void* X, int64_t lo, int64_t n, int64_t HD,
+                                                int64_t hoff, int i, int g,
+                                                bf16x8_t (&x)[Shape<D>::KS])
+{
+    const int64_t row = lo + i;
+#pragma unroll
+    for (int s = 0; s < Shape<D>::KS; ++s) {
+        x[s] = bf16x8_t{};
+        if (row < n) x[s] = ld_bf16x8(X, row * HD + hoff + 32 * s + 8 * g);
+    }
+}
+
 // At least 3 waves per SIMD: at D = 128 the compiler would otherwise keep
 // the accumulators twice (VGPR copies of MFMA results in AGPRs) and stop at 2;
 // with the target it keeps them in VGPRs only, without spilling.
@@ -286,37 +340,23 @@ template <int D>
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) void gt_bs_fwd(BsFwdArgs a)
 {
     using S = Shape<D>;
+    __shared__ __attribute__((aligned(16))) uint16_t ks_all[kWavesPerBlock][16 * S::LDV];
     __shared__ __attribute__((aligned(16))) uint16_t vs_all[kWavesPerBlock][16 * S::LDV];
     const int64_t br = logical_block();
     if (br >= a.n_tile_rows) return;          // the whole workgroup leaves; no barrier follows
     const int w = wave_id();
     const int l = threadIdx.x & 63, i = l & 15, g = l >> 4;
     const int64_t HD = static_cast<int64_t>(a.H) * D;
-    RowTiles tiles;
-    const int64_t r_lo = br * kTileDim;
-    const int64_t r_hi = r_lo + kTileDim < a.n ? r_lo + kTileDim : a.n;
-    tiles.n = a.n;
-    tiles.tb = a.tile_rowptr[br];
-    tiles.nd = a.tile_rowptr[br + 1] - tiles.tb;
-    tiles.rb = a.res_rowptr[r_lo];
-    tiles.re = a.res_rowptr[r_hi];
-    tiles.tile_col = a.tile_col;
-    tiles.tile_mask = a.tile_mask;
-    tiles.res_colidx = a.res_colidx;
-    tiles.starts.load(a.res_rowptr, r_lo, r_hi);
-    const int64_t nt = tiles.count();
-    const int64_t row = r_lo + i;
-    const bool row_ok = row < a.n;
+    Blk B;
+    B.load(a.tile_rowptr, a.res_rowptr, br, a.n);
+    const int64_t nt = B.count();
+    uint16_t* ks = ks_all[w];
     uint16_t* vs = vs_all[w];
 
     for (int h = w; h < a.H; h += kWavesPerBlock) {
         const int64_t hoff = static_cast<int64_t>(h) * D;
         bf16x8_t qf[S::KS];
-#pragma unroll
-        for (int s = 0; s < S::KS; ++s) {
-            qf[s] = bf16x8_t{};
-            if (row_ok) qf[s] = ld_bf16x8(a.Q, row * HD + hoff + 32 * s + 8 * g);
-        }
+        load_block_rows<D>(a.Q, B.lo, a.n, HD, hoff, i, g, qf);
         float m = kNegInf, lsum = 0.f;
         f32x4_t acc[S::NB];
 #pragma unroll
@@ -327,36 +367,23 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
         // consumed them, and arrives during phase B
         FwdTile<D> tile;
         RowRef rnext{0, 0};
-        int32_t col2 = 0;
-        uint32_t word2 = 0;
+        RowDesc d2{0, -1};
         if (nt > 0) {
-            int32_t c0;
-            uint32_t w0;
-            tiles.fetch(0, i, c0, w0);
-            rnext = tiles.decode(0, i, g, c0, w0);
-            tile.load(a.K, a.V, rnext.src * HD + hoff, __shfl(rnext.src, vrow(l)) * HD + hoff, g, l);
+            rnext = row_decode(B, 0, row_fetch(a, B, 0, i), i, g, a.n);
+            tile.load(a.K, a.V, rnext.src, HD, hoff, l);
         }
-        if (nt > 1) tiles.fetch(1, i, col2, word2);
+        if (nt > 1) d2 = row_fetch(a, B, 1, i);
         for (int64_t k = 0; k < nt; ++k) {
             const uint32_t valid = rnext.valid;
-            const f32x4_t st = fwd_phase_a<D>(tile, qf, vs, l);
+            const f32x4_t st = fwd_phase_a<D>(tile, qf, ks, vs, l, i, g);
             if (k + 1 < nt) {
-                rnext = tiles.decode(k + 1, i, g, col2, word2);
-                if (k + 2 < nt) tiles.fetch(k + 2, i, col2, word2);
-                tile.load(a.K, a.V, rnext.src * HD + hoff, __shfl(rnext.src, vrow(l)) * HD + hoff,
-                          g, l);
+                rnext = row_decode(B, k + 1, d2, i, g, a.n);
+                if (k + 2 < nt) d2 = row_fetch(a, B, k + 2, i);
+                tile.load(a.K, a.V, rnext.src, HD, hoff, l);
             }
             fwd_phase_b<D>(st, valid, m, lsum, acc, vs, a.scale2, i, g);
         }
-
-        if (row_ok) {
-            const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
-#pragma unroll
-            for (int s = 0; s < S::NB; ++s)
-                store_tile_rows(a.out, row * HD + hoff + 16 * s + 4 * g, acc[s], inv);
-            if (g == 0)
-                a.lse[row * a.H + h] = lsum > 0.f ? (m + __log2f(lsum)) * kLn2 : kNegInf;
-        }
+        fwd_finish<D>(a, B.lo, h, HD, m, lsum, acc, i, g);
     }
 }
 
@@ -373,7 +400,6 @@ struct BsBwdArgs {
     const int64_t* tile_rowptr;
     const int32_t* tile_col;
     const uint16_t* tile_mask;
-    const int32_t* tile_row;
     const int64_t* tile_colptr;
     const int32_t* tile_bycol;
     const int64_t* res_rowptr;
@@ -381,6 +407,9 @@ struct BsBwdArgs {
     const int64_t* res_colptr;
     const int32_t* res_rowidx;
     const int32_t* res_col_edge;
+    const int32_t* res_row;         // destination of each residual edge
+    const int32_t* res_colsrc;      // source of each transposed residual entry
+    const int32_t* tile_row_bycol;  // block row of each tile, in tile_bycol order
     const void *Q, *K, *V, *O, *dO;
     const float* lse;
     // weights and dS of every edge, from the tile-row pass to the tile-column
@@ -395,38 +424,39 @@ struct BsBwdArgs {
 
 template <int D>
 struct RowBwdTile {
-    Frag kf[Shape<D>::KS], vf[Shape<D>::KS];
-    __device__ __forceinline__ void load(const void* K, const void* V, int64_t base, int g)
+    TileRows<D> k, v;
+    __device__ __forceinline__ void load(const void* K, const void* V, int64_t src, int64_t HD,
+                                         int64_t hoff, int l)
     {
-#pragma unroll
-        for (int s = 0; s < Shape<D>::KS; ++s) {
-            kf[s] = ldg<SGAT_BF16>(K, base + 32 * s + 8 * g);
-            vf[s] = ldg<SGAT_BF16>(V, base + 32 * s + 8 * g);
-        }
+        k.load(K, src, HD, hoff, l);
+        v.load(V, src, HD, hoff, l);
     }
 };
 
 // Tile-row step: rows i = l%16, columns 4g..4g+3 in this lane;
-// dS = P (dP - Delta_i) and dQ^T += K^T dS^T (K transposed through LDS).
-// Phase A consumes the tile registers (S, dP; K into LDS); phase B forms dS
-// and accumulates from LDS, while the next tile's loads refill the registers.
+// dS = P (dP - Delta_i) and dQ^T += K^T dS^T (K read transposed from LDS).
+// Phase A consumes the tile registers (K and V rows into LDS; S and dP with
+// the operands read back); phase B forms dS and accumulates from LDS, while
+// the next tile's loads refill the registers.
 template <int D>
 __device__ __forceinline__ void row_bwd_phase_a(const RowBwdTile<D>& tl,
                                                 const bf16x8_t (&qf)[Shape<D>::KS],
                                                 const bf16x8_t (&df)[Shape<D>::KS], f32x4_t& st,
-                                                f32x4_t& dp, uint16_t* ks, int i, int g)
+                                                f32x4_t& dp, uint16_t* ks, uint16_t* vs, int l,
+                                                int i, int g)
 {
     using S = Shape<D>;
+    tl.k.store(ks, l);
+    tl.v.store(vs, l);
+    __builtin_amdgcn_wave_barrier();
     st = f32x4_t{0.f, 0.f, 0.f, 0.f};
     dp = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < S::KS; ++s) {
-        st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, tl.kf[s]), qf[s],
-                                                     st, 0, 0, 0);
-        dp = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, tl.vf[s]), df[s],
-                                                     dp, 0, 0, 0);
+        st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lds_operand<D>(ks, s, i, g), qf[s], st, 0, 0, 0);
+        dp = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lds_operand<D>(vs, s, i, g), df[s], dp, 0, 0, 0);
     }
-    store_operand_tile<D>(ks, tl.kf, i, g);
+    __builtin_amdgcn_wave_barrier();
 }
 
 // Tile-row step, phase B: P and dS of the lane's four entries (also staged
@@ -451,7 +481,7 @@ __device__ __forceinline__ void row_bwd_phase_b(const f32x4_t& st, const f32x4_t
     *reinterpret_cast<s16x4_t*>(&pt[0][i * kTileDim + 4 * g]) = s16x4_t{pb[0], pb[1], pb[2], pb[3]};
     *reinterpret_cast<s16x4_t*>(&pt[1][i * kTileDim + 4 * g]) = b;
     __builtin_amdgcn_wave_barrier();
-    const uint16_t* kt = operand_tr_base<D>(ks, i, g);
+    const uint16_t* kt = tr_base<D>(ks, i, g);
 #pragma unroll
     for (int s = 0; s < S::NB; ++s) {
         const s16x4_t ka = lds_read_tr16(kt + 16 * s);   // K[4g + kk][16s + i], kk = 0..3
@@ -463,27 +493,80 @@ __device__ __forceinline__ void row_bwd_phase_b(const f32x4_t& st, const f32x4_t
 // Hands tile k's P and dS, staged row-major in pt by phase B, to the
 // tile-column pass. Dense tile: read back with the transposing read so that
 // lane (c, g) holds rows 4g..4g+3 of column c (the column pass's B operand),
-// and stored as that lane's 8 bytes. Residual pseudo-tile: lane c < 16 stores
-// the pair of its column's edge e (at the edge's row) as one word.
-__device__ __forceinline__ void hand_off(const BsBwdArgs& a, const RowTiles& tiles, int64_t k,
-                                         int h, uint16_t (*pt)[kTileDim * kTileDim], int l,
-                                         int i, int g)
+// and stored as that lane's 8 bytes. Residual pseudo-tile: lane c < 16
+// stores the pair of its column's edge e at the edge's row `aux` as one word.
+__device__ __forceinline__ void hand_off(const BsBwdArgs& a, const Blk& B, int64_t k, int32_t aux,
+                                         int h, uint16_t (*pt)[kTileDim * kTileDim], int l, int i,
+                                         int g)
 {
-    if (k < tiles.nd) {
+    if (k < B.nd) {
         // lane m of a 16-lane group addresses row 4g + m / 4, columns 4 (m % 4)..+3
         const int off = (4 * g + i / 4) * kTileDim + 4 * (i % 4);
-        uint2* dst = a.tile_pd + (static_cast<int64_t>(tiles.tb + k) * a.H + h) * 2 * kWave;
+        uint2* dst = a.tile_pd + (static_cast<int64_t>(B.tb + k) * a.H + h) * 2 * kWave;
         dst[l] = __builtin_bit_cast(uint2, lds_read_tr16(&pt[0][off]));
         dst[kWave + l] = __builtin_bit_cast(uint2, lds_read_tr16(&pt[1][off]));
     } else {
-        const int64_t e = tiles.rb + (k - tiles.nd) * 16 + l;   // column l is residual edge e
-        if (l < kTileDim && e < tiles.re) {
-            const int r = tiles.starts.row_of(e);
-            a.res_pd[e * a.H + h] = static_cast<uint32_t>(pt[0][r * kTileDim + l]) |
-                                    (static_cast<uint32_t>(pt[1][r * kTileDim + l]) << 16);
+        const int64_t e = B.rb + (k - B.nd) * kTileDim + l;   // column l is residual edge e
+        if (l < kTileDim && e < B.re) {
+            a.res_pd[e * a.H + h] = static_cast<uint32_t>(pt[0][aux * kTileDim + l]) |
+                                    (static_cast<uint32_t>(pt[1][aux * kTileDim + l]) << 16);
         }
     }
     __builtin_amdgcn_wave_barrier();
+}
+
+// The per-row operands of a row block for head h: Q and dO (A operands of S
+// and dP), O (for Delta) and lse.
+template <int D>
+struct RowBlockRows {
+    bf16x8_t qf[Shape<D>::KS], df[Shape<D>::KS];
+    Frag of[Shape<D>::KS];
+    float lse;
+
+    __device__ __forceinline__ void load(const BsBwdArgs& a, int64_t lo, int64_t HD, int64_t hoff,
+                                         int h, int i, int g)
+    {
+        const int64_t row = lo + i;
+        lse = 0.f;
+#pragma unroll
+        for (int s = 0; s < Shape<D>::KS; ++s) {
+            qf[s] = bf16x8_t{};
+            df[s] = bf16x8_t{};
+            of[s] = frag_zero();
+            if (row < a.n) {
+                const int64_t o = row * HD + hoff + 32 * s + 8 * g;
+                qf[s] = ld_bf16x8(a.Q, o);
+                df[s] = __builtin_bit_cast(bf16x8_t, ldg<SGAT_BF16>(a.dO, o));
+                of[s] = ldg<SGAT_BF16>(a.O, o);
+            }
+        }
+        if (row < a.n) lse = a.lse[row * a.H + h];
+    }
+    // Delta of row i (the four lanes of the row hold its D channels) and lse
+    // in base 2
+    __device__ __forceinline__ void stats(float& delta, float& lse2) const
+    {
+        float d = 0.f;
+#pragma unroll
+        for (int s = 0; s < Shape<D>::KS; ++s)
+            d += dot<SGAT_BF16>(__builtin_bit_cast(Frag, df[s]), of[s]);
+        d += __shfl_xor(d, 16);
+        d += __shfl_xor(d, 32);
+        delta = d;
+        lse2 = lse * kLog2e;
+    }
+};
+
+template <int D>
+__device__ __forceinline__ void store_block_rows(void* dst, int64_t n, int64_t lo, int64_t HD,
+                                                 int64_t hoff, const f32x4_t (&acc)[Shape<D>::NB],
+                                                 float sc, int i, int g)
+{
+    const int64_t row = lo + i;
+    if (row >= n) return;
+#pragma unroll
+    for (int s = 0; s < Shape<D>::NB; ++s)
+        store_tile_rows(dst, row * HD + hoff + 16 * s + 4 * g, acc[s], sc);
 }
 
 template <int D>
@@ -491,6 +574,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
 {
     using S = Shape<D>;
     __shared__ __attribute__((aligned(16))) uint16_t ks_all[kWavesPerBlock][16 * S::LDV];
+    __shared__ __attribute__((aligned(16))) uint16_t vs_all[kWavesPerBlock][16 * S::LDV];
     // one 16x16 bf16 tile of P and one of dS, row-major, to transpose them
     __shared__ __attribute__((aligned(16))) uint16_t pt_all[kWavesPerBlock][2][kTileDim * kTileDim];
     const int64_t br = logical_block();
@@ -498,42 +582,16 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
     const int w = wave_id();
     const int l = threadIdx.x & 63, i = l & 15, g = l >> 4;
     const int64_t HD = static_cast<int64_t>(a.H) * D;
-    RowTiles tiles;
-    const int64_t r_lo = br * kTileDim;
-    const int64_t r_hi = r_lo + kTileDim < a.n ? r_lo + kTileDim : a.n;
-    tiles.n = a.n;
-    tiles.tb = a.tile_rowptr[br];
-    tiles.nd = a.tile_rowptr[br + 1] - tiles.tb;
-    tiles.rb = a.res_rowptr[r_lo];
-    tiles.re = a.res_rowptr[r_hi];
-    tiles.tile_col = a.tile_col;
-    tiles.tile_mask = a.tile_mask;
-    tiles.res_colidx = a.res_colidx;
-    tiles.starts.load(a.res_rowptr, r_lo, r_hi);
-    const int64_t nt = tiles.count();
-    const int64_t row = r_lo + i;
-    const bool row_ok = row < a.n;
+    Blk B;
+    B.load(a.tile_rowptr, a.res_rowptr, br, a.n);
+    const int64_t nt = B.count();
     uint16_t* ks = ks_all[w];
+    uint16_t* vs = vs_all[w];
 
     for (int h = w; h < a.H; h += kWavesPerBlock) {
         const int64_t hoff = static_cast<int64_t>(h) * D;
-        bf16x8_t qf[S::KS], df[S::KS];
-        float dsum = 0.f, lse2 = 0.f;
-#pragma unroll
-        for (int s = 0; s < S::KS; ++s) {
-            qf[s] = bf16x8_t{};
-            df[s] = bf16x8_t{};
-            if (row_ok) {
-                const int64_t o = row * HD + hoff + 32 * s + 8 * g;
-                qf[s] = ld_bf16x8(a.Q, o);
-                const Frag d = ldg<SGAT_BF16>(a.dO, o);
-                df[s] = __builtin_bit_cast(bf16x8_t, d);
-                dsum += dot<SGAT_BF16>(d, ldg<SGAT_BF16>(a.O, o));
-            }
-        }
-        dsum += __shfl_xor(dsum, 16);
-        dsum += __shfl_xor(dsum, 32);
-        if (row_ok) lse2 = a.lse[row * a.H + h] * kLog2e;
+        RowBlockRows<D> rows;
+        rows.load(a, B.lo, HD, hoff, h, i, g);
         f32x4_t acc[S::NB];
 #pragma unroll
         for (int s = 0; s < S::NB; ++s) acc[s] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -542,113 +600,111 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
         // tile registers once phase A of tile k has consumed them
         RowBwdTile<D> tile;
         RowRef rnext{0, 0};
-        int32_t col2 = 0;
-        uint32_t word2 = 0;
+        int32_t auxn = -1;
+        RowDesc d2{0, -1};
         if (nt > 0) {
-            int32_t c0;
-            uint32_t w0;
-            tiles.fetch(0, i, c0, w0);
-            rnext = tiles.decode(0, i, g, c0, w0);
-            tile.load(a.K, a.V, rnext.src * HD + hoff, g);
+            const RowDesc d0 = row_fetch(a, B, 0, i);
+            rnext = row_decode(B, 0, d0, i, g, a.n);
+            auxn = d0.aux;
+            tile.load(a.K, a.V, rnext.src, HD, hoff, l);
         }
-        if (nt > 1) tiles.fetch(1, i, col2, word2);
+        if (nt > 1) d2 = row_fetch(a, B, 1, i);
+        float delta, lse2;
+        rows.stats(delta, lse2);
         for (int64_t k = 0; k < nt; ++k) {
             const uint32_t valid = rnext.valid;
-            f32x4_t st, dp;
-            row_bwd_phase_a<D>(tile, qf, df, st, dp, ks, i, g);
+            const int32_t aux = auxn;
+            f32x4_t st, dpv;
+            row_bwd_phase_a<D>(tile, rows.qf, rows.df, st, dpv, ks, vs, l, i, g);
             if (k + 1 < nt) {
-                rnext = tiles.decode(k + 1, i, g, col2, word2);
-                if (k + 2 < nt) tiles.fetch(k + 2, i, col2, word2);
-                tile.load(a.K, a.V, rnext.src * HD + hoff, g);
+                rnext = row_decode(B, k + 1, d2, i, g, a.n);
+                auxn = d2.aux;
+                if (k + 2 < nt) d2 = row_fetch(a, B, k + 2, i);
+                tile.load(a.K, a.V, rnext.src, HD, hoff, l);
             }
-            row_bwd_phase_b<D>(st, dp, valid, lse2, dsum, acc, ks, a.scale2, i, g, pt_all[w]);
-            hand_off(a, tiles, k, h, pt_all[w], l, i, g);
+            row_bwd_phase_b<D>(st, dpv, valid, lse2, delta, acc, ks, a.scale2, i, g, pt_all[w]);
+            hand_off(a, B, k, aux, h, pt_all[w], l, i, g);
         }
-        if (row_ok) {
-#pragma unroll
-            for (int s = 0; s < S::NB; ++s)
-                store_tile_rows(a.dQ, row * HD + hoff + 16 * s + 4 * g, acc[s], a.oscale);
-        }
+        store_block_rows<D>(a.dQ, a.n, B.lo, HD, hoff, acc, a.oscale, i, g);
     }
 }
 
-// Tiles of one 16-source block, in order: its dense tiles (by block row),
-// then its residual edges (by source) in pseudo-tiles of 16. The lane's A
-// operand row is tile row l%16; its four entries are rows 4g..4g+3 of
-// column l%16. fetch() issues the raw description loads of a tile (used two
-// tiles later), ColBwdTile::load() its data (used one tile later).
-struct ColTiles {
-    int64_t n, tcb, nd, rcb, rce;
-    int H, h;
-    const int32_t* tile_bycol;
-    const int32_t* tile_row;
-    const int32_t* res_rowidx;
-    const int32_t* res_col_edge;
-    const uint2* tile_pd;
-    const uint32_t* res_pd;
-    BlockStarts starts;
-
-    __device__ __forceinline__ int64_t count() const { return nd + (rce - rcb + 15) / 16; }
-
-    // dense tile: t = tile id; residual pseudo-tile: dst = destination of row
-    // l%16 and re = its residual-CSR edge id
-    __device__ __forceinline__ void fetch(int64_t k, int c, int32_t& t, int32_t& dst,
-                                          int32_t& re) const
-    {
-        if (k < nd) {
-            t = tile_bycol[tcb + k];
-            dst = 0;
-            re = 0;
-        } else {
-            const int64_t e = rcb + (k - nd) * 16 + c;
-            t = 0;
-            dst = e < rce ? res_rowidx[e] : 0;
-            re = e < rce ? res_col_edge[e] : -1;
-        }
-    }
+// What a lane needs of a tile of a column block (16 sources), loaded two
+// tiles ahead. Dense tile (the column's tiles by block row): its tile id (for
+// its P and dS) and the destination of the lane's operand row c. Pseudo-tile
+// (residual entries by source, 16 at a time): the destination of entry c, its
+// residual edge id (-1 past the block's entries) and its source's column
+// within the block.
+struct ColDesc {
+    int32_t t, dst, re, cc;
 };
 
+__device__ __forceinline__ ColDesc col_fetch(const BsBwdArgs& a, const Blk& B, int64_t k, int c)
+{
+    ColDesc d;
+    if (k < B.nd) {
+        const int64_t x = B.tb + k;
+        d.t = a.tile_bycol[x];
+        d.dst = static_cast<int32_t>(min(static_cast<int64_t>(a.tile_row_bycol[x]) * kTileDim + c,
+                                         a.n - 1));
+        d.re = 0;
+        d.cc = 0;
+    } else {
+        const int64_t e = B.rb + (k - B.nd) * kTileDim + c;
+        const bool ok = e < B.re;
+        d.t = 0;
+        d.dst = ok ? a.res_rowidx[e] : 0;
+        d.re = ok ? a.res_col_edge[e] : -1;
+        d.cc = ok ? a.res_colsrc[e] - static_cast<int32_t>(B.lo) : -1;
+    }
+    return d;
+}
+
 // One tile of the column pass: the Q and dO rows of its 16 destinations (A
-// operand layout) and this lane's P^T and dS^T fragments (rows 4g..4g+3 of
-// column l%16), both left by the tile-row pass.
+// operand layout) and the raw P, dS the tile-row pass left: a dense tile's
+// two 8-byte fragments of this lane, or a pseudo-tile's word (bf16 P, bf16
+// dS) of entry c with its column cc. The B operands are formed when the tile
+// is computed (pt_dt), so that no load waits inside load().
 template <int D>
 struct ColBwdTile {
-    Frag qa[Shape<D>::KS], oa[Shape<D>::KS];
-    s16x4_t pt, dt;
+    TileRows<D> q, o;
+    uint2 praw, draw;
 
-    __device__ __forceinline__ void load(const ColTiles& T, int64_t k, int32_t t, int32_t dst,
-                                         int32_t re, const void* Q, const void* dO, int64_t HD,
-                                         int64_t hoff, int l, int c, int g)
+    __device__ __forceinline__ void load(const BsBwdArgs& a, bool dense, const ColDesc& d, int h,
+                                         int64_t HD, int64_t hoff, int l)
     {
-        int64_t arow = 0;
-        if (k < T.nd) {
-            arow = min(static_cast<int64_t>(T.tile_row[t]) * kTileDim + c, T.n - 1);
-            const uint2* f = T.tile_pd + (static_cast<int64_t>(t) * T.H + T.h) * 2 * kWave;
-            pt = __builtin_bit_cast(s16x4_t, f[l]);
-            dt = __builtin_bit_cast(s16x4_t, f[kWave + l]);
+        if (dense) {
+            const uint2* f = a.tile_pd + (static_cast<int64_t>(d.t) * a.H + h) * 2 * kWave;
+            praw = f[l];
+            draw = f[kWave + l];
         } else {
-            const int64_t e = T.rcb + (k - T.nd) * 16 + c;   // row c of this pseudo-tile is edge e
-            const int cc = e < T.rce ? T.starts.row_of(e) : -1;
-            const uint32_t w = re >= 0 ? T.res_pd[static_cast<int64_t>(re) * T.H + T.h] : 0u;
-            arow = dst;
-            short pb[4], db[4];
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int lq = 4 * g + q;   // entry (row 4g + q, column c)
-                const bool bit = __shfl(cc, lq) == c;
-                const uint32_t wq = __shfl(w, lq);
-                pb[q] = static_cast<short>(bit ? (wq & 0xffffu) : 0u);
-                db[q] = static_cast<short>(bit ? (wq >> 16) : 0u);
-            }
-            pt = s16x4_t{pb[0], pb[1], pb[2], pb[3]};
-            dt = s16x4_t{db[0], db[1], db[2], db[3]};
+            praw.x = d.re >= 0 ? a.res_pd[static_cast<int64_t>(d.re) * a.H + h] : 0u;
+            praw.y = static_cast<uint32_t>(d.cc);
+            draw = make_uint2(0u, 0u);
         }
-        const int64_t qbase = arow * HD + hoff;
-#pragma unroll
-        for (int s = 0; s < Shape<D>::KS; ++s) {
-            qa[s] = ldg<SGAT_BF16>(Q, qbase + 32 * s + 8 * g);
-            oa[s] = ldg<SGAT_BF16>(dO, qbase + 32 * s + 8 * g);
+        q.load(a.Q, d.dst, HD, hoff, l);
+        o.load(a.dO, d.dst, HD, hoff, l);
+    }
+
+    // P^T and dS^T B operands: rows 4g..4g+3 of column c
+    __device__ __forceinline__ void pt_dt(bool dense, int c, int g, s16x4_t& pt, s16x4_t& dt) const
+    {
+        if (dense) {
+            pt = __builtin_bit_cast(s16x4_t, praw);
+            dt = __builtin_bit_cast(s16x4_t, draw);
+            return;
         }
+        short pb[4], db[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int lq = 4 * g + q;   // entry (row 4g + q, column c)
+            const bool bit = __shfl(static_cast<int>(praw.y), lq) == c;
+            const uint32_t wq = static_cast<uint32_t>(__shfl(static_cast<int>(praw.x), lq));
+            pb[q] = static_cast<short>(bit ? (wq & 0xffffu) : 0u);
+            db[q] = static_cast<short>(bit ? (wq >> 16) : 0u);
+        }
+        pt = s16x4_t{pb[0], pb[1], pb[2], pb[3]};
+        dt = s16x4_t{db[0], db[1], db[2], db[3]};
     }
 };
 
@@ -663,8 +719,8 @@ __device__ __forceinline__ void col_bwd_phase_b(const s16x4_t& pt, const s16x4_t
 {
     using S = Shape<D>;
     __builtin_amdgcn_wave_barrier();
-    const uint16_t* qt = operand_tr_base<D>(qs, c, g);
-    const uint16_t* ot = operand_tr_base<D>(os, c, g);
+    const uint16_t* qt = tr_base<D>(qs, c, g);
+    const uint16_t* ot = tr_base<D>(os, c, g);
 #pragma unroll
     for (int s = 0; s < S::NB; ++s) {
         // Q[4g + kk][16s + c] and dO[4g + kk][16s + c], kk = 0..3
@@ -687,30 +743,13 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
     const int w = wave_id();
     const int l = threadIdx.x & 63, c = l & 15, g = l >> 4;
     const int64_t HD = static_cast<int64_t>(a.H) * D;
-    ColTiles T;
-    const int64_t c_lo = bc * kTileDim;
-    const int64_t c_hi = c_lo + kTileDim < a.n ? c_lo + kTileDim : a.n;
-    T.n = a.n;
-    T.tcb = a.tile_colptr[bc];
-    T.nd = a.tile_colptr[bc + 1] - T.tcb;
-    T.rcb = a.res_colptr[c_lo];
-    T.rce = a.res_colptr[c_hi];
-    T.H = a.H;
-    T.tile_bycol = a.tile_bycol;
-    T.tile_row = a.tile_row;
-    T.res_rowidx = a.res_rowidx;
-    T.res_col_edge = a.res_col_edge;
-    T.tile_pd = a.tile_pd;
-    T.res_pd = a.res_pd;
-    T.starts.load(a.res_colptr, c_lo, c_hi);
-    const int64_t nt = T.count();
-    const int64_t j = c_lo + c;
-    const bool j_ok = j < a.n;
+    Blk B;
+    B.load(a.tile_colptr, a.res_colptr, bc, a.n);
+    const int64_t nt = B.count();
     uint16_t* qs = qs_all[w];
     uint16_t* os = os_all[w];
 
     for (int h = w; h < a.H; h += kWavesPerBlock) {
-        T.h = h;
         const int64_t hoff = static_cast<int64_t>(h) * D;
         f32x4_t dk[S::NB], dv[S::NB];
 #pragma unroll
@@ -719,33 +758,25 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
             dv[s] = f32x4_t{0.f, 0.f, 0.f, 0.f};
         }
         // pipeline: descriptions two tiles ahead; tile k+1's data refills the
-        // tile registers once phase A of tile k has put them into LDS
+        // tile registers once tile k's rows are in LDS
         ColBwdTile<D> tile;
-        int32_t t2 = 0, d2 = 0, r2 = 0;
-        if (nt > 0) {
-            int32_t t0, d0, r0;
-            T.fetch(0, c, t0, d0, r0);
-            tile.load(T, 0, t0, d0, r0, a.Q, a.dO, HD, hoff, l, c, g);
-        }
-        if (nt > 1) T.fetch(1, c, t2, d2, r2);
+        ColDesc d2{0, 0, -1, -1};
+        if (nt > 0) tile.load(a, B.nd > 0, col_fetch(a, B, 0, c), h, HD, hoff, l);
+        if (nt > 1) d2 = col_fetch(a, B, 1, c);
         for (int64_t k = 0; k < nt; ++k) {
-            const s16x4_t pt = tile.pt, dt = tile.dt;
-            store_operand_tile<D>(qs, tile.qa, c, g);
-            store_operand_tile<D>(os, tile.oa, c, g);
+            s16x4_t pt, dt;
+            tile.pt_dt(k < B.nd, c, g, pt, dt);
+            tile.q.store(qs, l);
+            tile.o.store(os, l);
             if (k + 1 < nt) {
-                const int32_t t1 = t2, d1 = d2, r1 = r2;
-                if (k + 2 < nt) T.fetch(k + 2, c, t2, d2, r2);
-                tile.load(T, k + 1, t1, d1, r1, a.Q, a.dO, HD, hoff, l, c, g);
+                const ColDesc d1 = d2;
+                if (k + 2 < nt) d2 = col_fetch(a, B, k + 2, c);
+                tile.load(a, k + 1 < B.nd, d1, h, HD, hoff, l);
             }
             col_bwd_phase_b<D>(pt, dt, dk, dv, qs, os, c, g);
         }
-        if (j_ok) {
-#pragma unroll
-            for (int s = 0; s < S::NB; ++s) {
-                store_tile_rows(a.dK, j * HD + hoff + 16 * s + 4 * g, dk[s], a.oscale);
-                store_tile_rows(a.dV, j * HD + hoff + 16 * s + 4 * g, dv[s], 1.f);
-            }
-        }
+        store_block_rows<D>(a.dK, a.n, B.lo, HD, hoff, dk, a.oscale, c, g);
+        store_block_rows<D>(a.dV, a.n, B.lo, HD, hoff, dv, 1.f, c, g);
     }
 }
 

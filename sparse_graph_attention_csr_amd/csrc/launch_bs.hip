@@ -16,6 +16,7 @@ int launch_gt_bs_fwd(const Plan& p, int H, int D, const void* Q, const void* K, 
     a.tile_mask = p.dptr<uint16_t>(SGAT_ARR_TILE_MASK);
     a.res_rowptr = p.dptr<int64_t>(SGAT_ARR_RES_ROWPTR);
     a.res_colidx = p.dptr<int32_t>(SGAT_ARR_RES_COLIDX);
+    a.res_row = p.dptr<int32_t>(SGAT_ARR_RES_ROW);
     a.Q = Q; a.K = K; a.V = V;
     a.out = out;
     a.lse = lse;
@@ -39,7 +40,6 @@ int launch_gt_bs_bwd(const Plan& p, int H, int D, const void* Q, const void* K, 
     a.tile_rowptr = p.dptr<int64_t>(SGAT_ARR_TILE_ROWPTR);
     a.tile_col = p.dptr<int32_t>(SGAT_ARR_TILE_COL);
     a.tile_mask = p.dptr<uint16_t>(SGAT_ARR_TILE_MASK);
-    a.tile_row = p.dptr<int32_t>(SGAT_ARR_TILE_ROW);
     a.tile_colptr = p.dptr<int64_t>(SGAT_ARR_TILE_COLPTR);
     a.tile_bycol = p.dptr<int32_t>(SGAT_ARR_TILE_BYCOL);
     a.res_rowptr = p.dptr<int64_t>(SGAT_ARR_RES_ROWPTR);
@@ -47,6 +47,9 @@ int launch_gt_bs_bwd(const Plan& p, int H, int D, const void* Q, const void* K, 
     a.res_colptr = p.dptr<int64_t>(SGAT_ARR_RES_COLPTR);
     a.res_rowidx = p.dptr<int32_t>(SGAT_ARR_RES_ROWIDX);
     a.res_col_edge = p.dptr<int32_t>(SGAT_ARR_RES_COL_EDGE);
+    a.res_row = p.dptr<int32_t>(SGAT_ARR_RES_ROW);
+    a.res_colsrc = p.dptr<int32_t>(SGAT_ARR_RES_COLSRC);
+    a.tile_row_bycol = p.dptr<int32_t>(SGAT_ARR_TILE_ROW_BYCOL);
     a.Q = Q; a.K = K; a.V = V; a.O = O; a.dO = dO;
     a.lse = lse;
     a.tile_pd = static_cast<uint2*>(tile_pd);

@@ -259,6 +259,14 @@ void build_tile_columns(int64_t n, const std::vector<int64_t>& tile_rowptr,
         tile_bycol[static_cast<size_t>(fill[tile_col[t]]++)] = static_cast<int32_t>(t);
 }
 
+void expand_pointer(int64_t n, const std::vector<int64_t>& ptr, std::vector<int32_t>& out)
+{
+    out.assign(static_cast<size_t>(ptr[static_cast<size_t>(n)]), 0);
+    for (int64_t i = 0; i < n; ++i)
+        for (int64_t e = ptr[static_cast<size_t>(i)]; e < ptr[static_cast<size_t>(i) + 1]; ++e)
+            out[static_cast<size_t>(e)] = static_cast<int32_t>(i);
+}
+
 const void* Plan::host_array(int id) const
 {
     switch (id) {
@@ -281,6 +289,9 @@ const void* Plan::host_array(int id) const
     case SGAT_ARR_RES_COL_EDGE: return res_col_edge.data();
     case SGAT_ARR_COL_EDGE: return col_edge.data();
     case SGAT_ARR_ROW_TPOS: return row_tpos.data();
+    case SGAT_ARR_RES_ROW: return res_row.data();
+    case SGAT_ARR_RES_COLSRC: return res_colsrc.data();
+    case SGAT_ARR_TILE_ROW_BYCOL: return tile_row_bycol.data();
     default: return nullptr;
     }
 }
@@ -312,6 +323,9 @@ void Plan::layout()
     bytes[SGAT_ARR_RES_COL_EDGE] = res_col_edge.size() * sizeof(int32_t);
     bytes[SGAT_ARR_COL_EDGE] = col_edge.size() * sizeof(int32_t);
     bytes[SGAT_ARR_ROW_TPOS] = row_tpos.size() * sizeof(int32_t);
+    bytes[SGAT_ARR_RES_ROW] = res_row.size() * sizeof(int32_t);
+    bytes[SGAT_ARR_RES_COLSRC] = res_colsrc.size() * sizeof(int32_t);
+    bytes[SGAT_ARR_TILE_ROW_BYCOL] = tile_row_bycol.size() * sizeof(int32_t);
     size_t off = 0;
     for (int a = 0; a < SGAT_ARR_COUNT; ++a) {
         offset[a] = off;
@@ -385,6 +399,11 @@ int sgat_plan_create(int64_t n, int64_t nnz, const int64_t* rowptr, const int32_
                                      p.tile_bycol);
             sgat::build_transpose(n, p.res_rowptr.data(), p.res_colidx.data(), p.res_colptr,
                                   p.res_rowidx, &p.res_col_edge);
+            sgat::expand_pointer(n, p.res_rowptr, p.res_row);
+            sgat::expand_pointer(n, p.res_colptr, p.res_colsrc);
+            p.tile_row_bycol.resize(p.tile_bycol.size());
+            for (size_t x = 0; x < p.tile_bycol.size(); ++x)
+                p.tile_row_bycol[x] = p.tile_row[static_cast<size_t>(p.tile_bycol[x])];
         }
         p.layout();
     } catch (const std::bad_alloc&) {

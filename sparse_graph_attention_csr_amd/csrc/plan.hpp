@@ -55,6 +55,9 @@ struct Plan {
     std::vector<int64_t> res_colptr;    // transposed residual CSR
     std::vector<int32_t> res_rowidx;
     std::vector<int32_t> res_col_edge;  // residual-CSR edge id of each transposed residual entry
+    std::vector<int32_t> res_row;       // destination of each residual edge
+    std::vector<int32_t> res_colsrc;    // source of each transposed residual entry
+    std::vector<int32_t> tile_row_bycol;// block row of each tile, in tile_bycol order
     int64_t tile_edges = 0;
 
     // device image: every array at a 256-byte aligned offset of one buffer
@@ -100,6 +103,10 @@ void build_tiles(int64_t n, const int64_t* rowptr, const int32_t* colidx, int32_
                  std::vector<int64_t>& tile_rowptr, std::vector<int32_t>& tile_col,
                  std::vector<uint16_t>& tile_mask, std::vector<int64_t>& res_rowptr,
                  std::vector<int32_t>& res_colidx, int64_t& tile_edges);
+
+// The row of every entry of a CSR-like pointer array (out[e] = i for e in
+// [ptr[i], ptr[i+1])).
+void expand_pointer(int64_t n, const std::vector<int64_t>& ptr, std::vector<int32_t>& out);
 
 // A4 (column side): tiles grouped by block column (stable in block row) and
 // the block row of each tile.

@@ -112,7 +112,7 @@ def test_upload_checks(plan):
 def test_export_checks(plan):
     L = B.lib()
     b = ctypes.c_size_t()
-    assert L.sgat_plan_array_bytes(plan.handle, 19, ctypes.byref(b)) == 1
+    assert L.sgat_plan_array_bytes(plan.handle, 22, ctypes.byref(b)) == 1
     assert L.sgat_plan_array_bytes(plan.handle, B.ARR_ROW_ITEMS, ctypes.byref(b)) == 0
     assert b.value == plan.stats()["row_items"] * 24
     buf = ctypes.create_string_buffer(b.value)

@@ -50,6 +50,9 @@ def check_plan(rowptr, colidx, chunk, tmin=0, bs=False, loc=False, order=2):
         assert np.array_equal(p.export(B.ARR_RES_COLPTR), rcp)
         assert np.array_equal(p.export(B.ARR_RES_ROWIDX), rri)
         assert np.array_equal(p.export(B.ARR_RES_COL_EDGE), rce)
+        assert np.array_equal(p.export(B.ARR_RES_ROW), S.expand_pointer(rr))
+        assert np.array_equal(p.export(B.ARR_RES_COLSRC), S.expand_pointer(rcp))
+        assert np.array_equal(p.export(B.ARR_TILE_ROW_BYCOL), trow[tbc])
     return p
 
 
