@@ -23,13 +23,27 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")
-_LIB = os.path.join(_HERE, "liboracle.so")
+# SGAT_ORACLE_LIBRARY selects another build (the sanitizer build, see build())
+_LIB = os.environ.get("SGAT_ORACLE_LIBRARY") or os.path.join(_HERE, "liboracle.so")
+_SAN_LIB = os.path.join(_HERE, "liboracle_san.so")
 
 _DT = {np.dtype(np.float32): 0, np.dtype(np.uint16): 1, np.dtype(np.float64): 2}
 
 
-def build(force: bool = True) -> str:
-    """Compile oracle.c with gcc (-O2, OpenMP, IEEE semantics kept)."""
+def build(force: bool = True, sanitize: bool = False) -> str:
+    """Compile oracle.c with gcc (-O2, OpenMP, IEEE semantics kept). With
+    sanitize, build liboracle_san.so instead with clang's AddressSanitizer and
+    UndefinedBehaviorSanitizer (the runtime the library's sanitizer build
+    uses, so both can share one process)."""
+    if sanitize:
+        llvm = "/opt/rocm/llvm"
+        tmp = _SAN_LIB + ".tmp"
+        subprocess.check_call([f"{llvm}/bin/clang", "-O1", "-g", "-fno-omit-frame-pointer",
+                               "-fsanitize=address,undefined", "-fno-sanitize-recover=undefined",
+                               "-fopenmp", "-fPIC", "-shared", "-std=c99", "-Wall", "-Wextra",
+                               f"-Wl,-rpath,{llvm}/lib", "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, _SAN_LIB)
+        return _SAN_LIB
     if force or not os.path.exists(_LIB):
         tmp = _LIB + ".tmp"
         subprocess.check_call(["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c99",

@@ -15,7 +15,9 @@ import os
 
 import numpy as np
 
-_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsgattn.so")
+# SGAT_LIBRARY selects another build of the same library (the sanitizer build)
+_LIB_PATH = os.environ.get("SGAT_LIBRARY") or os.path.join(
+    os.path.dirname(os.path.abspath(__file__)), "libsgattn.so")
 
 F32, BF16 = 0, 1
 OP_GT_FWD, OP_GT_BWD, OP_GAT_FWD, OP_GAT_BWD, OP_REDUCE_FWD, OP_REDUCE_BWD = range(6)

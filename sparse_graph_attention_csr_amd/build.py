@@ -1,10 +1,16 @@
 """Build libsgattn.so (HIP for gfx950) in-tree.
 
-    python -m sparse_graph_attention_csr_amd.build
+    python -m sparse_graph_attention_csr_amd.build [--sanitize]
 
 Each source is compiled by hipcc into _build/, in parallel, then linked into
 sparse_graph_attention_csr_amd/libsgattn.so. Packed fp32 VALU instructions are
 disabled for all device code.
+
+--sanitize builds _build/san/libsgattn_san.so instead, with the host code
+(plan construction, CSR validation, the C ABI's checks) instrumented by
+AddressSanitizer and UndefinedBehaviorSanitizer; the device code is built as
+usual. Load it with SGAT_LIBRARY=<path> and clang's ASan runtime preloaded
+(tests/run_sanitized.sh does both).
 """
 from __future__ import annotations
 
@@ -31,10 +37,18 @@ FLAGS = [
 ]
 
 
-def _compile(src: str) -> str:
+SAN_BUILD = os.path.join(BUILD, "san")
+SAN_LIB = os.path.join(SAN_BUILD, "libsgattn_san.so")
+# host-side instrumentation only: every sanitizer flag applies to the host pass
+SAN_FLAGS = ["-g", "-Xarch_host", "-fno-omit-frame-pointer",
+             "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+             "-Xarch_host", "-fno-sanitize-recover=undefined"]
+
+
+def _compile(src: str, sanitize: bool = False) -> str:
     path = os.path.join(CSRC, src)
-    obj = os.path.join(BUILD, src + ".o")
-    cmd = [HIPCC, "-x", "hip", *FLAGS, "-c", path, "-o", obj]
+    obj = os.path.join(SAN_BUILD if sanitize else BUILD, src + ".o")
+    cmd = [HIPCC, "-x", "hip", *FLAGS, *(SAN_FLAGS if sanitize else []), "-c", path, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     noise = "is not a recognized feature for this target"
     err = "\n".join(l for l in (r.stderr or "").splitlines() if noise not in l)
@@ -45,16 +59,19 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(jobs: int | None = None) -> str:
-    os.makedirs(BUILD, exist_ok=True)
+def build(jobs: int | None = None, sanitize: bool = False) -> str:
+    os.makedirs(SAN_BUILD if sanitize else BUILD, exist_ok=True)
     jobs = jobs or min(len(SOURCES), os.cpu_count() or 4)
     with cf.ThreadPoolExecutor(jobs) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
-    subprocess.check_call([HIPCC, "-shared", "-fPIC", "--offload-arch=gfx950", "-o", tmp, *objs])
-    os.replace(tmp, LIB)
-    return LIB
+        objs = list(ex.map(lambda s: _compile(s, sanitize), SOURCES))
+    lib = SAN_LIB if sanitize else LIB
+    tmp = lib + ".tmp"
+    link = SAN_FLAGS if sanitize else []
+    subprocess.check_call([HIPCC, "-shared", "-fPIC", "--offload-arch=gfx950", *link, "-o", tmp,
+                           *objs])
+    os.replace(tmp, lib)
+    return lib
 
 
 if __name__ == "__main__":
-    print(build())
+    print(build(sanitize="--sanitize" in sys.argv[1:]))
