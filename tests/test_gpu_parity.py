@@ -273,6 +273,36 @@ def test_gt_edge_orders_bitwise_equal(dt, H, D):
         assert np.array_equal(x, y)
 
 
+@pytest.mark.parametrize("slope", [0.2])
+def test_gat_bwd_grid_stride(slope):
+    """The GATv2 backward passes take one work unit per wave up to 2^16
+    workgroups (4 waves each) and stride beyond. fp32 H=2 D=128 holds one edge
+    per wave, so every item is a unit of its own: 300,000 rows and sources make
+    both passes stride, with da summed over the strided partials."""
+    n, H, D = 300_000, 2, 128
+    note(f"gat bwd grid stride n={n} H={H} D={D}")
+    rng = np.random.default_rng(41)
+    deg = rng.integers(1, 4, size=n)
+    rp = np.zeros(n + 1, dtype=np.int64)
+    rp[1:] = np.cumsum(deg)
+    ci = rng.integers(0, n, size=int(rp[-1])).astype(np.int32)
+    t = tensors(42, n, H, D, "f32", ["xs", "xt", "dout"])
+    a = (rng.standard_normal((H, D)) / np.sqrt(D)).astype(np.float32)
+    r = Runner(rp, ci)
+    st = r.g.plan.stats()
+    assert st["row_items"] > 4 * 65536 and st["col_items"] > 4 * 65536
+    xs, xt, do, ad = dev(t["xs"]), dev(t["xt"]), dev(t["dout"]), dev(a)
+    out, lse = r.gat_fwd(xs, xt, ad, slope=slope)
+    dxs, dxt, da = r.gat_bwd(xs, xt, ad, out, lse, do, slope=slope)
+    ro, rl = oracle.gat_fwd(rp, ci, t["xs"], t["xt"], a, slope)
+    rs, rt, ra = oracle.gat_bwd(rp, ci, t["xs"], t["xt"], a, t["dout"], slope)
+    assert rel_err(host(out), ro) <= TOL["f32"]
+    assert rel_err(host(lse), rl) <= TOL_LSE
+    assert rel_err(host(dxs), rs) <= TOL["f32"]
+    assert rel_err(host(dxt), rt) <= TOL["f32"]
+    assert rel_err(host(da), ra) <= TOL["f32"]
+
+
 def test_empty_graph_and_no_edges():
     note("empty graph / no edges")
     import torch
