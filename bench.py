@@ -294,9 +294,11 @@ def cpu_baseline(w, seconds: float):
     while t < seconds / 8 and r < n:        # grow the probe until it is long enough to scale
         r = min(n, r * 4)
         e, t = run(r)
-    if r < n and t < seconds / 2:
+    for _ in range(2):                      # scale to the target; cost per edge is not flat
+        if r >= n or t >= seconds * 0.6:
+            break
         target = e * seconds / max(t, 1e-9)
-        r = int(min(n, np.searchsorted(rp, target)))
+        r = int(min(n, max(r + 1, np.searchsorted(rp, target))))
         e, t = run(r)
     reps = 1
     tf, tb = split
