@@ -75,6 +75,53 @@ struct Shape {
     static constexpr int LDV = D + 8;
 };
 
+// x of this lane and of lane l ^ 16 (R = 16) or l ^ 32 (R = 32), combined
+// with a commutative op, in every lane. gfx950's row swaps (v_permlane16_swap
+// exchanges the odd 16-lane rows of its first operand with the even rows of
+// its second, v_permlane32_swap the upper half with the lower half) are VALU
+// instructions: given x twice, one result holds this lane's value and the
+// other its partner's, in an order that depends on the row, which a
+// commutative op does not see. Bitwise equal to op(x, __shfl_xor(x, R)),
+// without the LDS round trip of a permute. All 64 lanes must be active.
+// (The results are copied out of the returned pair as scalars: a bit cast
+// applied to an element of it directly read element 0 for both.)
+template <int R>
+__device__ __forceinline__ void row_swap(float x, float& a, float& b)
+{
+    static_assert(R == 16 || R == 32, "");
+    const uint32_t u = __builtin_bit_cast(uint32_t, x);
+    uint32_t r0, r1;
+    if constexpr (R == 16) {
+        const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+        r0 = r[0];
+        r1 = r[1];
+    } else {
+        const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+        r0 = r[0];
+        r1 = r[1];
+    }
+    a = __builtin_bit_cast(float, r0);
+    b = __builtin_bit_cast(float, r1);
+}
+
+// Sum (max) over the four lanes l, l ^ 16, l ^ 32, l ^ 48, in the order
+// (x_l + x_{l^16}) + (x_{l^32} + x_{l^48}).
+__device__ __forceinline__ float sum_rows4(float x)
+{
+    float a, b;
+    row_swap<16>(x, a, b);
+    row_swap<32>(a + b, a, b);
+    return a + b;
+}
+
+__device__ __forceinline__ float max_rows4(float x)
+{
+    float a, b;
+    row_swap<16>(x, a, b);
+    row_swap<32>(fmaxf(a, b), a, b);
+    return fmaxf(a, b);
+}
+
 // Transposed 4 x 16-bit LDS read (gfx950 ds_read_b64_tr_b16). Within each
 // group of 16 lanes, lane j receives element j % 4 of the 64-bit word that
 // lane 4k + j / 4 addressed, in slot k.
@@ -100,10 +147,14 @@ __device__ __forceinline__ const uint16_t* tr_base(const uint16_t* t, int i, int
 // A workgroup owns one block of 16 nodes (a tile row, or a tile column in the
 // column pass): its dense tiles [tb, tb + nd) of the tile list, then its
 // residual entries [rb, re) in pseudo-tiles of 16; lo is its first node.
-// (Walking several consecutive blocks per workgroup, with the tile pipeline
-// running on across block boundaries, was measured slower: 1, 2, 4 and 8
-// blocks per workgroup gave 1.67, 1.72, 1.84 and 1.88 ms per community-graph
-// step, as the fewer, longer workgroups leave more of the chip idle at the end.)
+// (Walking several blocks per workgroup, with the tile pipeline running on
+// across block boundaries so that a block's first loads overlap the previous
+// block's last tiles, was measured slower twice: consecutive blocks, 1, 2, 4
+// and 8 per workgroup, gave 1.67, 1.72, 1.84 and 1.88 ms per community-graph
+// step; with whole-line loads, blocks strided by the grid, 1, 2, 4, 8 and 16
+// per workgroup gave 1.55, 1.54, 1.54, 1.55 and 1.63 ms, against 1.49 ms for
+// one block per workgroup: the stream's three block descriptors cost the row
+// pass registers (it spilled), and the forward did not gain.)
 struct Blk {
     int64_t tb, nd, rb, re, lo;
 
@@ -256,8 +307,7 @@ __device__ __forceinline__ void fwd_phase_b(const f32x4_t& st, uint32_t valid, f
         sv[k] = ((valid >> k) & 1u) ? st[k] * scale2 : kNegInf;
         rmax = fmaxf(rmax, sv[k]);
     }
-    rmax = fmaxf(rmax, __shfl_xor(rmax, 16));
-    rmax = fmaxf(rmax, __shfl_xor(rmax, 32));
+    rmax = max_rows4(rmax);
     // Lazy rescaling: m is a reference maximum, moved (and O, lsum rescaled)
     // only when a row's score passes it by more than 2^kRescaleLog2, so the
     // weights exp2(s - m) stay below 2^kRescaleLog2 and the common tile leaves
@@ -277,8 +327,7 @@ __device__ __forceinline__ void fwd_phase_b(const f32x4_t& st, uint32_t valid, f
         p[k] = ((valid >> k) & 1u) ? fast_exp2(sv[k] - m) : 0.f;
         ps += p[k];
     }
-    ps += __shfl_xor(ps, 16);
-    ps += __shfl_xor(ps, 32);
+    ps = sum_rows4(ps);
     lsum += ps;
     const s16x4_t pb = {bf16_bits(p[0]), bf16_bits(p[1]), bf16_bits(p[2]), bf16_bits(p[3])};
     __builtin_amdgcn_wave_barrier();
@@ -550,8 +599,7 @@ struct RowBlockRows {
 #pragma unroll
         for (int s = 0; s < Shape<D>::KS; ++s)
             d += dot<SGAT_BF16>(__builtin_bit_cast(Frag, df[s]), of[s]);
-        d += __shfl_xor(d, 16);
-        d += __shfl_xor(d, 32);
+        d = sum_rows4(d);
         delta = d;
         lse2 = lse * kLog2e;
     }
