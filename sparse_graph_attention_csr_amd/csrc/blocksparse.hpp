@@ -6,8 +6,9 @@
 // implementations", paragraph on attention-based architectures; IO-Aware
 // Layers paper, Abstract: block-sparse variants on locally dense graphs).
 //
-// One workgroup owns a tile row (16 destination rows); each wave owns one head
-// at a time. Per tile (16 source columns) and head:
+// One wave owns one head of a tile row (16 destination rows); a tile row's H
+// heads go to ceil(H / 4) workgroups of four waves. Per tile (16 source
+// columns) and head:
 //   S^T = K_t Q_t^T   v_mfma_f32_16x16x32_bf16, K over D in steps of 32
 //   masked online softmax over the row's tiles, in registers
 //   O^T += V_t^T P^T  v_mfma_f32_16x16x16_bf16 per 16-channel block
@@ -143,6 +144,12 @@ __device__ __forceinline__ const uint16_t* tr_base(const uint16_t* t, int i, int
 // ---------------------------------------------------------------------------
 // the tiles of one 16-node block
 // ---------------------------------------------------------------------------
+
+// Workgroups per 16-node block: one wave per head, four waves per workgroup.
+__device__ __host__ __forceinline__ int64_t head_groups(int H)
+{
+    return (H + kWavesPerBlock - 1) / kWavesPerBlock;
+}
 
 // A workgroup owns one block of 16 nodes (a tile row, or a tile column in the
 // column pass): its dense tiles [tb, tb + nd) of the tile list, then its
@@ -384,16 +391,21 @@ __device__ __forceinline__ void load_block_rows(const void* X, int64_t lo, int64
 
 // At least 3 waves per SIMD: at D = 128 the compiler would otherwise keep
 // the accumulators twice (VGPR copies of MFMA results in AGPRs) and stop at 2;
-// with the target it keeps them in VGPRs only, without spilling.
+// with the target it keeps them in VGPRs only, without spilling. (Asking for
+// 4 fits it in 126 VGPRs, also without spilling, and measured the same.)
 template <int D>
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) void gt_bs_fwd(BsFwdArgs a)
 {
     using S = Shape<D>;
     __shared__ __attribute__((aligned(16))) uint16_t ks_all[kWavesPerBlock][16 * S::LDV];
     __shared__ __attribute__((aligned(16))) uint16_t vs_all[kWavesPerBlock][16 * S::LDV];
-    const int64_t br = logical_block();
+    const int64_t per_block = head_groups(a.H);
+    const int64_t lb = logical_block();
+    const int64_t br = lb / per_block;
     if (br >= a.n_tile_rows) return;          // the whole workgroup leaves; no barrier follows
     const int w = wave_id();
+    const int h = static_cast<int>(lb - br * per_block) * kWavesPerBlock + w;
+    if (h >= a.H) return;                     // one head per wave; waves past H idle
     const int l = threadIdx.x & 63, i = l & 15, g = l >> 4;
     const int64_t HD = static_cast<int64_t>(a.H) * D;
     Blk B;
@@ -401,8 +413,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
     const int64_t nt = B.count();
     uint16_t* ks = ks_all[w];
     uint16_t* vs = vs_all[w];
-
-    for (int h = w; h < a.H; h += kWavesPerBlock) {
+    {
         const int64_t hoff = static_cast<int64_t>(h) * D;
         bf16x8_t qf[S::KS];
         load_block_rows<D>(a.Q, B.lo, a.n, HD, hoff, i, g, qf);
@@ -625,9 +636,13 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
     __shared__ __attribute__((aligned(16))) uint16_t vs_all[kWavesPerBlock][16 * S::LDV];
     // one 16x16 bf16 tile of P and one of dS, row-major, to transpose them
     __shared__ __attribute__((aligned(16))) uint16_t pt_all[kWavesPerBlock][2][kTileDim * kTileDim];
-    const int64_t br = logical_block();
+    const int64_t per_block = head_groups(a.H);
+    const int64_t lb = logical_block();
+    const int64_t br = lb / per_block;
     if (br >= a.n_blocks) return;
     const int w = wave_id();
+    const int h = static_cast<int>(lb - br * per_block) * kWavesPerBlock + w;
+    if (h >= a.H) return;                     // one head per wave; waves past H idle
     const int l = threadIdx.x & 63, i = l & 15, g = l >> 4;
     const int64_t HD = static_cast<int64_t>(a.H) * D;
     Blk B;
@@ -635,8 +650,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
     const int64_t nt = B.count();
     uint16_t* ks = ks_all[w];
     uint16_t* vs = vs_all[w];
-
-    for (int h = w; h < a.H; h += kWavesPerBlock) {
+    {
         const int64_t hoff = static_cast<int64_t>(h) * D;
         RowBlockRows<D> rows;
         rows.load(a, B.lo, HD, hoff, h, i, g);
@@ -780,52 +794,59 @@ __device__ __forceinline__ void col_bwd_phase_b(const s16x4_t& pt, const s16x4_t
     __builtin_amdgcn_wave_barrier();
 }
 
+// One head per wave: a block's H heads go to ceil(H / 4) consecutive
+// workgroups (waves past H idle). (Splitting each head's channels over two
+// waves, which halves a wave's accumulators and tile registers and fits 5
+// waves per SIMD, was measured slower: 0.567 against 0.513 ms on the
+// community graph, from twice the workgroup starts and hand-off reads.)
 template <int D>
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) void gt_bs_bwd_cols(BsBwdArgs a)
 {
     using S = Shape<D>;
     __shared__ __attribute__((aligned(16))) uint16_t qs_all[kWavesPerBlock][16 * S::LDV];
     __shared__ __attribute__((aligned(16))) uint16_t os_all[kWavesPerBlock][16 * S::LDV];
-    const int64_t bc = logical_block();
+    const int64_t per_block = head_groups(a.H);
+    const int64_t lb = logical_block();
+    const int64_t bc = lb / per_block;
     if (bc >= a.n_blocks) return;
     const int w = wave_id();
+    const int h = static_cast<int>(lb - bc * per_block) * kWavesPerBlock + w;
+    if (h >= a.H) return;                    // no workgroup barrier follows
     const int l = threadIdx.x & 63, c = l & 15, g = l >> 4;
     const int64_t HD = static_cast<int64_t>(a.H) * D;
+    const int64_t hoff = static_cast<int64_t>(h) * D;
     Blk B;
     B.load(a.tile_colptr, a.res_colptr, bc, a.n);
     const int64_t nt = B.count();
     uint16_t* qs = qs_all[w];
     uint16_t* os = os_all[w];
 
-    for (int h = w; h < a.H; h += kWavesPerBlock) {
-        const int64_t hoff = static_cast<int64_t>(h) * D;
-        f32x4_t dk[S::NB], dv[S::NB];
+    f32x4_t dk[S::NB], dv[S::NB];
 #pragma unroll
-        for (int s = 0; s < S::NB; ++s) {
-            dk[s] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-            dv[s] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        }
-        // pipeline: descriptions two tiles ahead; tile k+1's data refills the
-        // tile registers once tile k's rows are in LDS
-        ColBwdTile<D> tile;
-        ColDesc d2{0, 0, -1, -1};
-        if (nt > 0) tile.load(a, B.nd > 0, col_fetch(a, B, 0, c), h, HD, hoff, l);
-        if (nt > 1) d2 = col_fetch(a, B, 1, c);
-        for (int64_t k = 0; k < nt; ++k) {
-            s16x4_t pt, dt;
-            tile.pt_dt(k < B.nd, c, g, pt, dt);
-            tile.q.store(qs, l);
-            tile.o.store(os, l);
-            if (k + 1 < nt) {
-                const ColDesc d1 = d2;
-                if (k + 2 < nt) d2 = col_fetch(a, B, k + 2, c);
-                tile.load(a, k + 1 < B.nd, d1, h, HD, hoff, l);
-            }
-            col_bwd_phase_b<D>(pt, dt, dk, dv, qs, os, c, g);
-        }
-        store_block_rows<D>(a.dK, a.n, B.lo, HD, hoff, dk, a.oscale, c, g);
-        store_block_rows<D>(a.dV, a.n, B.lo, HD, hoff, dv, 1.f, c, g);
+    for (int s = 0; s < S::NB; ++s) {
+        dk[s] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        dv[s] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
+    // pipeline: descriptions two tiles ahead; tile k+1's data refills the
+    // tile registers once tile k's rows are in LDS
+    ColBwdTile<D> tile;
+    ColDesc d2{0, 0, -1, -1};
+    if (nt > 0) tile.load(a, B.nd > 0, col_fetch(a, B, 0, c), h, HD, hoff, l);
+    if (nt > 1) d2 = col_fetch(a, B, 1, c);
+    for (int64_t k = 0; k < nt; ++k) {
+        s16x4_t pt, dt;
+        tile.pt_dt(k < B.nd, c, g, pt, dt);
+        tile.q.store(qs, l);
+        tile.o.store(os, l);
+        if (k + 1 < nt) {
+            const ColDesc d1 = d2;
+            if (k + 2 < nt) d2 = col_fetch(a, B, k + 2, c);
+            tile.load(a, k + 1 < B.nd, d1, h, HD, hoff, l);
+        }
+        col_bwd_phase_b<D>(pt, dt, dk, dv, qs, os, c, g);
+    }
+    store_block_rows<D>(a.dK, a.n, B.lo, HD, hoff, dk, a.oscale, c, g);
+    store_block_rows<D>(a.dV, a.n, B.lo, HD, hoff, dv, 1.f, c, g);
 }
 
 }  // namespace sgat

@@ -24,8 +24,9 @@ int launch_gt_bs_fwd(const Plan& p, int H, int D, const void* Q, const void* K, 
     const void* fn = D == 32 ? reinterpret_cast<const void*>(&gt_bs_fwd<32>)
                    : D == 64 ? reinterpret_cast<const void*>(&gt_bs_fwd<64>)
                              : reinterpret_cast<const void*>(&gt_bs_fwd<128>);
-    // one workgroup per tile row, counted as four one-wave units for the grid
-    return launch("gt_bs_fwd", fn, dim3(static_cast<unsigned>(wave_grid(a.n_tile_rows * kWavesPerBlock))),
+    // one wave per (tile row, head): ceil(H / 4) workgroups per tile row
+    return launch("gt_bs_fwd", fn,
+                  dim3(static_cast<unsigned>(wave_grid(a.n_tile_rows * head_groups(H) * kWavesPerBlock))),
                   dim3(kBlock), &a, s);
 }
 
@@ -68,7 +69,8 @@ int launch_gt_bs_bwd(const Plan& p, int H, int D, const void* Q, const void* K, 
         fr = reinterpret_cast<const void*>(&gt_bs_bwd_rows<128>);
         fc = reinterpret_cast<const void*>(&gt_bs_bwd_cols<128>);
     }
-    const dim3 grid(static_cast<unsigned>(wave_grid(a.n_blocks * kWavesPerBlock)));
+    // one wave per (block, head): ceil(H / 4) workgroups per tile row or column
+    const dim3 grid(static_cast<unsigned>(wave_grid(a.n_blocks * head_groups(H) * kWavesPerBlock)));
     int rc = launch("gt_bs_bwd_rows", fr, grid, dim3(kBlock), &a, s);
     if (rc) return rc;
     return launch("gt_bs_bwd_cols", fc, grid, dim3(kBlock), &a, s);
