@@ -67,8 +67,10 @@ def check_bwd(r, rp, ci, q, k, v, do, out, lse):
 
 
 @pytest.mark.parametrize("D", [32, 64, 128])
-@pytest.mark.parametrize("H", [1, 4, 5])
+@pytest.mark.parametrize("H", [1, 4, 5, 16])
 def test_tiles_match_oracle(H, D):
+    """Each wave owns one head of a block: H = 5 puts three idle waves in a
+    block's second workgroup, H = 16 (the largest H) gives each block four."""
     note(f"tiles community H={H} D={D}")
     rp, ci = community_graph(8, seed=H * 10 + D)
     n = rp.size - 1
