@@ -2,6 +2,8 @@
 CSR work list into long items (one per wavefront) and the short suffix, and
 that the two row-pass kernels are charged exactly the edges and items of the
 whole pass between them. CPU only."""
+import re
+
 import numpy as np
 
 import bench
@@ -43,3 +45,25 @@ def test_row_item_split_partitions_the_work_list():
     both = sum(bench.algorithmic_bytes(k, deg.size, e, 2, 64, 2, None, sp)
                for k in ("gat_bwd_rows", "gat_bwd_rows_short"))
     assert both == bench.algorithmic_bytes("gat_bwd_rows", n_items, e, 2, 64, 2)
+
+
+def test_cpu_baseline_samples_a_prefix_of_rows():
+    """cpu_baseline on a workload the oracle cannot finish within the time it
+    is given: it times destination rows 0..r-1 only (the other rows emptied),
+    with r scaled towards the time target, and reports that sample."""
+    import dataclasses
+    rng = np.random.default_rng(7)
+    n, H, D = 20000, 2, 32
+    rp, ci = I.random_csr(n, 40, rng)
+    spec = dataclasses.replace(I.WORKLOADS["gt_er1k_h4d32_f32"], name="test", n=n, heads=H, dim=D)
+    w = {"spec": spec, "rowptr": rp, "colidx": ci}
+    for key in ("q", "k", "v", "dout"):
+        w[key] = rng.standard_normal((n, H, D))
+    cb = bench.cpu_baseline(w, 0.01)
+    assert cb["kind"] == "oracle" and cb["value"] > 0 and cb["cores"] >= 1
+    m = re.match(r"destination rows 0\.\.(\d+) of (\d+) \((\d+) of (\d+) edges\)", cb["sample"])
+    assert m, cb["sample"]
+    last, n_all, e, e_all = (int(x) for x in m.groups())
+    assert n_all == n and e_all == rp[-1]
+    assert 0 < last + 1 < n and e == rp[last + 1]
+    assert cb["fwd_seconds"] >= 0 and cb["bwd_seconds"] >= 0   # rounded to ms
