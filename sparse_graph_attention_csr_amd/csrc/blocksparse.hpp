@@ -413,38 +413,36 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
     const int64_t nt = B.count();
     uint16_t* ks = ks_all[w];
     uint16_t* vs = vs_all[w];
-    {
-        const int64_t hoff = static_cast<int64_t>(h) * D;
-        bf16x8_t qf[S::KS];
-        load_block_rows<D>(a.Q, B.lo, a.n, HD, hoff, i, g, qf);
-        float m = kNegInf, lsum = 0.f;
-        f32x4_t acc[S::NB];
+    const int64_t hoff = static_cast<int64_t>(h) * D;
+    bf16x8_t qf[S::KS];
+    load_block_rows<D>(a.Q, B.lo, a.n, HD, hoff, i, g, qf);
+    float m = kNegInf, lsum = 0.f;
+    f32x4_t acc[S::NB];
 #pragma unroll
-        for (int s = 0; s < S::NB; ++s) acc[s] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int s = 0; s < S::NB; ++s) acc[s] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-        // pipeline: descriptions two tiles ahead; the data of tile k+1 is
-        // loaded into the tile registers as soon as phase A of tile k has
-        // consumed them, and arrives during phase B
-        FwdTile<D> tile;
-        RowRef rnext{0, 0};
-        RowDesc d2{0, -1};
-        if (nt > 0) {
-            rnext = row_decode(B, 0, row_fetch(a, B, 0, i), i, g, a.n);
+    // pipeline: descriptions two tiles ahead; the data of tile k+1 is
+    // loaded into the tile registers as soon as phase A of tile k has
+    // consumed them, and arrives during phase B
+    FwdTile<D> tile;
+    RowRef rnext{0, 0};
+    RowDesc d2{0, -1};
+    if (nt > 0) {
+        rnext = row_decode(B, 0, row_fetch(a, B, 0, i), i, g, a.n);
+        tile.load(a.K, a.V, rnext.src, HD, hoff, l);
+    }
+    if (nt > 1) d2 = row_fetch(a, B, 1, i);
+    for (int64_t k = 0; k < nt; ++k) {
+        const uint32_t valid = rnext.valid;
+        const f32x4_t st = fwd_phase_a<D>(tile, qf, ks, vs, l, i, g);
+        if (k + 1 < nt) {
+            rnext = row_decode(B, k + 1, d2, i, g, a.n);
+            if (k + 2 < nt) d2 = row_fetch(a, B, k + 2, i);
             tile.load(a.K, a.V, rnext.src, HD, hoff, l);
         }
-        if (nt > 1) d2 = row_fetch(a, B, 1, i);
-        for (int64_t k = 0; k < nt; ++k) {
-            const uint32_t valid = rnext.valid;
-            const f32x4_t st = fwd_phase_a<D>(tile, qf, ks, vs, l, i, g);
-            if (k + 1 < nt) {
-                rnext = row_decode(B, k + 1, d2, i, g, a.n);
-                if (k + 2 < nt) d2 = row_fetch(a, B, k + 2, i);
-                tile.load(a.K, a.V, rnext.src, HD, hoff, l);
-            }
-            fwd_phase_b<D>(st, valid, m, lsum, acc, vs, a.scale2, i, g);
-        }
-        fwd_finish<D>(a, B.lo, h, HD, m, lsum, acc, i, g);
+        fwd_phase_b<D>(st, valid, m, lsum, acc, vs, a.scale2, i, g);
     }
+    fwd_finish<D>(a, B.lo, h, HD, m, lsum, acc, i, g);
 }
 
 // ---------------------------------------------------------------------------
@@ -650,45 +648,43 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
     const int64_t nt = B.count();
     uint16_t* ks = ks_all[w];
     uint16_t* vs = vs_all[w];
-    {
-        const int64_t hoff = static_cast<int64_t>(h) * D;
-        RowBlockRows<D> rows;
-        rows.load(a, B.lo, HD, hoff, h, i, g);
-        f32x4_t acc[S::NB];
+    const int64_t hoff = static_cast<int64_t>(h) * D;
+    RowBlockRows<D> rows;
+    rows.load(a, B.lo, HD, hoff, h, i, g);
+    f32x4_t acc[S::NB];
 #pragma unroll
-        for (int s = 0; s < S::NB; ++s) acc[s] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int s = 0; s < S::NB; ++s) acc[s] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-        // pipeline: descriptions two tiles ahead; tile k+1's data refills the
-        // tile registers once phase A of tile k has consumed them
-        RowBwdTile<D> tile;
-        RowRef rnext{0, 0};
-        int32_t auxn = -1;
-        RowDesc d2{0, -1};
-        if (nt > 0) {
-            const RowDesc d0 = row_fetch(a, B, 0, i);
-            rnext = row_decode(B, 0, d0, i, g, a.n);
-            auxn = d0.aux;
+    // pipeline: descriptions two tiles ahead; tile k+1's data refills the
+    // tile registers once phase A of tile k has consumed them
+    RowBwdTile<D> tile;
+    RowRef rnext{0, 0};
+    int32_t auxn = -1;
+    RowDesc d2{0, -1};
+    if (nt > 0) {
+        const RowDesc d0 = row_fetch(a, B, 0, i);
+        rnext = row_decode(B, 0, d0, i, g, a.n);
+        auxn = d0.aux;
+        tile.load(a.K, a.V, rnext.src, HD, hoff, l);
+    }
+    if (nt > 1) d2 = row_fetch(a, B, 1, i);
+    float delta, lse2;
+    rows.stats(delta, lse2);
+    for (int64_t k = 0; k < nt; ++k) {
+        const uint32_t valid = rnext.valid;
+        const int32_t aux = auxn;
+        f32x4_t st, dpv;
+        row_bwd_phase_a<D>(tile, rows.qf, rows.df, st, dpv, ks, vs, l, i, g);
+        if (k + 1 < nt) {
+            rnext = row_decode(B, k + 1, d2, i, g, a.n);
+            auxn = d2.aux;
+            if (k + 2 < nt) d2 = row_fetch(a, B, k + 2, i);
             tile.load(a.K, a.V, rnext.src, HD, hoff, l);
         }
-        if (nt > 1) d2 = row_fetch(a, B, 1, i);
-        float delta, lse2;
-        rows.stats(delta, lse2);
-        for (int64_t k = 0; k < nt; ++k) {
-            const uint32_t valid = rnext.valid;
-            const int32_t aux = auxn;
-            f32x4_t st, dpv;
-            row_bwd_phase_a<D>(tile, rows.qf, rows.df, st, dpv, ks, vs, l, i, g);
-            if (k + 1 < nt) {
-                rnext = row_decode(B, k + 1, d2, i, g, a.n);
-                auxn = d2.aux;
-                if (k + 2 < nt) d2 = row_fetch(a, B, k + 2, i);
-                tile.load(a.K, a.V, rnext.src, HD, hoff, l);
-            }
-            row_bwd_phase_b<D>(st, dpv, valid, lse2, delta, acc, ks, a.scale2, i, g, pt_all[w]);
-            hand_off(a, B, k, aux, h, pt_all[w], l, i, g);
-        }
-        store_block_rows<D>(a.dQ, a.n, B.lo, HD, hoff, acc, a.oscale, i, g);
+        row_bwd_phase_b<D>(st, dpv, valid, lse2, delta, acc, ks, a.scale2, i, g, pt_all[w]);
+        hand_off(a, B, k, aux, h, pt_all[w], l, i, g);
     }
+    store_block_rows<D>(a.dQ, a.n, B.lo, HD, hoff, acc, a.oscale, i, g);
 }
 
 // What a lane needs of a tile of a column block (16 sources), loaded two
